@@ -1,0 +1,300 @@
+"""Pins for the fp64 oracle: each check ties it to something other than itself
+(hand-worked values, closed forms, invariants of the method, an independent
+library implementation, finite differences).  CPU only."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _read_golden_blocks(name):
+    blocks, cur = [], []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line:
+                continue
+            if line.startswith("#"):
+                if cur:
+                    blocks.append(np.array(cur, dtype=np.float64))
+                    cur = []
+                continue
+            cur.append([float(v) for v in line.split()])
+    if cur:
+        blocks.append(np.array(cur, dtype=np.float64))
+    return blocks
+
+
+def setup_module(_):
+    oracle.build(force=False)
+
+
+# ------------------------------------------------------------- GEMM core
+
+def test_linear_hand_worked_2x3x4():
+    X, W, b, Y = _read_golden_blocks("linear_2x3x4.txt")
+    got = oracle.column_linear(X, W, b[0])
+    assert np.array_equal(got, Y)
+
+
+def test_linear_1x1x1():
+    got = oracle.column_linear(np.array([[3.0]]), np.array([[-2.0]]), np.array([0.5]))
+    assert got.tolist() == [[-5.5]]
+
+
+def test_matmul_matches_numpy_float64():
+    rng = np.random.default_rng(1)
+    A = rng.standard_normal((64, 96))
+    B = rng.standard_normal((96, 80))
+    ref = A @ B
+    got = oracle.matmul(A, B)
+    assert np.max(np.abs(got - ref)) <= 1e-13 * np.max(np.abs(ref))
+
+
+def test_all_ones_gives_h_exactly():
+    T, h, n = 5, 37, 11
+    Y = oracle.column_linear(np.ones((T, h)), np.ones((h, n)))
+    assert np.all(Y == h)
+
+
+def test_identity_weight_gives_x_plus_b():
+    rng = np.random.default_rng(2)
+    X = rng.standard_normal((7, 16))
+    b = rng.standard_normal(16)
+    Y = oracle.column_linear(X, np.eye(16), b)
+    assert np.array_equal(Y, X + b)
+
+
+def test_row_linear_non_square_orientation():
+    # Z[m][c] = sum_j X[m][j] W[j][c]; a transposed operand cannot even be
+    # shaped for these sizes, and values pin the index order.
+    X = np.array([[1.0, 2.0]])             # [1, 2]
+    W = np.array([[1.0, 10.0, 100.0],      # [2, 3]
+                  [1000.0, 1e4, 1e5]])
+    assert oracle.row_linear(X, W).tolist() == [[2001.0, 20010.0, 200100.0]]
+
+
+# ------------------------------------------------------------------ GeLU
+
+def test_gelu_special_values_and_odd_identity():
+    y = np.linspace(-8, 8, 2001)
+    g = oracle.gelu_tanh(y)
+    gm = oracle.gelu_tanh(-y)
+    assert oracle.gelu_tanh(np.array([0.0]))[0] == 0.0
+    # g(y) - g(-y) = y because tanh is odd
+    assert np.max(np.abs((g - gm) - y)) <= 4e-15
+    # limits: g(y) -> y for y >> 0 and -> 0 for y << 0
+    big = oracle.gelu_tanh(np.array([30.0, -30.0]))
+    assert big[0] == 30.0 and abs(big[1]) < 1e-10
+
+
+def test_gelu_matches_torch_tanh_gelu_float64():
+    y = torch.linspace(-10, 10, 4001, dtype=torch.float64)
+    ref = torch.nn.functional.gelu(y, approximate="tanh").numpy()
+    got = oracle.gelu_tanh(y.numpy())
+    assert np.max(np.abs(got - ref)) <= 1e-15 * 10
+
+
+def test_gelu_close_to_erf_gelu():
+    # The tanh form approximates x * Phi(x); the two differ by < 5e-4.
+    from scipy.special import erf
+    y = np.linspace(-6, 6, 1201)
+    exact = 0.5 * y * (1 + erf(y / np.sqrt(2)))
+    d = np.max(np.abs(oracle.gelu_tanh(y) - exact))
+    assert 1e-5 < d < 5e-4
+
+
+def test_gelu_grad_finite_difference():
+    y = np.linspace(-6, 6, 601)
+    eps = 1e-5
+    fd = (oracle.gelu_tanh(y + eps) - oracle.gelu_tanh(y - eps)) / (2 * eps)
+    assert np.max(np.abs(oracle.gelu_tanh_grad(y) - fd)) <= 1e-9
+
+
+def test_gelu_grad_matches_torch_autograd():
+    y = torch.linspace(-8, 8, 1601, dtype=torch.float64, requires_grad=True)
+    torch.nn.functional.gelu(y, approximate="tanh").sum().backward()
+    got = oracle.gelu_tanh_grad(y.detach().numpy())
+    assert np.max(np.abs(got - y.grad.numpy())) <= 1e-14
+
+
+# ------------------------------------------------- sharding invariants
+
+def _mlp_inputs(T=6, h=16, ffn=32, seed=3, bias=True):
+    rng = np.random.default_rng(seed)
+    X = rng.standard_normal((T, h))
+    W1 = 0.3 * rng.standard_normal((h, ffn))
+    b1 = 0.3 * rng.standard_normal(ffn) if bias else None
+    W2 = 0.3 * rng.standard_normal((ffn, h))
+    dZ = rng.standard_normal((T, h))
+    return X, W1, b1, W2, dZ
+
+
+def _shard(W1, b1, W2, t, r):
+    n = W1.shape[1] // t
+    cols = slice(r * n, (r + 1) * n)
+    return W1[:, cols], (None if b1 is None else b1[cols]), W2[cols, :]
+
+
+@pytest.mark.parametrize("t", [2, 4])
+def test_column_shards_concatenate_bit_exact(t):
+    # Page "PaddlePaddle张量并行" introduction / "张量并行实战" PyTorch example:
+    # the rank-ordered concatenation of X W_i is X W.
+    X, W1, b1, _, _ = _mlp_inputs()
+    full = oracle.column_linear(X, W1, b1)
+    n = W1.shape[1] // t
+    parts = np.stack([oracle.column_linear(X, W1[:, r * n:(r + 1) * n], b1[r * n:(r + 1) * n])
+                      for r in range(t)])
+    assert np.array_equal(oracle.shard_concat(parts), full)
+
+
+@pytest.mark.parametrize("t", [1, 2, 4, 8])
+def test_row_partials_sum_to_unsharded_mlp(t):
+    # Page "Tensor Parallelism原理与实践" §2.1 (distributivity) with the
+    # column->row pairing: sum_r g(X W1_r + b1_r) W2_r = g(X W1 + b1) W2.
+    X, W1, b1, W2, _ = _mlp_inputs(T=5, h=16, ffn=64)
+    _, _, Z = oracle.mlp_shard_fwd(X, W1, b1, W2)
+    parts = np.stack([oracle.mlp_shard_fwd(X, *_shard(W1, b1, W2, t, r))[2] for r in range(t)])
+    got = oracle.shard_sum(parts)
+    assert np.max(np.abs(got - Z)) <= 1e-13 * np.max(np.abs(Z))
+    if t == 1:
+        assert np.array_equal(got, Z)
+
+
+def test_page3_shape_example():
+    meta = {}
+    with open(os.path.join(GOLDEN, "page3_column_shapes.txt")) as f:
+        for line in f:
+            if line.strip() and not line.startswith("#"):
+                k, *v = line.split()
+                meta[k] = [int(x) for x in v]
+    ws, T = meta["world_size"][0], meta["tokens"][0]
+    fin, fout = meta["in_features"][0], meta["out_features"][0]
+    assert fout % ws == 0 and fout // ws == meta["local_out_features"][0]
+    rng = np.random.default_rng(4)
+    X = rng.standard_normal((T, fin))
+    parts = np.stack([oracle.column_linear(X, 0.01 * rng.standard_normal((fin, fout // ws)))
+                      for _ in range(ws)])
+    assert parts.shape == (ws, T, meta["local_out_features"][0])
+    assert oracle.shard_concat(parts).shape == tuple(meta["gathered_shape"])
+
+
+def test_forward_matches_torch_float64():
+    X, W1, b1, W2, _ = _mlp_inputs(T=9, h=24, ffn=40)
+    Y, H, Z = oracle.mlp_shard_fwd(X, W1, b1, W2)
+    tX, tW1, tb1, tW2 = (torch.from_numpy(a) for a in (X, W1, b1, W2))
+    tY = tX @ tW1 + tb1
+    tH = torch.nn.functional.gelu(tY, approximate="tanh")
+    tZ = tH @ tW2
+    for a, b in ((Y, tY), (H, tH), (Z, tZ)):
+        assert np.max(np.abs(a - b.numpy())) <= 1e-13 * max(1.0, np.max(np.abs(a)))
+
+
+# -------------------------------------------------------------- backward
+
+def test_backward_matches_torch_autograd_float64():
+    t = 2
+    X, W1, b1, W2, dZ = _mlp_inputs(T=7, h=16, ffn=48)
+    tX = torch.from_numpy(X).requires_grad_()
+    tW1 = torch.from_numpy(W1).requires_grad_()
+    tb1 = torch.from_numpy(b1)
+    tW2 = torch.from_numpy(W2).requires_grad_()
+    tY = tX @ tW1 + tb1
+    tY.retain_grad()
+    Zt = torch.nn.functional.gelu(tY, approximate="tanh") @ tW2
+    (Zt * torch.from_numpy(dZ)).sum().backward()
+    g = [oracle.mlp_shard_bwd(X, *_shard(W1, b1, W2, t, r), dZ) for r in range(t)]
+    dW1 = np.concatenate([gi["dW1"] for gi in g], axis=1)
+    dW2 = np.concatenate([gi["dW2"] for gi in g], axis=0)
+    dY = np.concatenate([gi["dY"] for gi in g], axis=1)
+    dX = oracle.shard_sum(np.stack([gi["dX"] for gi in g]))
+    for a, b in ((dW1, tW1.grad), (dW2, tW2.grad), (dY, tY.grad), (dX, tX.grad)):
+        b = b.numpy()
+        assert np.max(np.abs(a - b)) <= 1e-13 * max(1.0, np.max(np.abs(b)))
+
+
+def test_backward_finite_differences():
+    T, h, ffn, t = 4, 8, 16, 2
+    X, W1, b1, W2, dZ = _mlp_inputs(T=T, h=h, ffn=ffn, seed=5)
+
+    def loss(X_, W1_, b1_, W2_):
+        tot = 0.0
+        for r in range(t):
+            tot += np.sum(dZ * oracle.mlp_shard_fwd(X_, *_shard(W1_, b1_, W2_, t, r))[2])
+        return tot
+
+    g = [oracle.mlp_shard_bwd(X, *_shard(W1, b1, W2, t, r), dZ) for r in range(t)]
+    dW1 = np.concatenate([gi["dW1"] for gi in g], axis=1)
+    dW2 = np.concatenate([gi["dW2"] for gi in g], axis=0)
+    dX = sum(gi["dX"] for gi in g)
+    db1 = np.concatenate([gi["dY"].sum(axis=0) for gi in g])
+    eps = 1e-6
+    checks = [(X, dX, (1, 3)), (X, dX, (3, 7)), (W1, dW1, (2, 5)), (W1, dW1, (7, 12)),
+              (W2, dW2, (9, 4)), (W2, dW2, (0, 0)), (b1, db1, (13,))]
+    for arr, grad, idx in checks:
+        orig = arr[idx]
+        arr[idx] = orig + eps
+        lp = loss(X, W1, b1, W2)
+        arr[idx] = orig - eps
+        lm = loss(X, W1, b1, W2)
+        arr[idx] = orig
+        fd = (lp - lm) / (2 * eps)
+        assert abs(fd - grad[idx]) <= 1e-7 * max(1.0, abs(grad[idx])), (idx, fd, grad[idx])
+
+
+def test_backward_adjoint_identities():
+    # <dW2_i, W2_i> = <dZ, H_i W2_i> and <dW1_i, W1_i> = <dY_i, X W1_i>
+    # = <dX_i, X>: a transposed or mis-indexed product breaks one of them.
+    X, W1, b1, W2, dZ = _mlp_inputs(T=6, h=24, ffn=40, seed=6)
+    Y, H, Z = oracle.mlp_shard_fwd(X, W1, b1, W2)
+    g = oracle.mlp_shard_bwd(X, W1, b1, W2, dZ)
+    XW = oracle.matmul(X, W1)
+    s1 = np.sum(g["dW2"] * W2)
+    assert abs(s1 - np.sum(dZ * Z)) <= 1e-12 * abs(s1)
+    s2 = np.sum(g["dW1"] * W1)
+    assert abs(s2 - np.sum(g["dY"] * XW)) <= 1e-12 * abs(s2)
+    assert abs(np.sum(g["dX"] * X) - s2) <= 1e-12 * abs(s2)
+
+
+def test_sampled_rows_and_cols_equal_full():
+    X, W1, b1, W2, dZ = _mlp_inputs(T=10, h=16, ffn=24, seed=7)
+    Y, H, Z = oracle.mlp_shard_fwd(X, W1, b1, W2)
+    g = oracle.mlp_shard_bwd(X, W1, b1, W2, dZ)
+    rows = [0, 3, 9]
+    cols = [1, 5, 23]
+    Yr, Hr, Zr = oracle.mlp_shard_fwd_rows(X, W1, b1, W2, rows)
+    assert np.array_equal(Zr, Z[rows]) and np.array_equal(Hr, H[rows])
+    gr = oracle.mlp_shard_bwd_rows(X, W1, b1, W2, dZ, rows)
+    assert np.allclose(gr["dY"], g["dY"][rows], rtol=0, atol=1e-14)
+    assert np.allclose(gr["dX"], g["dX"][rows], rtol=0, atol=1e-13)
+    gc = oracle.mlp_shard_bwd_cols(X, W1, b1, W2, dZ, cols)
+    assert np.allclose(gc["dY"], g["dY"][:, cols], rtol=0, atol=1e-14)
+    assert np.allclose(gc["dW1"], g["dW1"][:, cols], rtol=0, atol=1e-13)
+    assert np.allclose(gc["dW2"], g["dW2"][cols, :], rtol=0, atol=1e-13)
+
+
+# ---------------------------------------------------------- shard reduce
+
+@pytest.mark.parametrize("t", [1, 2, 4, 8])
+def test_shard_sum_of_identical_parts_is_exact_multiple(t):
+    # dyadic values: every partial sum is exact, so the result must be t*part
+    part = np.random.default_rng(8).integers(-1000, 1000, (3, 5)) / 16.0
+    got = oracle.shard_sum(np.stack([part] * t))
+    assert np.array_equal(got, t * part)
+
+
+def test_shard_sum_rank_order_integers():
+    parts = np.arange(4 * 6, dtype=np.float64).reshape(4, 2, 3)
+    assert np.array_equal(oracle.shard_sum(parts), parts.sum(axis=0))
+
+
+def test_shard_concat_then_slice_is_identity():
+    parts = np.random.default_rng(9).standard_normal((3, 4, 5))
+    out = oracle.shard_concat(parts)
+    for r in range(3):
+        assert np.array_equal(out[:, r * 5:(r + 1) * 5], parts[r])
