@@ -64,7 +64,7 @@ def _load():
             "oracle_column_linear": [dp, dp, dp, dp, i64, i64, i64, ctypes.c_int],
             "oracle_row_linear": [dp, dp, dp, i64, i64, i64],
             "oracle_mlp_shard_fwd": [dp, dp, dp, dp, dp, dp, dp, i64, i64, i64],
-            "oracle_mlp_shard_bwd": [dp] * 10 + [i64, i64, i64],
+            "oracle_mlp_shard_bwd": [dp] * 11 + [i64, i64, i64],
             "oracle_shard_sum": [dp, dp, ctypes.c_int, i64],
             "oracle_shard_concat": [dp, dp, ctypes.c_int, i64, i64],
         }
@@ -151,17 +151,17 @@ def mlp_shard_fwd(X, W1_i, b1_i, W2_i):
 
 
 def mlp_shard_bwd(X, W1_i, b1_i, W2_i, dZ):
-    """Returns dict(dY, dW2, dW1, dX) for one shard.  The shard's forward
+    """Returns dict(dY, dW2, dW1, dX, db1) for one shard.  The shard's forward
     values Y_i, H_i are recomputed here by the oracle's own forward."""
     X, W1_i, W2_i, dZ = _f64(X), _f64(W1_i), _f64(W2_i), _f64(dZ)
     T, h = X.shape
     n = W1_i.shape[1]
     Y, H, _ = mlp_shard_fwd(X, W1_i, b1_i, W2_i)
     dY = np.empty((T, n)); dW2 = np.empty((n, h)); dW1 = np.empty((h, n))
-    dX = np.empty((T, h))
+    dX = np.empty((T, h)); db1 = np.empty(n)
     _load().oracle_mlp_shard_bwd(_p(X), _p(W1_i), _p(W2_i), _p(Y), _p(H), _p(dZ),
-                                 _p(dY), _p(dW2), _p(dW1), _p(dX), T, h, n)
-    return {"dY": dY, "dW2": dW2, "dW1": dW1, "dX": dX}
+                                 _p(dY), _p(dW2), _p(dW1), _p(dX), _p(db1), T, h, n)
+    return {"dY": dY, "dW2": dW2, "dW1": dW1, "dX": dX, "db1": db1}
 
 
 def shard_sum(parts) -> np.ndarray:
@@ -199,11 +199,11 @@ def mlp_shard_bwd_rows(X, W1_i, b1_i, W2_i, dZ, rows):
 
 
 def mlp_shard_bwd_cols(X, W1_i, b1_i, W2_i, dZ, cols):
-    """dY_i[:, cols], dW1_i[:, cols] and dW2_i[cols, :]: the backward of the
-    narrower column shard made of ``cols`` (its dX is a partial and is
-    dropped)."""
+    """dY_i[:, cols], dW1_i[:, cols], dW2_i[cols, :] and db1_i[cols]: the
+    backward of the narrower column shard made of ``cols`` (its dX is a
+    partial and is dropped)."""
     cols = np.asarray(cols)
     W1_i, W2_i = _f64(W1_i), _f64(W2_i)
     b = None if b1_i is None else _f64(b1_i)[cols]
     g = mlp_shard_bwd(X, W1_i[:, cols], b, W2_i[cols, :], dZ)
-    return {"dY": g["dY"], "dW1": g["dW1"], "dW2": g["dW2"]}
+    return {"dY": g["dY"], "dW1": g["dW1"], "dW2": g["dW2"], "db1": g["db1"]}

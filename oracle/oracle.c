@@ -141,11 +141,13 @@ ORACLE_API void oracle_mlp_shard_fwd(const double* X, const double* W1_i, const 
  *   dW1_i = X^T dY_i                      same rule, column layer [P4 §3.1]
  *   dX_i  = dY_i W1_i^T                   this rank's share of the input
  *                                         gradient, summed over ranks [P1]
- * Shapes: dZ [T,h]; dY_i [T,n]; dW2_i [n,h]; dW1_i [h,n]; dX_i [T,h]. */
+ *   db1_i = sum over tokens of dY_i       bias gradient (chain rule through
+ *                                         Y_i = X W1_i + b1_i); db1_i may be NULL
+ * Shapes: dZ [T,h]; dY_i [T,n]; dW2_i [n,h]; dW1_i [h,n]; dX_i [T,h]; db1_i [n]. */
 ORACLE_API void oracle_mlp_shard_bwd(const double* X, const double* W1_i, const double* W2_i,
                                      const double* Y_i, const double* H_i, const double* dZ,
                                      double* dY_i, double* dW2_i, double* dW1_i, double* dX_i,
-                                     int64_t T, int64_t h, int64_t n)
+                                     double* db1_i, int64_t T, int64_t h, int64_t n)
 {
     /* dY_i[m][j] = (sum_c dZ[m][c] W2_i[j][c]) * g'(Y_i[m][j]) */
 #pragma omp parallel for schedule(static)
@@ -186,6 +188,12 @@ ORACLE_API void oracle_mlp_shard_bwd(const double* X, const double* W1_i, const 
             for (int64_t j = 0; j < n; ++j) s += dY_i[m * n + j] * W1_i[k * n + j];
             dX_i[m * h + k] = s;
         }
+    }
+    /* db1_i[j] = sum_m dY_i[m][j] */
+    if (db1_i) {
+        for (int64_t j = 0; j < n; ++j) db1_i[j] = 0.0;
+        for (int64_t m = 0; m < T; ++m)
+            for (int64_t j = 0; j < n; ++j) db1_i[j] += dY_i[m * n + j];
     }
 }
 

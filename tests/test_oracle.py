@@ -202,7 +202,7 @@ def test_backward_matches_torch_autograd_float64():
     X, W1, b1, W2, dZ = _mlp_inputs(T=7, h=16, ffn=48)
     tX = torch.from_numpy(X).requires_grad_()
     tW1 = torch.from_numpy(W1).requires_grad_()
-    tb1 = torch.from_numpy(b1)
+    tb1 = torch.from_numpy(b1).requires_grad_()
     tW2 = torch.from_numpy(W2).requires_grad_()
     tY = tX @ tW1 + tb1
     tY.retain_grad()
@@ -213,7 +213,9 @@ def test_backward_matches_torch_autograd_float64():
     dW2 = np.concatenate([gi["dW2"] for gi in g], axis=0)
     dY = np.concatenate([gi["dY"] for gi in g], axis=1)
     dX = oracle.shard_sum(np.stack([gi["dX"] for gi in g]))
-    for a, b in ((dW1, tW1.grad), (dW2, tW2.grad), (dY, tY.grad), (dX, tX.grad)):
+    db1 = np.concatenate([gi["db1"] for gi in g])
+    for a, b in ((dW1, tW1.grad), (dW2, tW2.grad), (dY, tY.grad), (dX, tX.grad),
+                 (db1, tb1.grad)):
         b = b.numpy()
         assert np.max(np.abs(a - b)) <= 1e-13 * max(1.0, np.max(np.abs(b)))
 
@@ -232,7 +234,7 @@ def test_backward_finite_differences():
     dW1 = np.concatenate([gi["dW1"] for gi in g], axis=1)
     dW2 = np.concatenate([gi["dW2"] for gi in g], axis=0)
     dX = sum(gi["dX"] for gi in g)
-    db1 = np.concatenate([gi["dY"].sum(axis=0) for gi in g])
+    db1 = np.concatenate([gi["db1"] for gi in g])
     eps = 1e-6
     checks = [(X, dX, (1, 3)), (X, dX, (3, 7)), (W1, dW1, (2, 5)), (W1, dW1, (7, 12)),
               (W2, dW2, (9, 4)), (W2, dW2, (0, 0)), (b1, db1, (13,))]
@@ -276,6 +278,7 @@ def test_sampled_rows_and_cols_equal_full():
     assert np.allclose(gc["dY"], g["dY"][:, cols], rtol=0, atol=1e-14)
     assert np.allclose(gc["dW1"], g["dW1"][:, cols], rtol=0, atol=1e-13)
     assert np.allclose(gc["dW2"], g["dW2"][cols, :], rtol=0, atol=1e-13)
+    assert np.allclose(gc["db1"], g["db1"][cols], rtol=0, atol=1e-13)
 
 
 # ---------------------------------------------------------- shard reduce
