@@ -1,0 +1,170 @@
+/*
+ * tp_mlp.h - C ABI for one tensor-parallel rank's share of a transformer MLP
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * The layer is split the Megatron way: the first linear layer is column-
+ * parallel (its weight is split by columns, every rank holds the whole input
+ * X), the second is row-parallel (its weight is split by rows, its input is
+ * the first layer's output shard), so the only exchanges are a sum of the
+ * row layer's partial outputs in the forward and a sum of the input-gradient
+ * partials in the backward.  On one GPU those exchanges are replaced by
+ * tp_shard_reduce, which sums (or concatenates) the t shards held in HBM.
+ *
+ * Pages cited below:
+ *   [P1] "PaddlePaddle张量并行：从原理到工业落地的深度解析", introduction
+ *        (column split of the FFN weight, AllGather of the shards, input
+ *        gradient aggregated by ReduceScatter / AllReduce).
+ *   [P2] "张量并行是什么：2026 大模型训练核心原理与实战详解", section
+ *        "核心工作机制：切分矩阵，协同计算" (column layer then row layer).
+ *   [P3] "张量并行实战：从理论到PyTorch代码的完整落地指南", section
+ *        "PyTorch 实现示例：自定义张量并行 Linear 层" (weight shard
+ *        [in, out/t], x @ W + b, divisibility assert, rank-ordered concat).
+ *   [P4] "Tensor Parallelism原理与实践：大模型训练的关键技术", §2.1 (block
+ *        product, sum of partials), §3.1 (column and row backward).
+ *
+ * Conventions shared by every entry point:
+ *   - Matrices are dense, row-major and contiguous.  Weights are stored
+ *     [in_features, out_features] and used as x @ W [P3].  Pointers are
+ *     shard-local (the caller passes rank r's block, not the full matrix).
+ *   - All pointers are device pointers (HBM, from hipMalloc or torch), owned
+ *     by the caller.  The library never allocates or frees memory and keeps
+ *     no mutable global state; calls are re-entrant.
+ *   - `stream` is a hipStream_t (NULL = the legacy default stream).  Calls
+ *     only enqueue work and return; nothing is synchronised.
+ *   - Element types: TP_BF16 (bfloat16) or TP_F32 (float).  Products are
+ *     accumulated in fp32 (MFMA).  bf16 results are rounded to nearest even.
+ *   - `t` is the tensor-parallel degree (world size) and `rank` is in [0, t).
+ *     rank only identifies which block the shard is; it is validated and
+ *     does not change the arithmetic.
+ *   - Dimensions: tokens >= 0 (0 is a no-op), every feature dimension (and
+ *     the shard width out_features / t, in_features / t) must be a positive
+ *     multiple of 8.  Each operand must be smaller than 2^31 bytes.
+ *   - Pointers must be 16-byte aligned.  Optional pointers may be NULL.
+ *   - Errors: arguments are validated before anything is enqueued; on any
+ *     error nothing is launched and a negative tp_status is returned.  A
+ *     failed launch returns TP_ERR_HIP (work enqueued earlier in the same
+ *     call may already be on the stream).
+ */
+#ifndef TP_MLP_H
+#define TP_MLP_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#ifndef TP_API
+#define TP_API __attribute__((visibility("default")))
+#endif
+
+typedef enum {
+    TP_OK = 0,
+    TP_ERR_NULL = -1,        /* a required pointer is NULL */
+    TP_ERR_SHAPE = -2,       /* dimension negative, zero, not a multiple of 8, or too large */
+    TP_ERR_INDIVISIBLE = -3, /* the split dimension is not divisible by t [P3 assert] */
+    TP_ERR_RANK = -4,        /* t < 1 or rank outside [0, t) */
+    TP_ERR_DTYPE = -5,       /* unsupported element-type combination */
+    TP_ERR_ALIGN = -6,       /* a pointer is not 16-byte aligned */
+    TP_ERR_HIP = -7,         /* the HIP runtime rejected a launch */
+    TP_ERR_ARG = -8          /* an enum argument is out of range */
+} tp_status;
+
+typedef enum { TP_F32 = 0, TP_BF16 = 1 } tp_dtype;
+typedef enum { TP_ACT_NONE = 0, TP_ACT_GELU_TANH = 1 } tp_act;
+typedef enum { TP_REDUCE_SUM = 0, TP_REDUCE_CONCAT = 1 } tp_reduce_op;
+
+/*
+ * Column-parallel linear on one shard [P3; P4 §2.1; P1]:
+ *   Y_i[m][j] = act( pre[m][j] ),  pre[m][j] = sum_k X[m][k] * W_i[k][j] + b_i[j]
+ *   X   [tokens, in_features]              element type `dtype`
+ *   W_i [in_features, out_features / t]    element type `dtype`
+ *   b_i [out_features / t] or NULL (= 0)   element type `dtype`
+ *   Y_i [tokens, out_features / t]         element type `out_dtype`
+ *   pre_save [tokens, out_features / t] or NULL: receives the pre-activation
+ *            (element type `dtype`), the value the backward's g'() needs
+ * act: TP_ACT_NONE or TP_ACT_GELU_TANH, g(y) = 0.5 y (1 + tanh(sqrt(2/pi)
+ * (y + 0.044715 y^3))).  dtype TP_F32 requires out_dtype TP_F32; dtype
+ * TP_BF16 allows either.  out_features % t != 0 -> TP_ERR_INDIVISIBLE.
+ */
+TP_API int tp_column_linear(const void* X, const void* W_i, const void* b_i, void* Y_i,
+                            void* pre_save, int64_t tokens, int64_t in_features,
+                            int64_t out_features, int t, int rank, int dtype, int out_dtype,
+                            int act, void* stream);
+
+/*
+ * Row-parallel linear on one shard, partial output without bias
+ * [P2 "核心工作机制"; P4 §3.1 row parallel]:
+ *   Z_i[m][c] = sum_j X_i[m][j] * W_i[j][c]
+ *   X_i [tokens, in_features / t]          element type `dtype`
+ *   W_i [in_features / t, out_features]    element type `dtype`
+ *   Z_i [tokens, out_features]             element type `out_dtype`
+ * The partials of all ranks add up to the unsharded product (tp_shard_reduce
+ * with TP_REDUCE_SUM).  in_features % t != 0 -> TP_ERR_INDIVISIBLE.
+ */
+TP_API int tp_row_linear(const void* X_i, const void* W_i, void* Z_i,
+                  int64_t tokens, int64_t in_features, int64_t out_features,
+                  int t, int rank, int dtype, int out_dtype, void* stream);
+
+/*
+ * Forward of one MLP shard, column layer feeding the row layer with no
+ * exchange in between [P2 "核心工作机制"; P4 §3.1].  Same kernels and order
+ * as tp_column_linear(act = GeLU, out_dtype = dtype) followed by
+ * tp_row_linear(out_dtype = fp32):
+ *   Y_i = X W1_i + b1_i ;  H_i = g(Y_i) ;  Z_i = H_i W2_i
+ *   X    [tokens, h]       W1_i [h, n]      b1_i [n] or NULL     W2_i [n, h]
+ *   H_i  [tokens, n]  (required; it is an output and the row layer's input)
+ *   Y_i_save [tokens, n] or NULL (pre-activation, kept for the backward)
+ *   Z_i  [tokens, h]  fp32 partial output (sum over ranks = layer output)
+ * with n = ffn / t.  X, W1_i, b1_i, W2_i, H_i, Y_i_save have element type
+ * `dtype`; Z_i is always fp32.  ffn % t != 0 -> TP_ERR_INDIVISIBLE.
+ */
+TP_API int tp_mlp_shard_fwd(const void* X, const void* W1_i, const void* b1_i, const void* W2_i,
+                     void* H_i, void* Y_i_save, void* Z_i,
+                     int64_t tokens, int64_t h, int64_t ffn, int t, int rank,
+                     int dtype, void* stream);
+
+/*
+ * Backward of one MLP shard from the full output gradient dZ (replicated on
+ * every rank) and the forward's saved Y_i, H_i [P4 §3.1; P1]:
+ *   dY_i  = (dZ W2_i^T) * g'(Y_i)      elementwise product
+ *   dW2_i = H_i^T dZ
+ *   dW1_i = X^T dY_i
+ *   dX_i  = dY_i W1_i^T                this rank's share of dL/dX
+ *   db1_i = sum over tokens of dY_i    (only if db1_i != NULL)
+ *   inputs:  X [tokens,h], W1_i [h,n], W2_i [n,h], Y_i [tokens,n],
+ *            H_i [tokens,n], dZ [tokens,h]         element type `dtype`
+ *   outputs: dY_i [tokens,n] (element type `dtype`; also the input of the
+ *            last two products), dW2_i [n,h], dW1_i [h,n], dX_i [tokens,h],
+ *            db1_i [n] or NULL                     fp32
+ * tokens == 0 is valid: the weight gradients are then written as zeros.
+ */
+TP_API int tp_mlp_shard_bwd(const void* X, const void* W1_i, const void* W2_i,
+                     const void* Y_i, const void* H_i, const void* dZ,
+                     void* dY_i, void* dW2_i, void* dW1_i, void* dX_i, void* db1_i,
+                     int64_t tokens, int64_t h, int64_t ffn, int t, int rank,
+                     int dtype, void* stream);
+
+/*
+ * Stand-in for the collective between ranks, over the t shards held on one
+ * GPU.  parts is [t][tokens][cols], contiguous, element type in_dtype.
+ *   TP_REDUCE_SUM    (AllReduce of row-parallel partials [P4 §2.1, §2.2]):
+ *                    out[m][c] = parts[0][m][c] + ... + parts[t-1][m][c],
+ *                    added in fp32 in rank order 0..t-1 (run-to-run
+ *                    deterministic), out [tokens][cols] of type out_dtype.
+ *   TP_REDUCE_CONCAT (AllGather + concat along the last dim [P3; P1]):
+ *                    out[m][r*cols + c] = parts[r][m][c], out
+ *                    [tokens][t*cols]; requires out_dtype == in_dtype.
+ * cols must be a positive multiple of 8; parts and out must not overlap.
+ */
+TP_API int tp_shard_reduce(const void* parts, void* out, int64_t tokens, int64_t cols, int t,
+                    int op, int in_dtype, int out_dtype, void* stream);
+
+/* Static description of a status code (never NULL). */
+TP_API const char* tp_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TP_MLP_H */

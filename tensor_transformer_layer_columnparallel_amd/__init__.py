@@ -21,8 +21,7 @@ _ABI_NAMES = (
 
 def __getattr__(name):
     if name in _ABI_NAMES or name in ("binding", "TPError", "load_library"):
-        from . import binding
-        if name == "binding":
-            return binding
-        return getattr(binding, name)
+        import importlib
+        binding = importlib.import_module(__name__ + ".binding")
+        return binding if name == "binding" else getattr(binding, name)
     raise AttributeError(name)

@@ -1,0 +1,31 @@
+// Internal launch interface between the C entry points and the kernels.
+#pragma once
+
+#include "common.h"
+
+namespace tpmlp {
+
+// Operand layouts of C = op(A) op(B), named by whether each operand is used
+// as stored ("N": A [M][K], B [K][N]) or transposed ("T").
+//   NN: A [M][K] K-contiguous, B [K][N] N-contiguous   (forward products)
+//   NT: A [M][K] K-contiguous, B [N][K] K-contiguous   (x W^T products)
+//   TN: A [K][M] M-contiguous, B [K][N] N-contiguous   (x^T dy products)
+enum class Layout { NN = 0, NT = 1, TN = 2 };
+
+// General kernel: any layout, fp32 or bf16, any M (ragged tiles masked).
+hipError_t gemm_simple(const GemmArgs& p, Elt elt, Layout layout, Epi epi, Elt out,
+                       hipStream_t stream);
+
+// out[e] = sum_{r=0}^{t-1} parts[r][e] (fp32, rank order); count % 8 == 0.
+hipError_t shard_sum(const void* parts, void* out, int64_t count, int t, Elt in, Elt out_elt,
+                     hipStream_t stream);
+
+// out[m][r*cols + c] = parts[r][m][c]; cols % 8 == 0.
+hipError_t shard_concat(const void* parts, void* out, int64_t rows, int64_t cols, int t,
+                        Elt elt, hipStream_t stream);
+
+// out[j] = sum_m in[m][j] in fp32, fixed summation order: the bias gradient.
+hipError_t column_sum(const void* in, float* out, int64_t rows, int64_t cols, Elt elt,
+                      hipStream_t stream);
+
+}  // namespace tpmlp

@@ -1,0 +1,197 @@
+// HBM-streaming kernels: the on-device stand-ins for the collectives between
+// ranks (sum of row-parallel partials, concatenation of column shards) and
+// the bias gradient (a column sum).  None of them uses LDS tiling beyond a
+// final fixed-order combine, and none uses atomics, so every result is
+// bitwise reproducible from run to run.
+#include "common.h"
+#include "kernels.h"
+
+namespace tpmlp {
+namespace {
+
+constexpr int kThreads = 256;
+
+// 8 consecutive elements, loaded or stored as 16-byte vectors.
+struct Oct {
+    float v[8];
+};
+
+__device__ __forceinline__ Oct load8(const float* p)
+{
+    const f32x4 a = *reinterpret_cast<const f32x4*>(p);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+    return Oct{{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]}};
+}
+__device__ __forceinline__ Oct load8(const bf16* p)
+{
+    const bf16x8 a = *reinterpret_cast<const bf16x8*>(p);
+    Oct o;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o.v[e] = (float)a[e];
+    return o;
+}
+__device__ __forceinline__ void store8(float* p, const Oct& o)
+{
+    *reinterpret_cast<f32x4*>(p) = f32x4{o.v[0], o.v[1], o.v[2], o.v[3]};
+    *reinterpret_cast<f32x4*>(p + 4) = f32x4{o.v[4], o.v[5], o.v[6], o.v[7]};
+}
+__device__ __forceinline__ void store8(bf16* p, const Oct& o)
+{
+    bf16x8 a;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) a[e] = (bf16)o.v[e];
+    *reinterpret_cast<bf16x8*>(p) = a;
+}
+
+// out[e] = parts[0][e] + ... + parts[t-1][e].  TT > 0: t == TT known at
+// compile time, so all t loads of a vector are issued before the adds.
+template <typename In, typename Out, int TT>
+__global__ __launch_bounds__(kThreads) void shard_sum_kernel(const In* __restrict__ parts,
+                                                             Out* __restrict__ out,
+                                                             int64_t nvec, int64_t count, int t)
+{
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    for (int64_t v = (int64_t)blockIdx.x * kThreads + threadIdx.x; v < nvec; v += stride) {
+        const int64_t e0 = v * 8;
+        Oct s;
+        if constexpr (TT > 0) {
+            Oct x[TT];
+#pragma unroll
+            for (int r = 0; r < TT; ++r) x[r] = load8(parts + (int64_t)r * count + e0);
+            s = x[0];
+#pragma unroll
+            for (int r = 1; r < TT; ++r)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) s.v[e] += x[r].v[e];
+        } else {
+            s = load8(parts + e0);
+            for (int r = 1; r < t; ++r) {
+                const Oct x = load8(parts + (int64_t)r * count + e0);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) s.v[e] += x.v[e];
+            }
+        }
+        store8(out + e0, s);
+    }
+}
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void shard_concat_kernel(const T* __restrict__ parts,
+                                                                T* __restrict__ out, int64_t rows,
+                                                                int64_t cols, int t)
+{
+    const int64_t pairs = rows * t;
+    const int64_t c8 = cols / 8;
+    for (int64_t q = blockIdx.x; q < pairs; q += gridDim.x) {
+        const int64_t m = q / t;
+        const int r = (int)(q - m * t);
+        const T* src = parts + ((int64_t)r * rows + m) * cols;
+        T* dst = out + m * (cols * t) + (int64_t)r * cols;
+        // 8 elements per step: one 16-byte vector for bf16, two for fp32.
+        for (int64_t c = threadIdx.x; c < c8; c += kThreads) {
+#pragma unroll
+            for (int h = 0; h < (int)sizeof(T) / 2; ++h)
+                *reinterpret_cast<i32x4*>(dst + c * 8 + h * 4) =
+                    *reinterpret_cast<const i32x4*>(src + c * 8 + h * 4);
+        }
+    }
+}
+
+// Column sums: 8 consecutive columns per thread, kRowGroups threads per
+// column octet stepping through rows, combined in LDS in fixed order.
+constexpr int kColOcts = 8;                       // 64 columns per block
+constexpr int kRowGroups = kThreads / kColOcts;   // 32
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void column_sum_kernel(const T* __restrict__ in,
+                                                              float* __restrict__ out,
+                                                              int64_t rows, int64_t cols)
+{
+    __shared__ float part[kRowGroups][kColOcts * 8];
+    const int oct = threadIdx.x % kColOcts;
+    const int rg = threadIdx.x / kColOcts;
+    const int64_t c0 = (int64_t)blockIdx.x * kColOcts * 8 + oct * 8;
+    Oct s{{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}};
+    if (c0 < cols) {
+        for (int64_t m = rg; m < rows; m += kRowGroups) {
+            const Oct x = load8(in + m * cols + c0);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) s.v[e] += x.v[e];
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) part[rg][oct * 8 + e] = s.v[e];
+    __syncthreads();
+    if (threadIdx.x < kColOcts * 8) {
+        const int64_t c = (int64_t)blockIdx.x * kColOcts * 8 + threadIdx.x;
+        float acc = 0.f;
+        for (int g = 0; g < kRowGroups; ++g) acc += part[g][threadIdx.x];
+        if (c < cols) out[c] = acc;
+    }
+}
+
+unsigned stream_grid(int64_t work_items)
+{
+    const int64_t cap = 256 * 16;   // 16 workgroups per CU, grid-stride beyond
+    const int64_t g = (work_items + kThreads - 1) / kThreads;
+    return (unsigned)(g < 1 ? 1 : (g > cap ? cap : g));
+}
+
+template <typename In, typename Out>
+hipError_t sum_launch(const void* parts, void* out, int64_t count, int t, hipStream_t s)
+{
+    const int64_t nvec = count / 8;
+    const dim3 grid(stream_grid(nvec)), block(kThreads);
+    const In* p = static_cast<const In*>(parts);
+    Out* o = static_cast<Out*>(out);
+    switch (t) {
+    case 1: hipLaunchKernelGGL((shard_sum_kernel<In, Out, 1>), grid, block, 0, s, p, o, nvec, count, t); break;
+    case 2: hipLaunchKernelGGL((shard_sum_kernel<In, Out, 2>), grid, block, 0, s, p, o, nvec, count, t); break;
+    case 4: hipLaunchKernelGGL((shard_sum_kernel<In, Out, 4>), grid, block, 0, s, p, o, nvec, count, t); break;
+    case 8: hipLaunchKernelGGL((shard_sum_kernel<In, Out, 8>), grid, block, 0, s, p, o, nvec, count, t); break;
+    default: hipLaunchKernelGGL((shard_sum_kernel<In, Out, 0>), grid, block, 0, s, p, o, nvec, count, t); break;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t shard_sum(const void* parts, void* out, int64_t count, int t, Elt in, Elt out_elt,
+                     hipStream_t stream)
+{
+    if (count <= 0) return hipSuccess;
+    if (in == Elt::F32 && out_elt == Elt::F32) return sum_launch<float, float>(parts, out, count, t, stream);
+    if (in == Elt::F32 && out_elt == Elt::BF16) return sum_launch<float, bf16>(parts, out, count, t, stream);
+    if (in == Elt::BF16 && out_elt == Elt::F32) return sum_launch<bf16, float>(parts, out, count, t, stream);
+    return sum_launch<bf16, bf16>(parts, out, count, t, stream);
+}
+
+hipError_t shard_concat(const void* parts, void* out, int64_t rows, int64_t cols, int t,
+                        Elt elt, hipStream_t stream)
+{
+    if (rows <= 0) return hipSuccess;
+    const int64_t pairs = rows * t;
+    const unsigned grid = (unsigned)(pairs < 256 * 16 ? pairs : 256 * 16);
+    if (elt == Elt::F32)
+        hipLaunchKernelGGL((shard_concat_kernel<float>), dim3(grid), dim3(kThreads), 0, stream,
+                           static_cast<const float*>(parts), static_cast<float*>(out), rows, cols, t);
+    else
+        hipLaunchKernelGGL((shard_concat_kernel<bf16>), dim3(grid), dim3(kThreads), 0, stream,
+                           static_cast<const bf16*>(parts), static_cast<bf16*>(out), rows, cols, t);
+    return hipGetLastError();
+}
+
+hipError_t column_sum(const void* in, float* out, int64_t rows, int64_t cols, Elt elt,
+                      hipStream_t stream)
+{
+    const unsigned grid = (unsigned)((cols + kColOcts * 8 - 1) / (kColOcts * 8));
+    if (elt == Elt::F32)
+        hipLaunchKernelGGL((column_sum_kernel<float>), dim3(grid), dim3(kThreads), 0, stream,
+                           static_cast<const float*>(in), out, rows, cols);
+    else
+        hipLaunchKernelGGL((column_sum_kernel<bf16>), dim3(grid), dim3(kThreads), 0, stream,
+                           static_cast<const bf16*>(in), out, rows, cols);
+    return hipGetLastError();
+}
+
+}  // namespace tpmlp

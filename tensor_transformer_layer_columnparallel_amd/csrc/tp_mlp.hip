@@ -1,0 +1,208 @@
+// C entry points of libtpmlp: argument validation, then kernel launches on the
+// caller's stream.  The declarations, with the meaning of every argument and
+// the pages each operation follows, are in include/tp_mlp.h.
+#include "tp_mlp.h"
+
+#include "common.h"
+#include "kernels.h"
+
+using namespace tpmlp;
+
+namespace {
+
+constexpr int64_t kMaxOperandBytes = (int64_t(1) << 31) - 1;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int elt_size(int dtype) { return dtype == TP_F32 ? 4 : 2; }
+
+bool valid_dtype(int d) { return d == TP_F32 || d == TP_BF16; }
+
+Elt to_elt(int d) { return d == TP_F32 ? Elt::F32 : Elt::BF16; }
+
+// A feature dimension: positive multiple of 8.
+bool feature_dim_ok(int64_t d) { return d > 0 && d % 8 == 0; }
+
+bool fits(int64_t rows, int64_t cols, int bytes)
+{
+    if (rows < 0 || cols < 0) return false;
+    if (rows == 0 || cols == 0) return true;
+    return rows <= kMaxOperandBytes / cols / bytes;
+}
+
+int check_ptrs(std::initializer_list<const void*> required,
+               std::initializer_list<const void*> optional)
+{
+    for (const void* p : required)
+        if (!p) return TP_ERR_NULL;
+    for (const void* p : required)
+        if (!aligned16(p)) return TP_ERR_ALIGN;
+    for (const void* p : optional)
+        if (p && !aligned16(p)) return TP_ERR_ALIGN;
+    return TP_OK;
+}
+
+int check_split(int64_t full, int t, int rank, int64_t* local)
+{
+    if (t < 1 || rank < 0 || rank >= t) return TP_ERR_RANK;
+    if (!feature_dim_ok(full)) return TP_ERR_SHAPE;
+    if (full % t != 0) return TP_ERR_INDIVISIBLE;
+    *local = full / t;
+    if (!feature_dim_ok(*local)) return TP_ERR_SHAPE;
+    return TP_OK;
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? TP_OK : TP_ERR_HIP; }
+
+hipError_t run_gemm(const void* A, const void* B, void* C, const void* bias, const void* aux,
+                    void* save, int64_t M, int64_t N, int64_t K, Elt elt, Layout layout, Epi epi,
+                    Elt out, hipStream_t stream)
+{
+    if (M == 0 || N == 0) return hipSuccess;
+    GemmArgs p{A, B, C, bias, aux, save, M, N, K};
+    return gemm_simple(p, elt, layout, epi, out, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* tp_status_string(int status)
+{
+    switch (status) {
+    case TP_OK: return "ok";
+    case TP_ERR_NULL: return "a required pointer is NULL";
+    case TP_ERR_SHAPE: return "a dimension is negative, zero, not a multiple of 8, or too large";
+    case TP_ERR_INDIVISIBLE: return "the split dimension is not divisible by t";
+    case TP_ERR_RANK: return "t < 1 or rank outside [0, t)";
+    case TP_ERR_DTYPE: return "unsupported element-type combination";
+    case TP_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case TP_ERR_HIP: return "the HIP runtime rejected a launch";
+    case TP_ERR_ARG: return "an enum argument is out of range";
+    default: return "unknown status";
+    }
+}
+
+int tp_column_linear(const void* X, const void* W_i, const void* b_i, void* Y_i,
+                     void* pre_save, int64_t tokens, int64_t in_features, int64_t out_features,
+                     int t, int rank, int dtype, int out_dtype, int act, void* stream)
+{
+    if (!valid_dtype(dtype) || !valid_dtype(out_dtype)) return TP_ERR_DTYPE;
+    if (dtype == TP_F32 && out_dtype != TP_F32) return TP_ERR_DTYPE;
+    if (act != TP_ACT_NONE && act != TP_ACT_GELU_TANH) return TP_ERR_ARG;
+    int st = check_ptrs({X, W_i, Y_i}, {b_i, pre_save});
+    if (st) return st;
+    int64_t n = 0;
+    if ((st = check_split(out_features, t, rank, &n))) return st;
+    if (tokens < 0 || !feature_dim_ok(in_features)) return TP_ERR_SHAPE;
+    const int es = elt_size(dtype);
+    if (!fits(tokens, in_features, es) || !fits(in_features, n, es) ||
+        !fits(tokens, n, elt_size(out_dtype)) || !fits(tokens, n, es))
+        return TP_ERR_SHAPE;
+    // Without an activation the output is the pre-activation itself.
+    const Epi epi = act == TP_ACT_GELU_TANH ? Epi::BiasGelu : Epi::Bias;
+    if (epi == Epi::Bias && pre_save) return TP_ERR_ARG;
+    return status_of(run_gemm(X, W_i, Y_i, b_i, nullptr, pre_save, tokens, n, in_features,
+                              to_elt(dtype), Layout::NN, epi, to_elt(out_dtype),
+                              static_cast<hipStream_t>(stream)));
+}
+
+int tp_row_linear(const void* X_i, const void* W_i, void* Z_i, int64_t tokens,
+                  int64_t in_features, int64_t out_features, int t, int rank, int dtype,
+                  int out_dtype, void* stream)
+{
+    if (!valid_dtype(dtype) || !valid_dtype(out_dtype)) return TP_ERR_DTYPE;
+    if (dtype == TP_F32 && out_dtype != TP_F32) return TP_ERR_DTYPE;
+    int st = check_ptrs({X_i, W_i, Z_i}, {});
+    if (st) return st;
+    int64_t k = 0;
+    if ((st = check_split(in_features, t, rank, &k))) return st;
+    if (tokens < 0 || !feature_dim_ok(out_features)) return TP_ERR_SHAPE;
+    const int es = elt_size(dtype);
+    if (!fits(tokens, k, es) || !fits(k, out_features, es) ||
+        !fits(tokens, out_features, elt_size(out_dtype)))
+        return TP_ERR_SHAPE;
+    return status_of(run_gemm(X_i, W_i, Z_i, nullptr, nullptr, nullptr, tokens, out_features, k,
+                              to_elt(dtype), Layout::NN, Epi::Store, to_elt(out_dtype),
+                              static_cast<hipStream_t>(stream)));
+}
+
+int tp_mlp_shard_fwd(const void* X, const void* W1_i, const void* b1_i, const void* W2_i,
+                     void* H_i, void* Y_i_save, void* Z_i, int64_t tokens, int64_t h,
+                     int64_t ffn, int t, int rank, int dtype, void* stream)
+{
+    if (!valid_dtype(dtype)) return TP_ERR_DTYPE;
+    int st = check_ptrs({X, W1_i, W2_i, H_i, Z_i}, {b1_i, Y_i_save});
+    if (st) return st;
+    int64_t n = 0;
+    if ((st = check_split(ffn, t, rank, &n))) return st;
+    if (tokens < 0 || !feature_dim_ok(h)) return TP_ERR_SHAPE;
+    const int es = elt_size(dtype);
+    if (!fits(tokens, h, es) || !fits(h, n, es) || !fits(tokens, n, es) || !fits(tokens, h, 4))
+        return TP_ERR_SHAPE;
+    const Elt e = to_elt(dtype);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t err = run_gemm(X, W1_i, H_i, b1_i, nullptr, Y_i_save, tokens, n, h, e, Layout::NN,
+                              Epi::BiasGelu, e, s);
+    if (err != hipSuccess) return TP_ERR_HIP;
+    return status_of(run_gemm(H_i, W2_i, Z_i, nullptr, nullptr, nullptr, tokens, h, n, e,
+                              Layout::NN, Epi::Store, Elt::F32, s));
+}
+
+int tp_mlp_shard_bwd(const void* X, const void* W1_i, const void* W2_i, const void* Y_i,
+                     const void* H_i, const void* dZ, void* dY_i, void* dW2_i, void* dW1_i,
+                     void* dX_i, void* db1_i, int64_t tokens, int64_t h, int64_t ffn, int t,
+                     int rank, int dtype, void* stream)
+{
+    if (!valid_dtype(dtype)) return TP_ERR_DTYPE;
+    int st = check_ptrs({X, W1_i, W2_i, Y_i, H_i, dZ, dY_i, dW2_i, dW1_i, dX_i}, {db1_i});
+    if (st) return st;
+    int64_t n = 0;
+    if ((st = check_split(ffn, t, rank, &n))) return st;
+    if (tokens < 0 || !feature_dim_ok(h)) return TP_ERR_SHAPE;
+    const int es = elt_size(dtype);
+    if (!fits(tokens, h, es) || !fits(h, n, es) || !fits(tokens, n, es) || !fits(tokens, h, 4) ||
+        !fits(h, n, 4))
+        return TP_ERR_SHAPE;
+    const Elt e = to_elt(dtype);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t err;
+    // dY_i = (dZ W2_i^T) * g'(Y_i): W2_i [n][h] is the K-contiguous [N][K] operand.
+    if ((err = run_gemm(dZ, W2_i, dY_i, nullptr, Y_i, nullptr, tokens, n, h, e, Layout::NT,
+                        Epi::DGelu, e, s)) != hipSuccess)
+        return TP_ERR_HIP;
+    // dW2_i = H_i^T dZ: H_i [T][n] is [K][M], dZ [T][h] is [K][N].
+    if ((err = run_gemm(H_i, dZ, dW2_i, nullptr, nullptr, nullptr, n, h, tokens, e, Layout::TN,
+                        Epi::Store, Elt::F32, s)) != hipSuccess)
+        return TP_ERR_HIP;
+    // dW1_i = X^T dY_i: X [T][h] is [K][M], dY_i [T][n] is [K][N].
+    if ((err = run_gemm(X, dY_i, dW1_i, nullptr, nullptr, nullptr, h, n, tokens, e, Layout::TN,
+                        Epi::Store, Elt::F32, s)) != hipSuccess)
+        return TP_ERR_HIP;
+    // dX_i = dY_i W1_i^T: W1_i [h][n] is the K-contiguous [N][K] operand.
+    if ((err = run_gemm(dY_i, W1_i, dX_i, nullptr, nullptr, nullptr, tokens, h, n, e, Layout::NT,
+                        Epi::Store, Elt::F32, s)) != hipSuccess)
+        return TP_ERR_HIP;
+    if (db1_i)
+        return status_of(column_sum(dY_i, static_cast<float*>(db1_i), tokens, n, e, s));
+    return TP_OK;
+}
+
+int tp_shard_reduce(const void* parts, void* out, int64_t tokens, int64_t cols, int t, int op,
+                    int in_dtype, int out_dtype, void* stream)
+{
+    if (op != TP_REDUCE_SUM && op != TP_REDUCE_CONCAT) return TP_ERR_ARG;
+    if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return TP_ERR_DTYPE;
+    if (op == TP_REDUCE_CONCAT && in_dtype != out_dtype) return TP_ERR_DTYPE;
+    int st = check_ptrs({parts, out}, {});
+    if (st) return st;
+    if (t < 1) return TP_ERR_RANK;
+    if (tokens < 0 || !feature_dim_ok(cols)) return TP_ERR_SHAPE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (op == TP_REDUCE_SUM)
+        return status_of(shard_sum(parts, out, tokens * cols, t, to_elt(in_dtype),
+                                   to_elt(out_dtype), s));
+    return status_of(shard_concat(parts, out, tokens, cols, t, to_elt(in_dtype), s));
+}
+
+}  // extern "C"

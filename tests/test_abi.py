@@ -1,0 +1,117 @@
+"""CPU-side checks of the C ABI: the library loads, exports every symbol the
+header declares, and rejects bad arguments before touching the GPU (every
+call here fails validation, so no kernel is ever launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tp_mlp.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    return re.findall(r"TP_API\s+(?:const\s+)?\w+\s*\*?\s*(tp_\w+)\s*\(", text)
+
+
+@pytest.fixture(scope="module")
+def B():
+    from tensor_transformer_layer_columnparallel_amd import binding
+    return binding
+
+
+def test_header_declares_the_five_entry_points_and_status_string():
+    assert set(_declared_functions()) == {
+        "tp_column_linear", "tp_row_linear", "tp_mlp_shard_fwd", "tp_mlp_shard_bwd",
+        "tp_shard_reduce", "tp_status_string"}
+
+
+def test_library_exports_every_declared_symbol(B):
+    lib = ctypes.CDLL(B.LIB_PATH)
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(B):
+    for st in range(0, -9, -1):
+        assert B.tp_status_string(st) and B.tp_status_string(st) != "unknown status"
+    assert B.tp_status_string(12345) == "unknown status"
+
+
+# Fake, 16-byte-aligned device addresses: validation must reject each call
+# before any HIP call is made, so they are never dereferenced.
+P = 0x10000
+P2 = 0x20000
+MIS = 0x10008
+
+
+def test_column_linear_rejects(B):
+    f = lambda **kw: B.tp_column_linear(**{**dict(
+        X=P, W_i=P, b_i=None, Y_i=P, pre_save=None, tokens=32, in_features=768, out_features=3072, t=4,
+        rank=0, dtype=B.TP_BF16, out_dtype=B.TP_BF16, act=B.TP_ACT_NONE, stream=0,
+        check=False), **kw})
+    assert f(X=None) == B.TP_ERR_NULL
+    assert f(Y_i=None) == B.TP_ERR_NULL
+    assert f(W_i=MIS) == B.TP_ERR_ALIGN
+    assert f(b_i=MIS) == B.TP_ERR_ALIGN
+    assert f(out_features=3080, t=3) == B.TP_ERR_INDIVISIBLE  # 3080 = 8 * 385
+    assert f(out_features=3072 + 4) == B.TP_ERR_SHAPE        # not a multiple of 8
+    assert f(t=4, out_features=4 * 12) == B.TP_ERR_SHAPE     # shard width 12
+    assert f(rank=4) == B.TP_ERR_RANK
+    assert f(rank=-1) == B.TP_ERR_RANK
+    assert f(t=0) == B.TP_ERR_RANK
+    assert f(tokens=-1) == B.TP_ERR_SHAPE
+    assert f(in_features=0) == B.TP_ERR_SHAPE
+    assert f(in_features=770) == B.TP_ERR_SHAPE
+    assert f(dtype=B.TP_F32, out_dtype=B.TP_BF16) == B.TP_ERR_DTYPE
+    assert f(dtype=7) == B.TP_ERR_DTYPE
+    assert f(act=5) == B.TP_ERR_ARG
+    assert f(pre_save=P2) == B.TP_ERR_ARG                   # save without activation
+    assert f(pre_save=MIS, act=B.TP_ACT_GELU_TANH) == B.TP_ERR_ALIGN
+    # an operand of 2^31 bytes or more
+    assert f(tokens=1 << 20, in_features=1 << 10) == B.TP_ERR_SHAPE
+
+
+def test_row_linear_rejects(B):
+    f = lambda **kw: B.tp_row_linear(**{**dict(
+        X_i=P, W_i=P, Z_i=P, tokens=8, in_features=64, out_features=32, t=2, rank=1,
+        dtype=B.TP_BF16, out_dtype=B.TP_F32, stream=0, check=False), **kw})
+    assert f(Z_i=None) == B.TP_ERR_NULL
+    assert f(in_features=72, t=2) == B.TP_ERR_SHAPE          # 36-wide shard
+    assert f(in_features=64, t=3) == B.TP_ERR_INDIVISIBLE
+    assert f(rank=2) == B.TP_ERR_RANK
+    assert f(out_features=36) == B.TP_ERR_SHAPE
+
+
+def test_mlp_fwd_bwd_reject(B):
+    fwd = lambda **kw: B.tp_mlp_shard_fwd(**{**dict(
+        X=P, W1_i=P, b1_i=None, W2_i=P, H_i=P, Y_i_save=None, Z_i=P, tokens=16, h=64,
+        ffn=256, t=8, rank=0, dtype=B.TP_BF16, stream=0, check=False), **kw})
+    assert fwd(H_i=None) == B.TP_ERR_NULL
+    assert fwd(Y_i_save=MIS) == B.TP_ERR_ALIGN
+    assert fwd(ffn=260) == B.TP_ERR_SHAPE
+    assert fwd(ffn=264, t=5) == B.TP_ERR_INDIVISIBLE
+    assert fwd(ffn=264, t=8) == B.TP_ERR_SHAPE               # shard width 33
+    assert fwd(dtype=3) == B.TP_ERR_DTYPE
+    bwd = lambda **kw: B.tp_mlp_shard_bwd(**{**dict(
+        X=P, W1_i=P, W2_i=P, Y_i=P, H_i=P, dZ=P, dY_i=P, dW2_i=P, dW1_i=P, dX_i=P, db1_i=None,
+        tokens=16, h=64, ffn=256, t=8, rank=7, dtype=B.TP_BF16, stream=0, check=False), **kw})
+    assert bwd(dZ=None) == B.TP_ERR_NULL
+    assert bwd(db1_i=MIS) == B.TP_ERR_ALIGN
+    assert bwd(rank=8) == B.TP_ERR_RANK
+    assert bwd(h=60) == B.TP_ERR_SHAPE
+
+
+def test_shard_reduce_rejects(B):
+    f = lambda **kw: B.tp_shard_reduce(**{**dict(
+        parts=P, out=P2, tokens=4, cols=16, t=8, op=B.TP_REDUCE_SUM, in_dtype=B.TP_F32,
+        out_dtype=B.TP_F32, stream=0, check=False), **kw})
+    assert f(op=2) == B.TP_ERR_ARG
+    assert f(op=B.TP_REDUCE_CONCAT, out_dtype=B.TP_BF16) == B.TP_ERR_DTYPE
+    assert f(parts=None) == B.TP_ERR_NULL
+    assert f(out=MIS) == B.TP_ERR_ALIGN
+    assert f(t=0) == B.TP_ERR_RANK
+    assert f(cols=12) == B.TP_ERR_SHAPE
+    assert f(tokens=-3) == B.TP_ERR_SHAPE
