@@ -1,0 +1,318 @@
+// Large-tile bf16 MFMA GEMM for gfx950: C[M,N] = epi( op(A)[M,K] * op(B)[K,N] ).
+//
+// Workgroup: 256 threads = 4 waves in a 2 x 2 grid, a 256 x 256 output tile
+// per workgroup, 128 x 128 per wave (8 x 8 MFMA 16x16x32 bf16 tiles, fp32
+// accumulators).  K advances in slabs of 64.
+//
+// HBM -> LDS: buffer_load_dwordx4 ... lds (each lane's 16 bytes land directly
+// in LDS, no VGPR staging).  Buffer loads clamp to the operand's extent, so a
+// ragged M or N tail reads zeros (or stays inside the operand) and can never
+// fault.  Two LDS stages: slab k+1 streams in while slab k is multiplied.
+//
+// LDS layouts (both 16-byte-chunk XOR swizzled so fragment reads are free of
+// bank conflicts):
+//   K-major operand  [rows][64 k]     read with ds_read_b128 (8 k per lane)
+//   MN-major operand [64 k][rows]     read with ds_read_b64_tr_b16: within a
+//     16-lane group, lane i receives element (i % 4) of the 8-byte pieces
+//     loaded by lanes 4e + i/4, e = 0..3.  Pointing lane 4e + g at
+//     row k0 + e, columns 4g..4g+3 gives every lane four consecutive k of
+//     one column: half of an MFMA operand; two reads make the 8.
+//
+// The MFMA is issued with the B fragment in the first operand slot and the A
+// fragment in the second, so a lane's four results are four consecutive
+// columns of one output row (16-byte fp32 / 8-byte bf16 stores).
+//
+// Workgroups are remapped so that consecutive output tiles, which share
+// operand panels, run on the same XCD (hardware dispatches workgroup w to
+// XCD w % 8) and hit that XCD's L2.
+#include "common.h"
+#include "epilogue.h"
+#include "kernels.h"
+
+namespace tpmlp {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kTile = 256;        // BM = BN
+constexpr int kBK = 64;
+constexpr int kWaveTile = 128;
+constexpr int kFrag = kWaveTile / 16;   // 8 fragments per wave per dimension
+constexpr int kStageElems = kTile * kBK; // one operand, one stage (bf16 elements)
+constexpr int kXcds = 8;
+
+// Third descriptor word of a raw buffer resource on gfx9-family GPUs.
+constexpr int kRsrcWord3 = 0x00020000;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             kRsrcWord3);
+}
+
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rsrc, bf16* lds_base,
+                                           uint32_t voffset, uint32_t soffset)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (TP_LDS void*)lds_base, 16, voffset, soffset,
+                                             0, 0);
+}
+
+// Chunk swizzles (16-byte chunks).  K-major rows hold 8 chunks; the read of
+// a 16-lane group touches 16 consecutive rows at one logical chunk.
+__device__ __forceinline__ int swz_kmaj(int row) { return (row >> 1) & 7; }
+// MN-major rows hold kTile/8 = 32 chunks; a transposed read touches rows
+// 4j..4j+3 (j = group) at one chunk pair.  Even values keep chunk pairs
+// together.
+__device__ __forceinline__ int swz_mnmaj(int krow) { return 2 * ((krow & 3) | (((krow >> 3) & 1) << 2)); }
+
+// Issues the loads of one 256 x 64 operand slab into LDS stage `s`.
+//   K-major  [rows][K]: 8 rows x 8 chunks per instruction, 8 instructions.
+//   MN-major [K][rows]: 2 k-rows x 32 chunks per instruction, 8 instructions.
+template <bool KMAJ>
+struct SlabDma {
+    uint32_t voff[8];   // per-instruction byte offsets of this lane (k slab 0)
+    uint32_t kstep;     // bytes to advance one slab along K
+
+    __device__ __forceinline__ void init(int wave, int lane, int64_t r0, int64_t ld)
+    {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if (KMAJ) {
+                const int row = wave * 64 + j * 8 + (lane >> 3);
+                const int chunk = (lane & 7) ^ swz_kmaj(row);
+                voff[j] = (uint32_t)(((r0 + row) * ld + chunk * 8) * 2);
+            } else {
+                const int krow = wave * 16 + j * 2 + (lane >> 5);
+                const int chunk = (lane & 31) ^ swz_mnmaj(krow);
+                voff[j] = (uint32_t)((krow * ld + r0 + chunk * 8) * 2);
+            }
+        }
+        kstep = KMAJ ? (uint32_t)(kBK * 2) : (uint32_t)(kBK * ld * 2);
+    }
+
+    __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rsrc, bf16* stage, int wave,
+                                          uint32_t soff) const
+    {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            bf16* dst = KMAJ ? stage + (wave * 64 + j * 8) * kBK
+                             : stage + (wave * 16 + j * 2) * kTile;
+            load_lds16(rsrc, dst, voff[j], soff);
+        }
+    }
+};
+
+// Fragment reads for one 32-wide k half (ks) of a stage: 8 fragments of 16
+// rows (M for A, N for B) x 32 k, 8 bf16 per lane.
+template <bool KMAJ>
+__device__ __forceinline__ void read_frags(const bf16* stage, int wrow0, int ks, int lane,
+                                           bf16x8 (&f)[kFrag])
+{
+    const int i = lane & 15, g = lane >> 4;
+    if constexpr (KMAJ) {
+        const int chunk = (ks * 4 + g) ^ swz_kmaj(i);
+#pragma unroll
+        for (int q = 0; q < kFrag; ++q) {
+            const int row = wrow0 + q * 16 + i;
+            f[q] = *reinterpret_cast<const bf16x8*>(stage + row * kBK + chunk * 8);
+        }
+    } else {
+        const int sw = 2 * ((i >> 2) | ((g & 1) << 2));   // swz_mnmaj of the k-rows read
+        const int krow0 = ks * 32 + g * 8 + (i >> 2);
+#pragma unroll
+        for (int q = 0; q < kFrag; ++q) {
+            const int col = wrow0 + q * 16 + 4 * (i & 3);
+            const int chunk = ((col >> 3) ^ sw);
+            bf16x4 half[2];
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const bf16* p = stage + (krow0 + 4 * hh) * kTile + chunk * 8 + (col & 7);
+                const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (TP_LDS i16x4*)((TP_LDS bf16*)p));
+                half[hh] = __builtin_bit_cast(bf16x4, v);
+            }
+            f[q] = bf16x8{half[0][0], half[0][1], half[0][2], half[0][3],
+                          half[1][0], half[1][1], half[1][2], half[1][3]};
+        }
+    }
+}
+
+template <bool A_KMAJ, bool B_KMAJ, Epi EPI, typename OutT>
+__global__ __launch_bounds__(kThreads, 1) void gemm_tile_kernel(GemmArgs p, int tiles_m,
+                                                                int tiles_n)
+{
+    __shared__ __attribute__((aligned(1024))) bf16 smem[2][2 * kStageElems];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+
+    // XCD-aware tile order: the tiles of one XCD form a contiguous run of the
+    // m-fastest tile sequence.
+    const int ntiles = tiles_m * tiles_n;
+    int tile = blockIdx.x;
+    if (ntiles % kXcds == 0) tile = (tile % kXcds) * (ntiles / kXcds) + tile / kXcds;
+    const int tm = tile % tiles_m, tn = tile / tiles_m;
+    const int64_t m0 = (int64_t)tm * kTile, n0 = (int64_t)tn * kTile;
+
+    const bf16* A = static_cast<const bf16*>(p.A);
+    const bf16* B = static_cast<const bf16*>(p.B);
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(A, (uint32_t)(p.M * p.K * 2));
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(B, (uint32_t)(p.N * p.K * 2));
+
+    SlabDma<A_KMAJ> da;
+    SlabDma<B_KMAJ> db;
+    da.init(wave, lane, m0, A_KMAJ ? p.K : p.M);
+    db.init(wave, lane, n0, B_KMAJ ? p.K : p.N);
+
+    f32x4 acc[kFrag][kFrag];
+#pragma unroll
+    for (int a = 0; a < kFrag; ++a)
+#pragma unroll
+        for (int b = 0; b < kFrag; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int nk = (int)((p.K + kBK - 1) / kBK);
+    bf16x8 fa[2][kFrag], fb[2][kFrag];
+
+    if (nk > 0) {
+        da.issue(ra, smem[0], wave, 0);
+        db.issue(rb, smem[0] + kStageElems, wave, 0);
+        __syncthreads();
+        read_frags<A_KMAJ>(smem[0], wm * kWaveTile, 0, lane, fa[0]);
+        read_frags<B_KMAJ>(smem[0] + kStageElems, wn * kWaveTile, 0, lane, fb[0]);
+    }
+
+    // Per slab: read the second k half of the current stage, then start the
+    // DMA of the next slab into the other stage.  All LDS reads of the
+    // current stage precede the DMA in program order, so the wait for the
+    // DMA (which the compiler places before the next LDS read) falls after
+    // the 128 MFMAs of this slab instead of before them.
+    for (int kt = 0; kt < nk; ++kt) {
+        const int cur = kt & 1;
+        read_frags<A_KMAJ>(smem[cur], wm * kWaveTile, 1, lane, fa[1]);
+        read_frags<B_KMAJ>(smem[cur] + kStageElems, wn * kWaveTile, 1, lane, fb[1]);
+        if (kt + 1 < nk) {
+            da.issue(ra, smem[cur ^ 1], wave, (uint32_t)(kt + 1) * da.kstep);
+            db.issue(rb, smem[cur ^ 1] + kStageElems, wave, (uint32_t)(kt + 1) * db.kstep);
+        }
+#pragma unroll
+        for (int a = 0; a < kFrag; ++a)
+#pragma unroll
+            for (int b = 0; b < kFrag; ++b)
+                acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[0][b], fa[0][a], acc[a][b],
+                                                                     0, 0, 0);
+#pragma unroll
+        for (int a = 0; a < kFrag; ++a)
+#pragma unroll
+            for (int b = 0; b < kFrag; ++b)
+                acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[1][b], fa[1][a], acc[a][b],
+                                                                     0, 0, 0);
+        // Keep the MFMAs above the barrier: its fence waits for the DMA.
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();
+        if (kt + 1 < nk) {
+            read_frags<A_KMAJ>(smem[cur ^ 1], wm * kWaveTile, 0, lane, fa[0]);
+            read_frags<B_KMAJ>(smem[cur ^ 1] + kStageElems, wn * kWaveTile, 0, lane, fb[0]);
+        }
+    }
+
+    // Epilogue: lane holds row (lane % 16) and columns 4 * (lane / 16) + 0..3
+    // of every 16 x 16 fragment.
+    const bf16* bias = static_cast<const bf16*>(p.bias);
+    const bf16* aux = static_cast<const bf16*>(p.aux);
+    bf16* save = static_cast<bf16*>(p.save);
+    OutT* C = static_cast<OutT*>(p.C);
+#pragma unroll
+    for (int b = 0; b < kFrag; ++b) {
+        const int64_t col = n0 + wn * kWaveTile + b * 16 + 4 * (lane >> 4);
+        if (col >= p.N) continue;
+        float bv[4] = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (EPI == Epi::Bias || EPI == Epi::BiasGelu) {
+            if (bias) {
+                const bf16x4 t4 = *reinterpret_cast<const bf16x4*>(bias + col);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) bv[e] = (float)t4[e];
+            }
+        }
+#pragma unroll
+        for (int a = 0; a < kFrag; ++a) {
+            const int64_t row = m0 + wm * kWaveTile + a * 16 + (lane & 15);
+            if (row >= p.M) continue;
+            const int64_t off = row * p.N + col;
+            float v[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = acc[a][b][e];
+            if constexpr (EPI == Epi::Bias) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] += bv[e];
+            } else if constexpr (EPI == Epi::BiasGelu) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] += bv[e];
+                if (save)
+                    *reinterpret_cast<bf16x4*>(save + off) =
+                        bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = gelu_tanh(v[e]);
+            } else if constexpr (EPI == Epi::DGelu) {
+                const bf16x4 y4 = *reinterpret_cast<const bf16x4*>(aux + off);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] *= gelu_tanh_grad((float)y4[e]);
+            }
+            if constexpr (sizeof(OutT) == 4) {
+                *reinterpret_cast<f32x4*>(C + off) = f32x4{v[0], v[1], v[2], v[3]};
+            } else {
+                *reinterpret_cast<bf16x4*>(C + off) =
+                    bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+            }
+        }
+    }
+}
+
+template <bool AK, bool BK, Epi E, typename O>
+hipError_t launch(const GemmArgs& p, hipStream_t stream)
+{
+    const int tm = (int)((p.M + kTile - 1) / kTile);
+    const int tn = (int)((p.N + kTile - 1) / kTile);
+    hipLaunchKernelGGL((gemm_tile_kernel<AK, BK, E, O>), dim3((unsigned)(tm * tn)),
+                       dim3(kThreads), 0, stream, p, tm, tn);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool gemm_tile_supported(const GemmArgs& p, Layout layout)
+{
+    if (p.M < kTile || p.N < kTile) return false;
+    // A K-major operand must not run past the end of a row inside a slab.
+    if (layout != Layout::TN && p.K % kBK != 0) return false;
+    const int64_t lim = (int64_t(1) << 31) - 1;
+    return p.M * p.K * 2 <= lim && p.N * p.K * 2 <= lim;
+}
+
+hipError_t gemm_tile(const GemmArgs& p, Layout layout, Epi epi, Elt out, hipStream_t stream)
+{
+    switch (layout) {
+    case Layout::NN:
+        if (epi == Epi::BiasGelu) {
+            if (out == Elt::BF16) return launch<true, false, Epi::BiasGelu, bf16>(p, stream);
+            return launch<true, false, Epi::BiasGelu, float>(p, stream);
+        }
+        if (epi == Epi::Bias) {
+            if (out == Elt::BF16) return launch<true, false, Epi::Bias, bf16>(p, stream);
+            return launch<true, false, Epi::Bias, float>(p, stream);
+        }
+        if (out == Elt::BF16) return launch<true, false, Epi::Store, bf16>(p, stream);
+        return launch<true, false, Epi::Store, float>(p, stream);
+    case Layout::NT:
+        if (epi == Epi::DGelu) {
+            if (out == Elt::BF16) return launch<true, true, Epi::DGelu, bf16>(p, stream);
+            return launch<true, true, Epi::DGelu, float>(p, stream);
+        }
+        if (out == Elt::BF16) return launch<true, true, Epi::Store, bf16>(p, stream);
+        return launch<true, true, Epi::Store, float>(p, stream);
+    case Layout::TN:
+        return launch<false, false, Epi::Store, float>(p, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace tpmlp

@@ -140,6 +140,8 @@ REDUCED = [
     (1, 64, 256, 2),         # a single token
     (130, 136, 1088, 8),     # n = 136, h = 136
     (256, 512, 2048, 8),     # exact tiles
+    (270, 328, 2624, 8),     # K = 328 not a multiple of 64; ragged K = 270 in x^T dy
+    (520, 768, 4096, 8),     # two 256-row tiles + 8 rows, 512-wide shard
 ]
 
 
