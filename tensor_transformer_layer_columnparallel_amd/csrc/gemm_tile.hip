@@ -1,16 +1,19 @@
 // Large-tile bf16 MFMA GEMM for gfx950: C[M,N] = epi( op(A)[M,K] * op(B)[K,N] ).
 //
-// Workgroup: 256 threads = 4 waves in a 2 x 2 grid, a 256 x 256 output tile
-// per workgroup, 128 x 128 per wave (8 x 8 MFMA 16x16x32 bf16 tiles, fp32
-// accumulators).  K advances in slabs of 64.
+// Workgroup: 256 threads = 4 waves in a 2 x 2 grid, a 256 x BN output tile
+// per workgroup (BN = 256 or 192), 128 x BN/2 per wave (8 x BN/32 MFMA
+// 16x16x32 bf16 tiles, fp32 accumulators).  K advances in slabs of 64.
+// BN = 192 exists for wave quantisation: the six products of the GPT-3-shaped
+// shard (M = 2048 with N = 6144 or 12288, and the 6144 x 12288 weight
+// gradients) all split into whole multiples of 256 tiles of 256 x 192.
 //
 // HBM -> LDS: buffer_load_dwordx4 ... lds (each lane's 16 bytes land directly
 // in LDS, no VGPR staging).  Buffer loads clamp to the operand's extent, so a
 // ragged M or N tail reads zeros (or stays inside the operand) and can never
 // fault.  Two LDS stages: slab k+1 streams in while slab k is multiplied.
 //
-// LDS layouts (both 16-byte-chunk XOR swizzled so fragment reads are free of
-// bank conflicts):
+// LDS layouts (16-byte chunks permuted per row so that fragment reads are
+// free of bank conflicts):
 //   K-major operand  [rows][64 k]     read with ds_read_b128 (8 k per lane)
 //   MN-major operand [64 k][rows]     read with ds_read_b64_tr_b16: within a
 //     16-lane group, lane i receives element (i % 4) of the 8-byte pieces
@@ -33,11 +36,10 @@ namespace tpmlp {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kTile = 256;        // BM = BN
+constexpr int kBM = 256;
 constexpr int kBK = 64;
-constexpr int kWaveTile = 128;
-constexpr int kFrag = kWaveTile / 16;   // 8 fragments per wave per dimension
-constexpr int kStageElems = kTile * kBK; // one operand, one stage (bf16 elements)
+constexpr int kWaveM = 128;
+constexpr int kFragM = kWaveM / 16;     // 8 fragments of 16 rows per wave
 constexpr int kXcds = 8;
 
 // Third descriptor word of a raw buffer resource on gfx9-family GPUs.
@@ -56,76 +58,113 @@ __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rsrc, bf16* ld
                                              0, 0);
 }
 
-// Chunk swizzles (16-byte chunks).  K-major rows hold 8 chunks; the read of
-// a 16-lane group touches 16 consecutive rows at one logical chunk.
-__device__ __forceinline__ int swz_kmaj(int row) { return (row >> 1) & 7; }
-// MN-major rows hold kTile/8 = 32 chunks; a transposed read touches rows
-// 4j..4j+3 (j = group) at one chunk pair.  Even values keep chunk pairs
-// together.
-__device__ __forceinline__ int swz_mnmaj(int krow) { return 2 * ((krow & 3) | (((krow >> 3) & 1) << 2)); }
+// K-major slab [R rows][64 k]: 8 chunks per row, XOR-permuted by row so that
+// the 16 rows read by one 16-lane group hit distinct banks (whether the LDS
+// serves 8 or 16 lanes of a 16-byte read per cycle).
+__device__ __forceinline__ int swz_kmaj(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
-// Issues the loads of one 256 x 64 operand slab into LDS stage `s`.
-//   K-major  [rows][K]: 8 rows x 8 chunks per instruction, 8 instructions.
-//   MN-major [K][rows]: 2 k-rows x 32 chunks per instruction, 8 instructions.
-template <bool KMAJ>
+// MN-major slab [64 k][R cols]: R/8 chunks per k-row, permuted in pairs (a
+// transposed read covers 16 columns = one chunk pair) by a k-row-dependent
+// amount so that the 16 k-rows one read instruction touches land on
+// distinct banks.  R = 256 (16 pairs): rotation of the pairs.  R = 192
+// (12 pairs, where a rotation would wrap unevenly): XOR inside aligned
+// blocks of 4 pairs.
+__device__ __forceinline__ int rot_mnmaj(int krow) { return (krow & 3) + 4 * ((krow >> 3) & 1); }
+__device__ __forceinline__ int xor_mnmaj(int krow)
+{
+    return ((krow >> 1) & 1) + 2 * ((krow & 1) ^ ((krow >> 3) & 1));
+}
+
+template <int R>
+__device__ __forceinline__ int mn_phys_chunk(int krow, int logical_chunk)
+{
+    int pair = logical_chunk >> 1;
+    if constexpr (R == 256) {
+        pair += rot_mnmaj(krow);
+        if (pair >= 16) pair -= 16;
+    } else {
+        pair ^= xor_mnmaj(krow);
+    }
+    return 2 * pair + (logical_chunk & 1);
+}
+
+template <int R>
+__device__ __forceinline__ int mn_logical_chunk(int krow, int phys_chunk)
+{
+    int pair = phys_chunk >> 1;
+    if constexpr (R == 256) {
+        pair -= rot_mnmaj(krow);
+        if (pair < 0) pair += 16;
+    } else {
+        pair ^= xor_mnmaj(krow);
+    }
+    return 2 * pair + (phys_chunk & 1);
+}
+
+// Loads of one R x 64 operand slab (R = 256 or 192 rows of M or N) into an
+// LDS stage.  The slab is R * 8 chunks of 16 bytes; instruction j of wave w
+// fills chunks [(w * R/32 + j) * 64, +64), one per lane, contiguously.
+template <bool KMAJ, int R>
 struct SlabDma {
-    uint32_t voff[8];   // per-instruction byte offsets of this lane (k slab 0)
-    uint32_t kstep;     // bytes to advance one slab along K
+    static constexpr int kPerWave = R / 32;
+    uint32_t voff[kPerWave];   // byte offsets of this lane, slab 0
+    uint32_t kstep;            // bytes to advance one slab along K
 
     __device__ __forceinline__ void init(int wave, int lane, int64_t r0, int64_t ld)
     {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < kPerWave; ++j) {
+            const int linear = (wave * kPerWave + j) * 64 + lane;
             if (KMAJ) {
-                const int row = wave * 64 + j * 8 + (lane >> 3);
-                const int chunk = (lane & 7) ^ swz_kmaj(row);
+                const int row = linear >> 3;
+                const int chunk = (linear & 7) ^ swz_kmaj(row);
                 voff[j] = (uint32_t)(((r0 + row) * ld + chunk * 8) * 2);
             } else {
-                const int krow = wave * 16 + j * 2 + (lane >> 5);
-                const int chunk = (lane & 31) ^ swz_mnmaj(krow);
+                const int krow = linear / (R / 8);
+                const int chunk = mn_logical_chunk<R>(krow, linear % (R / 8));
                 voff[j] = (uint32_t)((krow * ld + r0 + chunk * 8) * 2);
             }
         }
         kstep = KMAJ ? (uint32_t)(kBK * 2) : (uint32_t)(kBK * ld * 2);
     }
 
-    __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rsrc, bf16* stage, int wave,
+    __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rsrc, bf16* slab, int wave,
                                           uint32_t soff) const
     {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            bf16* dst = KMAJ ? stage + (wave * 64 + j * 8) * kBK
-                             : stage + (wave * 16 + j * 2) * kTile;
-            load_lds16(rsrc, dst, voff[j], soff);
-        }
+        for (int j = 0; j < kPerWave; ++j)
+            load_lds16(rsrc, slab + (wave * kPerWave + j) * 64 * 8, voff[j], soff);
     }
 };
 
-// Fragment reads for one 32-wide k half (ks) of a stage: 8 fragments of 16
+// Fragment reads for one 32-wide k half (ks) of a slab: NF fragments of 16
 // rows (M for A, N for B) x 32 k, 8 bf16 per lane.
-template <bool KMAJ>
-__device__ __forceinline__ void read_frags(const bf16* stage, int wrow0, int ks, int lane,
-                                           bf16x8 (&f)[kFrag])
+template <bool KMAJ, int R, int NF>
+__device__ __forceinline__ void read_frags(const bf16* slab, int wrow0, int ks, int lane,
+                                           bf16x8 (&f)[NF])
 {
     const int i = lane & 15, g = lane >> 4;
     if constexpr (KMAJ) {
         const int chunk = (ks * 4 + g) ^ swz_kmaj(i);
 #pragma unroll
-        for (int q = 0; q < kFrag; ++q) {
+        for (int q = 0; q < NF; ++q) {
             const int row = wrow0 + q * 16 + i;
-            f[q] = *reinterpret_cast<const bf16x8*>(stage + row * kBK + chunk * 8);
+            f[q] = *reinterpret_cast<const bf16x8*>(slab + row * kBK + chunk * 8);
         }
     } else {
-        const int sw = 2 * ((i >> 2) | ((g & 1) << 2));   // swz_mnmaj of the k-rows read
+        // Lane 4e + c of each 16-lane group points at k-row e, columns
+        // 4c..4c+3 of the fragment; the transposed read hands every lane four
+        // consecutive k of its own column.
         const int krow0 = ks * 32 + g * 8 + (i >> 2);
 #pragma unroll
-        for (int q = 0; q < kFrag; ++q) {
+        for (int q = 0; q < NF; ++q) {
             const int col = wrow0 + q * 16 + 4 * (i & 3);
-            const int chunk = ((col >> 3) ^ sw);
             bf16x4 half[2];
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
-                const bf16* p = stage + (krow0 + 4 * hh) * kTile + chunk * 8 + (col & 7);
+                const int krow = krow0 + 4 * hh;
+                const int chunk = mn_phys_chunk<R>(krow, col >> 3);
+                const bf16* p = slab + krow * R + chunk * 8 + (col & 7);
                 const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                     (TP_LDS i16x4*)((TP_LDS bf16*)p));
                 half[hh] = __builtin_bit_cast(bf16x4, v);
@@ -136,11 +175,14 @@ __device__ __forceinline__ void read_frags(const bf16* stage, int wrow0, int ks,
     }
 }
 
-template <bool A_KMAJ, bool B_KMAJ, Epi EPI, typename OutT>
+template <int BN, bool A_KMAJ, bool B_KMAJ, Epi EPI, typename OutT>
 __global__ __launch_bounds__(kThreads, 1) void gemm_tile_kernel(GemmArgs p, int tiles_m,
                                                                 int tiles_n)
 {
-    __shared__ __attribute__((aligned(1024))) bf16 smem[2][2 * kStageElems];
+    constexpr int kWaveN = BN / 2;
+    constexpr int kFragN = kWaveN / 16;
+    constexpr int kSlabA = kBM * kBK, kSlabB = BN * kBK;   // elements
+    __shared__ __attribute__((aligned(1024))) bf16 smem[2][kSlabA + kSlabB];
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -152,33 +194,34 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tile_kernel(GemmArgs p, int 
     int tile = blockIdx.x;
     if (ntiles % kXcds == 0) tile = (tile % kXcds) * (ntiles / kXcds) + tile / kXcds;
     const int tm = tile % tiles_m, tn = tile / tiles_m;
-    const int64_t m0 = (int64_t)tm * kTile, n0 = (int64_t)tn * kTile;
+    const int64_t m0 = (int64_t)tm * kBM, n0 = (int64_t)tn * BN;
 
     const bf16* A = static_cast<const bf16*>(p.A);
     const bf16* B = static_cast<const bf16*>(p.B);
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(A, (uint32_t)(p.M * p.K * 2));
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(B, (uint32_t)(p.N * p.K * 2));
 
-    SlabDma<A_KMAJ> da;
-    SlabDma<B_KMAJ> db;
+    SlabDma<A_KMAJ, kBM> da;
+    SlabDma<B_KMAJ, BN> db;
     da.init(wave, lane, m0, A_KMAJ ? p.K : p.M);
     db.init(wave, lane, n0, B_KMAJ ? p.K : p.N);
 
-    f32x4 acc[kFrag][kFrag];
+    f32x4 acc[kFragM][kFragN];
 #pragma unroll
-    for (int a = 0; a < kFrag; ++a)
+    for (int a = 0; a < kFragM; ++a)
 #pragma unroll
-        for (int b = 0; b < kFrag; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int b = 0; b < kFragN; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int nk = (int)((p.K + kBK - 1) / kBK);
-    bf16x8 fa[2][kFrag], fb[2][kFrag];
+    bf16x8 fa[2][kFragM], fb[2][kFragN];
+    const int wrow_a = wm * kWaveM, wrow_b = wn * kWaveN;
 
     if (nk > 0) {
         da.issue(ra, smem[0], wave, 0);
-        db.issue(rb, smem[0] + kStageElems, wave, 0);
+        db.issue(rb, smem[0] + kSlabA, wave, 0);
         __syncthreads();
-        read_frags<A_KMAJ>(smem[0], wm * kWaveTile, 0, lane, fa[0]);
-        read_frags<B_KMAJ>(smem[0] + kStageElems, wn * kWaveTile, 0, lane, fb[0]);
+        read_frags<A_KMAJ, kBM>(smem[0], wrow_a, 0, lane, fa[0]);
+        read_frags<B_KMAJ, BN>(smem[0] + kSlabA, wrow_b, 0, lane, fb[0]);
     }
 
     // Per slab: read the second k half of the current stage, then start the
@@ -188,30 +231,30 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tile_kernel(GemmArgs p, int 
     // the 128 MFMAs of this slab instead of before them.
     for (int kt = 0; kt < nk; ++kt) {
         const int cur = kt & 1;
-        read_frags<A_KMAJ>(smem[cur], wm * kWaveTile, 1, lane, fa[1]);
-        read_frags<B_KMAJ>(smem[cur] + kStageElems, wn * kWaveTile, 1, lane, fb[1]);
+        read_frags<A_KMAJ, kBM>(smem[cur], wrow_a, 1, lane, fa[1]);
+        read_frags<B_KMAJ, BN>(smem[cur] + kSlabA, wrow_b, 1, lane, fb[1]);
         if (kt + 1 < nk) {
             da.issue(ra, smem[cur ^ 1], wave, (uint32_t)(kt + 1) * da.kstep);
-            db.issue(rb, smem[cur ^ 1] + kStageElems, wave, (uint32_t)(kt + 1) * db.kstep);
+            db.issue(rb, smem[cur ^ 1] + kSlabA, wave, (uint32_t)(kt + 1) * db.kstep);
         }
 #pragma unroll
-        for (int a = 0; a < kFrag; ++a)
+        for (int a = 0; a < kFragM; ++a)
 #pragma unroll
-            for (int b = 0; b < kFrag; ++b)
+            for (int b = 0; b < kFragN; ++b)
                 acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[0][b], fa[0][a], acc[a][b],
                                                                      0, 0, 0);
 #pragma unroll
-        for (int a = 0; a < kFrag; ++a)
+        for (int a = 0; a < kFragM; ++a)
 #pragma unroll
-            for (int b = 0; b < kFrag; ++b)
+            for (int b = 0; b < kFragN; ++b)
                 acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[1][b], fa[1][a], acc[a][b],
                                                                      0, 0, 0);
         // Keep the MFMAs above the barrier: its fence waits for the DMA.
         __builtin_amdgcn_sched_barrier(0);
         __syncthreads();
         if (kt + 1 < nk) {
-            read_frags<A_KMAJ>(smem[cur ^ 1], wm * kWaveTile, 0, lane, fa[0]);
-            read_frags<B_KMAJ>(smem[cur ^ 1] + kStageElems, wn * kWaveTile, 0, lane, fb[0]);
+            read_frags<A_KMAJ, kBM>(smem[cur ^ 1], wrow_a, 0, lane, fa[0]);
+            read_frags<B_KMAJ, BN>(smem[cur ^ 1] + kSlabA, wrow_b, 0, lane, fb[0]);
         }
     }
 
@@ -222,8 +265,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tile_kernel(GemmArgs p, int 
     bf16* save = static_cast<bf16*>(p.save);
     OutT* C = static_cast<OutT*>(p.C);
 #pragma unroll
-    for (int b = 0; b < kFrag; ++b) {
-        const int64_t col = n0 + wn * kWaveTile + b * 16 + 4 * (lane >> 4);
+    for (int b = 0; b < kFragN; ++b) {
+        const int64_t col = n0 + wrow_b + b * 16 + 4 * (lane >> 4);
         if (col >= p.N) continue;
         float bv[4] = {0.f, 0.f, 0.f, 0.f};
         if constexpr (EPI == Epi::Bias || EPI == Epi::BiasGelu) {
@@ -234,8 +277,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tile_kernel(GemmArgs p, int 
             }
         }
 #pragma unroll
-        for (int a = 0; a < kFrag; ++a) {
-            const int64_t row = m0 + wm * kWaveTile + a * 16 + (lane & 15);
+        for (int a = 0; a < kFragM; ++a) {
+            const int64_t row = m0 + wrow_a + a * 16 + (lane & 15);
             if (row >= p.M) continue;
             const int64_t off = row * p.N + col;
             float v[4];
@@ -267,21 +310,46 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tile_kernel(GemmArgs p, int 
     }
 }
 
+constexpr int kCUs = 256;   // MI355X compute units
+
+// Fraction of the chip's MFMA time that does useful work for a tile width:
+// the tiles of the last partial wave leave CUs idle, and ragged tiles
+// compute padding.
+double tile_efficiency(int64_t M, int64_t N, int bn)
+{
+    const int64_t tm = (M + kBM - 1) / kBM, tn = (N + bn - 1) / bn;
+    const int64_t tiles = tm * tn;
+    const int64_t waves = (tiles + kCUs - 1) / kCUs;
+    return (double)(M * N) / ((double)waves * kCUs * kBM * bn);
+}
+
+int pick_bn(int64_t M, int64_t N)
+{
+    return tile_efficiency(M, N, 192) > tile_efficiency(M, N, 256) + 1e-9 ? 192 : 256;
+}
+
+template <int BN, bool AK, bool BK, Epi E, typename O>
+hipError_t launch_bn(const GemmArgs& p, hipStream_t stream)
+{
+    const int tm = (int)((p.M + kBM - 1) / kBM);
+    const int tn = (int)((p.N + BN - 1) / BN);
+    hipLaunchKernelGGL((gemm_tile_kernel<BN, AK, BK, E, O>), dim3((unsigned)(tm * tn)),
+                       dim3(kThreads), 0, stream, p, tm, tn);
+    return hipGetLastError();
+}
+
 template <bool AK, bool BK, Epi E, typename O>
 hipError_t launch(const GemmArgs& p, hipStream_t stream)
 {
-    const int tm = (int)((p.M + kTile - 1) / kTile);
-    const int tn = (int)((p.N + kTile - 1) / kTile);
-    hipLaunchKernelGGL((gemm_tile_kernel<AK, BK, E, O>), dim3((unsigned)(tm * tn)),
-                       dim3(kThreads), 0, stream, p, tm, tn);
-    return hipGetLastError();
+    if (pick_bn(p.M, p.N) == 192) return launch_bn<192, AK, BK, E, O>(p, stream);
+    return launch_bn<256, AK, BK, E, O>(p, stream);
 }
 
 }  // namespace
 
 bool gemm_tile_supported(const GemmArgs& p, Layout layout)
 {
-    if (p.M < kTile || p.N < kTile) return false;
+    if (p.M < kBM || p.N < 192) return false;
     // A K-major operand must not run past the end of a row inside a slab.
     if (layout != Layout::TN && p.K % kBK != 0) return false;
     const int64_t lim = (int64_t(1) << 31) - 1;

@@ -142,6 +142,7 @@ REDUCED = [
     (256, 512, 2048, 8),     # exact tiles
     (270, 328, 2624, 8),     # K = 328 not a multiple of 64; ragged K = 270 in x^T dy
     (520, 768, 4096, 8),     # two 256-row tiles + 8 rows, 512-wide shard
+    (64, 4096, 8192, 2),     # 4096 x 4096 weight gradients: 256-wide tiles
 ]
 
 
