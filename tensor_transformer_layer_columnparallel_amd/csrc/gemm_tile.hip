@@ -1,8 +1,10 @@
 // Large-tile bf16 MFMA GEMM for gfx950: C[M,N] = epi( op(A)[M,K] * op(B)[K,N] ).
 //
-// Workgroup: 256 threads = 4 waves in a 2 x 2 grid, a 256 x BN output tile
-// per workgroup (BN = 256 or 192), 128 x BN/2 per wave (8 x BN/32 MFMA
-// 16x16x32 bf16 tiles, fp32 accumulators).  K advances in slabs of 64.
+// Workgroup: 512 threads = 8 waves (two per SIMD) in a 4 x 2 grid, a
+// 256 x BN output tile per workgroup (BN = 256 or 192), 64 x BN/2 per wave
+// (4 x BN/32 MFMA 16x16x32 bf16 tiles, fp32 accumulators).  K advances in
+// slabs of 64.  Two waves per SIMD let one wave's LDS and barrier waits
+// overlap the other's MFMAs.
 // BN = 192 exists for wave quantisation: the six products of the GPT-3-shaped
 // shard (M = 2048 with N = 6144 or 12288, and the 6144 x 12288 weight
 // gradients) all split into whole multiples of 256 tiles of 256 x 192.
@@ -11,6 +13,9 @@
 // in LDS, no VGPR staging).  Buffer loads clamp to the operand's extent, so a
 // ragged M or N tail reads zeros (or stays inside the operand) and can never
 // fault.  Two LDS stages: slab k+1 streams in while slab k is multiplied.
+// (All LDS reads of a stage are issued before the DMA into the other stage:
+// the compiler cannot tell the two stages apart and waits for the DMA
+// before any LDS read that follows it in program order.)
 //
 // LDS layouts (16-byte chunks permuted per row so that fragment reads are
 // free of bank conflicts):
@@ -35,12 +40,19 @@
 namespace tpmlp {
 namespace {
 
-constexpr int kThreads = 256;
 constexpr int kBM = 256;
 constexpr int kBK = 64;
-constexpr int kWaveM = 128;
-constexpr int kFragM = kWaveM / 16;     // 8 fragments of 16 rows per wave
 constexpr int kXcds = 8;
+#ifndef TPMLP_TILE_WAVES_M
+#define TPMLP_TILE_WAVES_M 4
+#endif
+#ifndef TPMLP_TILE_WAVES_N
+#define TPMLP_TILE_WAVES_N 2
+#endif
+constexpr int kWavesM = TPMLP_TILE_WAVES_M;   // wave grid of a workgroup
+constexpr int kWavesN = TPMLP_TILE_WAVES_N;
+constexpr int kWaves = kWavesM * kWavesN;
+constexpr int kThreads = 64 * kWaves;
 
 // Third descriptor word of a raw buffer resource on gfx9-family GPUs.
 constexpr int kRsrcWord3 = 0x00020000;
@@ -103,10 +115,11 @@ __device__ __forceinline__ int mn_logical_chunk(int krow, int phys_chunk)
 
 // Loads of one R x 64 operand slab (R = 256 or 192 rows of M or N) into an
 // LDS stage.  The slab is R * 8 chunks of 16 bytes; instruction j of wave w
-// fills chunks [(w * R/32 + j) * 64, +64), one per lane, contiguously.
+// fills chunks [(w * kPerWave + j) * 64, +64), one per lane, contiguously.
 template <bool KMAJ, int R>
 struct SlabDma {
-    static constexpr int kPerWave = R / 32;
+    static constexpr int kPerWave = R / 8 / kWaves;
+    static_assert(kPerWave * kWaves * 8 == R, "slab does not split evenly over the waves");
     uint32_t voff[kPerWave];   // byte offsets of this lane, slab 0
     uint32_t kstep;            // bytes to advance one slab along K
 
@@ -179,14 +192,16 @@ template <int BN, bool A_KMAJ, bool B_KMAJ, Epi EPI, typename OutT>
 __global__ __launch_bounds__(kThreads, 1) void gemm_tile_kernel(GemmArgs p, int tiles_m,
                                                                 int tiles_n)
 {
-    constexpr int kWaveN = BN / 2;
+    constexpr int kWaveM = kBM / kWavesM;
+    constexpr int kWaveN = BN / kWavesN;
+    constexpr int kFragM = kWaveM / 16;
     constexpr int kFragN = kWaveN / 16;
     constexpr int kSlabA = kBM * kBK, kSlabB = BN * kBK;   // elements
     __shared__ __attribute__((aligned(1024))) bf16 smem[2][kSlabA + kSlabB];
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / kWavesN, wn = wave % kWavesN;
 
     // XCD-aware tile order: the tiles of one XCD form a contiguous run of the
     // m-fastest tile sequence.
