@@ -55,7 +55,76 @@ def stored_traffic():
         return None
     if c.get("kernel_source_digest") != kernel_source_digest():
         return None
-    return c.get("hbm_bytes_per_launch")
+    b = c.get("hbm_bytes_per_launch")
+    return None if b is None else int(round(b))
+
+
+COLUMN_KERNEL_KEYS = ("gemm_tile_kernelILi192ELb1ELb0ELNS_3EpiE2EDF16b",
+                      "gemm_tile_kernel<192, true, false, (tpmlp::Epi)2, __bf16>")
+COPY_KERNEL_KEYS = ("shard_concat_kernel",)
+
+
+def _counter_per_dispatch(csv_dir: str, counter: str, keys) -> float:
+    """Mean over dispatches of `counter` (summed over its instances) for the
+    kernels whose name contains one of `keys`, from a rocprofv3 --pmc CSV."""
+    import csv
+    import glob
+    per = {}
+    for path in glob.glob(os.path.join(csv_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                if row["Counter_Name"] != counter:
+                    continue
+                if not any(k in row["Kernel_Name"] for k in keys):
+                    continue
+                per[row["Dispatch_Id"]] = per.get(row["Dispatch_Id"], 0.0) + float(row["Counter_Value"])
+    if not per:
+        raise SystemExit(f"no {counter} samples for {keys} under {csv_dir}")
+    return sum(per.values()) / len(per)
+
+
+def ingest_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, commands):
+    """Turns four rocprofv3 --pmc runs (FETCH_SIZE and WRITE_SIZE of the bench
+    and of the calibration copy) into HBM bytes per launch of the column GEMM.
+    The counters report KiB; each is scaled by the ratio of the copy's known
+    byte count to what the same counter reads for the copy."""
+    copy_bytes = COPY_ROWS * COPY_COLS * 4
+    f_col = _counter_per_dispatch(fetch_dir, "FETCH_SIZE", COLUMN_KERNEL_KEYS)
+    w_col = _counter_per_dispatch(write_dir, "WRITE_SIZE", COLUMN_KERNEL_KEYS)
+    f_cp = _counter_per_dispatch(copy_fetch_dir, "FETCH_SIZE", COPY_KERNEL_KEYS)
+    w_cp = _counter_per_dispatch(copy_write_dir, "WRITE_SIZE", COPY_KERNEL_KEYS)
+    f_scale = copy_bytes / (f_cp * 1024)
+    w_scale = copy_bytes / (w_cp * 1024)
+    read_b = f_col * 1024 * f_scale
+    write_b = w_col * 1024 * w_scale
+    out = {"kernel": COLUMN_KERNEL_KEYS[1], "kernel_source_digest": kernel_source_digest(),
+           "fetch_kib_raw": f_col, "write_kib_raw": w_col,
+           "copy_bytes": copy_bytes, "copy_fetch_kib_raw": f_cp, "copy_write_kib_raw": w_cp,
+           "fetch_scale": f_scale, "write_scale": w_scale,
+           "hbm_read_bytes_per_launch": read_b, "hbm_write_bytes_per_launch": write_b,
+           "hbm_bytes_per_launch": read_b + write_b, "commands": commands}
+    os.makedirs(os.path.dirname(COUNTERS_FILE), exist_ok=True)
+    with open(COUNTERS_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
+
+
+COPY_ROWS, COPY_COLS = 8192, 8192
+
+
+def copy_calibration(reps: int):
+    """A plain device copy of known size (8192 x 8192 fp32 = 256 MiB read and
+    written), issued through the library's concatenation with t = 1."""
+    import torch
+    from tensor_transformer_layer_columnparallel_amd import binding as B
+    src = torch.randn(1, COPY_ROWS, COPY_COLS, device="cuda")
+    dst = torch.empty(COPY_ROWS, COPY_COLS, device="cuda")
+    for _ in range(reps):
+        B.tp_shard_reduce(src, dst, COPY_ROWS, COPY_COLS, 1, B.TP_REDUCE_CONCAT, torch.float32,
+                          torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(src[0], dst)
+    log(f"copy calibration: {reps} copies of {COPY_ROWS * COPY_COLS * 4} bytes")
 
 
 def cpu_baseline(w, d_h, seconds: float):
@@ -94,7 +163,19 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="wall-clock budget of the oracle baseline (0 disables it)")
     ap.add_argument("--no-reduce", action="store_true", help="skip the shard-sum measurement")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="REPS",
+                    help="only run the HBM-counter calibration copy REPS times")
+    ap.add_argument("--ingest-counters", nargs=4,
+                    metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+                    help="turn rocprofv3 --pmc CSV output into the stored traffic figure")
+    ap.add_argument("--counter-commands", default="", help="commands recorded with the counters")
     args = ap.parse_args()
+    if args.ingest_counters:
+        ingest_counters(*args.ingest_counters, commands=args.counter_commands)
+        return
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build runs one tensor-parallel rank's "
               "shard per GPU and has no multi-GPU exchange; run with --gpus 1.", flush=True)
