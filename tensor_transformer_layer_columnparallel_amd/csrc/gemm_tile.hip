@@ -10,9 +10,9 @@
 // gradients) all split into whole multiples of 256 tiles of 256 x 192.
 //
 // HBM -> LDS: buffer_load_dwordx4 ... lds (each lane's 16 bytes land directly
-// in LDS, no VGPR staging).  Buffer loads clamp to the operand's extent, so a
-// ragged M or N tail reads zeros (or stays inside the operand) and can never
-// fault.  Two LDS stages: slab k+1 streams in while slab k is multiplied.
+// in LDS, no VGPR staging).  Elements outside the operand (ragged M, N or K
+// tails) are given a per-lane offset beyond the buffer descriptor's extent,
+// which returns zeros; every other address stays inside the operand.  Two LDS stages: slab k+1 streams in while slab k is multiplied.
 // (All LDS reads of a stage are issued before the DMA into the other stage:
 // the compiler cannot tell the two stages apart and waits for the DMA
 // before any LDS read that follows it in program order.)
@@ -120,33 +120,55 @@ template <bool KMAJ, int R>
 struct SlabDma {
     static constexpr int kPerWave = R / 8 / kWaves;
     static_assert(kPerWave * kWaves * 8 == R, "slab does not split evenly over the waves");
-    uint32_t voff[kPerWave];   // byte offsets of this lane, slab 0
+    // Byte offsets of this lane for slab 0.  Out-of-range elements are given
+    // the offset 0x80000000, beyond any operand (< 2^31 bytes), so the buffer
+    // descriptor returns zeros for them; only the per-lane offset is relied on
+    // for that, never the scalar one.
+    static constexpr uint32_t kInvalid = 0x80000000u;
+    uint32_t voff[kPerWave];
+    int krow[kPerWave];        // MN-major: k-row of the slab this lane loads
     uint32_t kstep;            // bytes to advance one slab along K
+    int64_t K;
 
-    __device__ __forceinline__ void init(int wave, int lane, int64_t r0, int64_t ld)
+    __device__ __forceinline__ void init(int wave, int lane, int64_t r0, int64_t ld,
+                                         int64_t extent, int64_t K_)
     {
+        K = K_;
 #pragma unroll
         for (int j = 0; j < kPerWave; ++j) {
             const int linear = (wave * kPerWave + j) * 64 + lane;
             if (KMAJ) {
                 const int row = linear >> 3;
                 const int chunk = (linear & 7) ^ swz_kmaj(row);
-                voff[j] = (uint32_t)(((r0 + row) * ld + chunk * 8) * 2);
+                voff[j] = r0 + row < extent ? (uint32_t)(((r0 + row) * ld + chunk * 8) * 2)
+                                            : kInvalid;
+                krow[j] = 0;
             } else {
-                const int krow = linear / (R / 8);
-                const int chunk = mn_logical_chunk<R>(krow, linear % (R / 8));
-                voff[j] = (uint32_t)((krow * ld + r0 + chunk * 8) * 2);
+                krow[j] = linear / (R / 8);
+                const int chunk = mn_logical_chunk<R>(krow[j], linear % (R / 8));
+                voff[j] = r0 + chunk * 8 < extent ? (uint32_t)((krow[j] * ld + r0 + chunk * 8) * 2)
+                                                  : kInvalid;
             }
         }
         kstep = KMAJ ? (uint32_t)(kBK * 2) : (uint32_t)(kBK * ld * 2);
     }
 
+    // K-major: K is a multiple of the slab depth, so the slab offset (scalar)
+    // keeps every in-range row inside the operand.  MN-major: the slab offset
+    // is added per lane, and k-rows past K are invalidated.
     __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rsrc, bf16* slab, int wave,
-                                          uint32_t soff) const
+                                          int kt) const
     {
 #pragma unroll
-        for (int j = 0; j < kPerWave; ++j)
-            load_lds16(rsrc, slab + (wave * kPerWave + j) * 64 * 8, voff[j], soff);
+        for (int j = 0; j < kPerWave; ++j) {
+            bf16* dst = slab + (wave * kPerWave + j) * 64 * 8;
+            if (KMAJ) {
+                load_lds16(rsrc, dst, voff[j], (uint32_t)kt * kstep);
+            } else {
+                const bool ok = voff[j] != kInvalid && (int64_t)kt * kBK + krow[j] < K;
+                load_lds16(rsrc, dst, ok ? voff[j] + (uint32_t)kt * kstep : kInvalid, 0u);
+            }
+        }
     }
 };
 
@@ -218,8 +240,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tile_kernel(GemmArgs p, int 
 
     SlabDma<A_KMAJ, kBM> da;
     SlabDma<B_KMAJ, BN> db;
-    da.init(wave, lane, m0, A_KMAJ ? p.K : p.M);
-    db.init(wave, lane, n0, B_KMAJ ? p.K : p.N);
+    da.init(wave, lane, m0, A_KMAJ ? p.K : p.M, p.M, p.K);
+    db.init(wave, lane, n0, B_KMAJ ? p.K : p.N, p.N, p.K);
 
     f32x4 acc[kFragM][kFragN];
 #pragma unroll
@@ -249,8 +271,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tile_kernel(GemmArgs p, int 
         read_frags<A_KMAJ, kBM>(smem[cur], wrow_a, 1, lane, fa[1]);
         read_frags<B_KMAJ, BN>(smem[cur] + kSlabA, wrow_b, 1, lane, fb[1]);
         if (kt + 1 < nk) {
-            da.issue(ra, smem[cur ^ 1], wave, (uint32_t)(kt + 1) * da.kstep);
-            db.issue(rb, smem[cur ^ 1] + kSlabA, wave, (uint32_t)(kt + 1) * db.kstep);
+            da.issue(ra, smem[cur ^ 1], wave, kt + 1);
+            db.issue(rb, smem[cur ^ 1] + kSlabA, wave, kt + 1);
         }
 #pragma unroll
         for (int a = 0; a < kFragM; ++a)

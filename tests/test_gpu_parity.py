@@ -334,3 +334,50 @@ def test_full_layer_emulation_8_shards_sampled(B):
     W1, b1, W2 = _unsharded(d_h, w.ranks)
     _, _, rZ = oracle.mlp_shard_fwd_rows(d_h["X"], W1, b1, W2, rows)
     assert_close(Zc[rows], rZ, "bf16", "full layer Z rows")
+
+
+def _nan_padded(x, pad=1 << 16):
+    """x on the device, followed inside the same allocation by `pad` NaNs."""
+    flat = torch.full((x.numel() + pad,), float("nan"), dtype=x.dtype, device="cuda")
+    flat[:x.numel()].copy_(x.reshape(-1))
+    return flat, flat[:x.numel()].view(x.shape)
+
+
+@pytest.mark.parametrize("shape", [(270, 512, 2048, 8), (300, 384, 1024, 4), (520, 768, 4096, 8)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_ragged_tails_touch_nothing_past_the_operands(B, shape):
+    # Ragged token counts (the K of the x^T dy products) and shard widths that
+    # are not multiples of the tile (ragged N of the forward products): every
+    # operand and output sits at the start of an allocation whose remaining
+    # bytes are NaN.  A read past an operand would put NaN into the results;
+    # a write past an output would overwrite the NaN tail.
+    T, h, ffn, t = shape
+    w = configs.scaled(configs.GPT3_SHARD, "ragged_pad", T=T, h=h, ffn=ffn, t=t)
+    n = w.n
+    _log(f"case padded ragged {shape}")
+    d_h = synth.make_inputs(w)
+    bufs, dev_in = {}, {}
+    for k, x in (("X", d_h["X"]), ("W1", d_h["W1"][0]), ("b1", d_h["b1"][0]),
+                 ("W2", d_h["W2"][0]), ("dZ", d_h["dZ"])):
+        bufs[k], dev_in[k] = _nan_padded(x.to("cuda"))
+    outs = {}
+    for k, shp, dt in (("H", (T, n), torch.bfloat16), ("Y", (T, n), torch.bfloat16),
+                       ("Z", (T, h), torch.float32), ("dY", (T, n), torch.bfloat16),
+                       ("dW2", (n, h), torch.float32), ("dW1", (h, n), torch.float32),
+                       ("dX", (T, h), torch.float32), ("db1", (n,), torch.float32)):
+        bufs[k], outs[k] = _nan_padded(torch.zeros(shp, dtype=dt, device="cuda"))
+    bf = torch.bfloat16
+    B.tp_mlp_shard_fwd(dev_in["X"], dev_in["W1"], dev_in["b1"], dev_in["W2"], outs["H"], outs["Y"],
+                       outs["Z"], T, h, ffn, t, 0, bf)
+    B.tp_mlp_shard_bwd(dev_in["X"], dev_in["W1"], dev_in["W2"], outs["Y"], outs["H"], dev_in["dZ"],
+                       outs["dY"], outs["dW2"], outs["dW1"], outs["dX"], outs["db1"], T, h, ffn, t,
+                       0, bf)
+    torch.cuda.synchronize()
+    for k, buf in bufs.items():
+        size = (dev_in[k] if k in dev_in else outs[k]).numel()
+        assert torch.isnan(buf[size:]).all(), f"{k}: bytes past the tensor were written"
+    _, _, rZ = oracle.mlp_shard_fwd(d_h["X"], d_h["W1"][0], d_h["b1"][0], d_h["W2"][0])
+    rg = oracle.mlp_shard_bwd(d_h["X"], d_h["W1"][0], d_h["b1"][0], d_h["W2"][0], d_h["dZ"])
+    assert_close(outs["Z"], rZ, "bf16", "padded Z")
+    for k in ("dY", "dW2", "dW1", "dX", "db1"):
+        assert_close(outs[k], rg[k], "bf16", f"padded {k}")
