@@ -59,8 +59,8 @@ def stored_traffic():
     return None if b is None else int(round(b))
 
 
-COLUMN_KERNEL_KEYS = ("gemm_tile_kernelILi192ELb1ELb0ELNS_3EpiE2EDF16b",
-                      "gemm_tile_kernel<192, true, false, (tpmlp::Epi)2, __bf16>")
+COLUMN_KERNEL_KEYS = ("gemm_ring_kernelILi192ELb1ELb0ELNS_3EpiE2EDF16b",
+                      "gemm_ring_kernel<192, true, false, (tpmlp::Epi)2, __bf16>")
 COPY_KERNEL_KEYS = ("shard_concat_kernel",)
 
 

@@ -1,0 +1,439 @@
+// Large-shape bf16 MFMA GEMM for gfx950: C[M,N] = epi( op(A)[M,K] * op(B)[K,N] ).
+//
+// Tiles of 256 x 192 outputs, one workgroup of 8 waves (4 x 2, 64 x 96
+// outputs each, two waves per SIMD), v_mfma_f32_16x16x32_bf16 with fp32
+// accumulators and the B fragment in the first MFMA slot, so that each lane
+// ends with four consecutive columns of one row.  Tiles are numbered so that
+// consecutive workgroups (which the dispatcher spreads round-robin over the
+// 8 XCDs) map to neighbouring tiles on the same XCD and share its L2.
+//
+// K is walked in 32-deep slabs through a ring of 4 LDS stages.  Slabs are
+// copied L2 -> LDS by buffer_load_dwordx4 ... lds (DMA, no VGPR staging),
+// issued from inline assembly: the compiler's wait analysis cannot tell the
+// stages apart and would wait for a DMA just issued before any LDS read.  The
+// waits are explicit instead.  At slab k every wave
+//   1. waits until at most its loads of slabs k+2 and k+3 are outstanding
+//      (the vector memory counter retires loads in issue order), and for its
+//      own LDS reads of stage k;
+//   2. passes a barrier: slab k+1 is now in LDS for everybody, and nobody
+//      reads stage k any more;
+//   3. in four groups, each with one DMA instruction, the MFMAs of one A
+//      fragment and a share of the fragment reads: refills stage k with slab
+//      k+4, multiplies slab k (fragments read during slab k-1) and reads the
+//      fragments of slab k+1.
+// Spreading the memory instructions over the MFMAs keeps the waves of a SIMD
+// from stalling together on a burst of loads while the matrix pipe idles.
+// Loads for slabs past the end of K are issued with an invalid offset (they
+// read nothing and write zeros into stages that are never read), so every
+// wave issues the same number of loads per slab and the counts are static.
+//
+// LDS layouts (16-byte chunks permuted per row for conflict-free reads):
+//   K-major slab  [rows][32 k]: 4 chunks per row, chunk c of row r stored at
+//                 c ^ (((r >> 1) & 3) ^ ((r >> 3) & 1)); read with ds_read_b128.
+//   MN-major slab [32 k][R cols]: chunk pairs rotated by k-row (R = 256, an A
+//                 operand) or XORed in blocks of four (R = 192, a B operand);
+//                 read with ds_read_b64_tr_b16 (lane i of a 16-lane group
+//                 receives halfword i % 4 of the 8-byte pieces of lanes
+//                 4e + i / 4).
+#include "common.h"
+#include "epilogue.h"
+#include "kernels.h"
+
+namespace tpmlp {
+namespace {
+
+constexpr int kBM = 256;
+constexpr int kBK = 32;
+constexpr int kStages = 4;
+constexpr int kWavesM = 4, kWavesN = 2;
+constexpr int kWaves = kWavesM * kWavesN;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kDmaPerOperand = 2;           // DMA instructions per wave per operand and slab
+constexpr int kDmaPerSlab = 2 * kDmaPerOperand;
+constexpr int kGroups = kDmaPerSlab;        // interleave groups per slab
+constexpr int kXcds = 8;
+constexpr int kCUs = 256;
+
+// Raw buffer descriptor (gfx9 family): base, stride 0, byte extent, word 3.
+__device__ __forceinline__ i32x4 make_desc(const void* base, uint32_t bytes)
+{
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    i32x4 d;
+    d[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    d[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu));
+    d[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+    d[3] = 0x00020000;
+    return d;
+}
+
+// One 16-byte-per-lane DMA: lane l's bytes land at LDS byte address
+// lds + 16 l (M0 holds lds).
+__device__ __forceinline__ void dma16(i32x4 desc, uint32_t lds, uint32_t voff, uint32_t soff)
+{
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :
+                 : "s"(lds), "v"(voff), "s"(desc), "s"(soff)
+                 : "memory", "m0");
+}
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt
+// 6:4, lgkmcnt 11:8).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt out of range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+__device__ __forceinline__ void barrier()
+{
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p)
+{
+    return (uint32_t)reinterpret_cast<uintptr_t>((TP_LDS const void*)p);
+}
+
+__device__ __forceinline__ int swz_k(int row) { return ((row >> 1) & 3) ^ ((row >> 3) & 1); }
+
+__device__ __forceinline__ int rot_mn(int krow) { return (krow & 3) + 4 * ((krow >> 3) & 1); }
+__device__ __forceinline__ int xor_mn(int krow)
+{
+    return ((krow >> 1) & 1) + 2 * ((krow & 1) ^ ((krow >> 3) & 1));
+}
+template <int R>
+__device__ __forceinline__ int mn_phys(int krow, int chunk)
+{
+    int pair = chunk >> 1;
+    if constexpr (R == 256) {
+        pair += rot_mn(krow);
+        if (pair >= 16) pair -= 16;
+    } else {
+        pair ^= xor_mn(krow);
+    }
+    return 2 * pair + (chunk & 1);
+}
+template <int R>
+__device__ __forceinline__ int mn_logical(int krow, int phys)
+{
+    int pair = phys >> 1;
+    if constexpr (R == 256) {
+        pair -= rot_mn(krow);
+        if (pair < 0) pair += 16;
+    } else {
+        pair ^= xor_mn(krow);
+    }
+    return 2 * pair + (phys & 1);
+}
+
+// DMA plan of one operand: R rows (M or N) x 32 k per slab = R * 4 chunks =
+// R / 16 instructions of 64 chunks; instruction idx = wave * 2 + j fills
+// chunks [idx * 64, idx * 64 + 64).  Instructions past R / 16 (R = 192) are
+// dummies that read nothing (invalid offset) into a junk LDS area.
+//
+// Only the per-lane offset is used to leave an operand: an element outside
+// it gets the offset 0x80000000, beyond any operand (< 2^31 bytes), and the
+// buffer descriptor returns zeros.  K-major operands advance along K with
+// the scalar offset (K is a multiple of 32, so in-range rows stay inside the
+// operand); slabs past the end reload the last slab into a stage that is
+// never read again.  MN-major operands advance with the per-lane offset, and
+// k-rows past K are invalidated.
+template <bool KMAJ, int R>
+struct DmaPlan {
+    static constexpr int kInstr = R / 16;
+    static constexpr uint32_t kInvalid = 0x80000000u;
+    uint32_t voff[kDmaPerOperand];
+    uint32_t dst[kDmaPerOperand];   // byte offset inside a stage (or the junk area)
+    int krow[kDmaPerOperand];
+    bool real[kDmaPerOperand];
+    uint32_t kstep;
+    int nk;
+    int64_t K;
+
+    __device__ __forceinline__ void init(int wave, int lane, int64_t r0, int64_t ld,
+                                         int64_t extent, int64_t K_, uint32_t operand_off)
+    {
+        K = K_;
+        nk = (int)((K_ + kBK - 1) / kBK);
+        kstep = KMAJ ? (uint32_t)(kBK * 2) : (uint32_t)(kBK * ld * 2);
+#pragma unroll
+        for (int j = 0; j < kDmaPerOperand; ++j) {
+            const int idx = wave * kDmaPerOperand + j;
+            real[j] = idx < kInstr;
+            const int linear = idx * 64 + lane;
+            krow[j] = 0;
+            if (!real[j]) {
+                voff[j] = kInvalid;
+            } else if (KMAJ) {
+                const int row = linear >> 2;
+                const int chunk = (linear & 3) ^ swz_k(row);
+                voff[j] = r0 + row < extent ? (uint32_t)(((r0 + row) * ld + chunk * 8) * 2)
+                                            : kInvalid;
+            } else {
+                krow[j] = linear / (R / 8);
+                const int chunk = mn_logical<R>(krow[j], linear % (R / 8));
+                voff[j] = r0 + chunk * 8 < extent
+                              ? (uint32_t)((krow[j] * ld + r0 + chunk * 8) * 2)
+                              : kInvalid;
+            }
+            dst[j] = real[j] ? operand_off + (uint32_t)idx * 1024u
+                             : (uint32_t)(idx - kInstr) / kDmaPerOperand * 1024u;
+        }
+    }
+    // Instruction j of slab `slab` into the stage at stage_base.  Slabs past
+    // the end of K read nothing (zeros land in a stage that is never used).
+    __device__ __forceinline__ void issue(int j, i32x4 desc, uint32_t stage_base,
+                                          uint32_t junk_base, int slab) const
+    {
+        uint32_t v;
+        if (KMAJ) {
+            v = slab < nk ? voff[j] + (uint32_t)slab * kstep : kInvalid;
+        } else {
+            const bool ok = voff[j] != kInvalid && (int64_t)slab * kBK + krow[j] < K;
+            v = ok ? voff[j] + (uint32_t)slab * kstep : kInvalid;
+        }
+        const uint32_t lds = __builtin_amdgcn_readfirstlane(
+            (int)((real[j] ? stage_base : junk_base) + dst[j]));
+        dma16(desc, lds, v, 0u);
+    }
+};
+
+// One fragment of a 32-k slab: 16 rows (M for A, N for B) starting at row0,
+// 8 bf16 per lane (lane l: row l % 16, k 8 (l / 16) .. 8 (l / 16) + 7).
+template <bool KMAJ, int R>
+__device__ __forceinline__ bf16x8 read_frag(const bf16* slab, int row0, int lane)
+{
+    const int i = lane & 15, g = lane >> 4;
+    if constexpr (KMAJ) {
+        const int chunk = g ^ swz_k(i);
+        return *reinterpret_cast<const bf16x8*>(slab + (row0 + i) * kBK + chunk * 8);
+    } else {
+        const int krow0 = g * 8 + (i >> 2);
+        const int col = row0 + 4 * (i & 3);
+        bf16x4 half[2];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const int krow = krow0 + 4 * hh;
+            const bf16* p = slab + krow * R + mn_phys<R>(krow, col >> 3) * 8 + (col & 7);
+            const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TP_LDS i16x4*)((TP_LDS bf16*)p));
+            half[hh] = __builtin_bit_cast(bf16x4, v);
+        }
+        return bf16x8{half[0][0], half[0][1], half[0][2], half[0][3],
+                      half[1][0], half[1][1], half[1][2], half[1][3]};
+    }
+}
+
+template <int BN, bool A_KMAJ, bool B_KMAJ, Epi EPI, typename OutT>
+__global__ __launch_bounds__(kThreads, 1) void gemm_ring_kernel(GemmArgs p, int tiles_m,
+                                                                int tiles_n)
+{
+    constexpr int kWaveM = kBM / kWavesM, kWaveN = BN / kWavesN;
+    constexpr int kFragM = kWaveM / 16, kFragN = kWaveN / 16;
+    constexpr int kSlabA = kBM * kBK, kSlabB = BN * kBK;   // elements
+    constexpr int kStage = kSlabA + kSlabB;
+    constexpr int kJunkWaves = kWaves - DmaPlan<B_KMAJ, BN>::kInstr / kDmaPerOperand;
+    __shared__ __attribute__((aligned(1024))) bf16 smem[kStages * kStage];
+    __shared__ __attribute__((aligned(1024))) bf16 junk[(kJunkWaves > 0 ? kJunkWaves : 1) * 512];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave / kWavesN, wn = wave % kWavesN;
+
+    const int ntiles = tiles_m * tiles_n;
+    int tile = blockIdx.x;
+    if (ntiles % kXcds == 0) tile = (tile % kXcds) * (ntiles / kXcds) + tile / kXcds;
+    const int tm = tile % tiles_m, tn = tile / tiles_m;
+    const int64_t m0 = (int64_t)tm * kBM, n0 = (int64_t)tn * BN;
+
+    const i32x4 da = make_desc(p.A, (uint32_t)(p.M * p.K * 2));
+    const i32x4 db = make_desc(p.B, (uint32_t)(p.N * p.K * 2));
+    DmaPlan<A_KMAJ, kBM> pa;
+    DmaPlan<B_KMAJ, BN> pb;
+    pa.init(wave, lane, m0, A_KMAJ ? p.K : p.M, p.M, p.K, 0u);
+    pb.init(wave, lane, n0, B_KMAJ ? p.K : p.N, p.N, p.K, (uint32_t)(kSlabA * 2));
+    const uint32_t smem_base = lds_addr(smem);
+    const uint32_t junk_base = lds_addr(junk);
+
+    const int wrow_a = wm * kWaveM, wrow_b = wn * kWaveN;
+    f32x4 acc[kFragM][kFragN];
+#pragma unroll
+    for (int a = 0; a < kFragM; ++a)
+#pragma unroll
+        for (int b = 0; b < kFragN; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    bf16x8 fa[2][kFragM], fb[2][kFragN];
+
+    // The work of one slab is cut into kGroups groups, each holding one DMA
+    // instruction, the MFMAs of one A fragment and a share of the fragment
+    // reads, so that the waves never stall on a burst of memory instructions
+    // while the matrix pipe idles.
+    static_assert(kFragM == kGroups, "one A fragment per group");
+    auto dma_op = [&](int g, int slab) {
+        const uint32_t stage_base = smem_base + (uint32_t)((slab % kStages) * kStage * 2);
+        if (g < kDmaPerOperand) pa.issue(g, da, stage_base, junk_base, slab);
+        else pb.issue(g - kDmaPerOperand, db, stage_base, junk_base, slab);
+    };
+    auto read_group = [&](int g, int slab, int buf) {
+        const bf16* st = smem + (slab % kStages) * kStage;
+        fa[buf][g] = read_frag<A_KMAJ, kBM>(st, wrow_a + g * 16, lane);
+#pragma unroll
+        for (int q = g; q < kFragN; q += kGroups)
+            fb[buf][q] = read_frag<B_KMAJ, BN>(st + kSlabA, wrow_b + q * 16, lane);
+    };
+    auto mfma_group = [&](int g, int buf) {
+#pragma unroll
+        for (int b = 0; b < kFragN; ++b)
+            acc[g][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[buf][b], fa[buf][g], acc[g][b],
+                                                                0, 0, 0);
+    };
+    // Slab kt: wait for slab kt+1 (own loads, then everybody's via the
+    // barrier, which also retires every wave's reads of stage kt), then refill
+    // stage kt with slab kt+kStages while multiplying slab kt (fragments read
+    // during the previous slab) and reading the fragments of slab kt+1.
+    auto slab_step = [&](int kt, int cbuf, int nbuf) {
+        wait_vmcnt<kDmaPerSlab * (kStages - 2)>();
+        wait_lgkmcnt0();
+        barrier();
+#pragma unroll
+        for (int g = 0; g < kGroups; ++g) {
+            dma_op(g, kt + kStages);
+            read_group(g, kt + 1, nbuf);
+            mfma_group(g, cbuf);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    const int nk = (int)((p.K + kBK - 1) / kBK);
+    if (nk > 0) {
+#pragma unroll
+        for (int s = 0; s < kStages; ++s)
+#pragma unroll
+            for (int g = 0; g < kGroups; ++g) dma_op(g, s);
+        wait_vmcnt<kDmaPerSlab * (kStages - 1)>();
+        barrier();
+#pragma unroll
+        for (int g = 0; g < kGroups; ++g) read_group(g, 0, 0);
+        int kt = 0;
+        for (; kt + 1 < nk; kt += 2) {
+            slab_step(kt, 0, 1);
+            slab_step(kt + 1, 1, 0);
+        }
+        if (kt < nk) slab_step(kt, 0, 1);
+    }
+    wait_vmcnt<0>();
+    wait_lgkmcnt0();
+
+    // Epilogue: lane holds row (lane % 16) and columns 4 * (lane / 16) + 0..3
+    // of every 16 x 16 fragment.
+    const bf16* bias = static_cast<const bf16*>(p.bias);
+    const bf16* aux = static_cast<const bf16*>(p.aux);
+    bf16* save = static_cast<bf16*>(p.save);
+    OutT* C = static_cast<OutT*>(p.C);
+#pragma unroll
+    for (int b = 0; b < kFragN; ++b) {
+        const int64_t col = n0 + wrow_b + b * 16 + 4 * (lane >> 4);
+        if (col >= p.N) continue;
+        float bv[4] = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (EPI == Epi::Bias || EPI == Epi::BiasGelu) {
+            if (bias) {
+                const bf16x4 t4 = *reinterpret_cast<const bf16x4*>(bias + col);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) bv[e] = (float)t4[e];
+            }
+        }
+#pragma unroll
+        for (int a = 0; a < kFragM; ++a) {
+            const int64_t row = m0 + wrow_a + a * 16 + (lane & 15);
+            if (row >= p.M) continue;
+            const int64_t off = row * p.N + col;
+            float v[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = acc[a][b][e];
+            if constexpr (EPI == Epi::Bias) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] += bv[e];
+            } else if constexpr (EPI == Epi::BiasGelu) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] += bv[e];
+                if (save)
+                    *reinterpret_cast<bf16x4*>(save + off) =
+                        bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = gelu_tanh(v[e]);
+            } else if constexpr (EPI == Epi::DGelu) {
+                const bf16x4 y4 = *reinterpret_cast<const bf16x4*>(aux + off);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] *= gelu_tanh_grad((float)y4[e]);
+            }
+            if constexpr (sizeof(OutT) == 4) {
+                *reinterpret_cast<f32x4*>(C + off) = f32x4{v[0], v[1], v[2], v[3]};
+            } else {
+                *reinterpret_cast<bf16x4*>(C + off) =
+                    bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+            }
+        }
+    }
+}
+
+template <int BN, bool AK, bool BK, Epi E, typename O>
+hipError_t launch_bn(const GemmArgs& p, hipStream_t stream)
+{
+    const int tm = (int)((p.M + kBM - 1) / kBM);
+    const int tn = (int)((p.N + BN - 1) / BN);
+    hipLaunchKernelGGL((gemm_ring_kernel<BN, AK, BK, E, O>), dim3((unsigned)(tm * tn)),
+                       dim3(kThreads), 0, stream, p, tm, tn);
+    return hipGetLastError();
+}
+
+// 256 x 192 tiles only: a 256-column tile needs more registers than two
+// waves per SIMD leave once the fragments are double-buffered.
+template <bool AK, bool BK, Epi E, typename O>
+hipError_t launch(const GemmArgs& p, hipStream_t stream)
+{
+    return launch_bn<192, AK, BK, E, O>(p, stream);
+}
+
+}  // namespace
+
+bool gemm_ring_supported(const GemmArgs& p, Layout layout)
+{
+    if (p.M < kBM || p.N < 192) return false;
+    // M/N-major operands are loaded and masked in 8-element chunks.
+    if (p.N % 8 != 0 || (layout == Layout::TN && p.M % 8 != 0)) return false;
+    // A K-major operand must not run past the end of a row inside a slab.
+    if (layout != Layout::TN && p.K % kBK != 0) return false;
+    const int64_t lim = (int64_t(1) << 31) - 1;
+    return p.M * p.K * 2 <= lim && p.N * p.K * 2 <= lim;
+}
+
+hipError_t gemm_ring(const GemmArgs& p, Layout layout, Epi epi, Elt out, hipStream_t stream)
+{
+    switch (layout) {
+    case Layout::NN:
+        if (epi == Epi::BiasGelu) {
+            if (out == Elt::BF16) return launch<true, false, Epi::BiasGelu, bf16>(p, stream);
+            return launch<true, false, Epi::BiasGelu, float>(p, stream);
+        }
+        if (epi == Epi::Bias) {
+            if (out == Elt::BF16) return launch<true, false, Epi::Bias, bf16>(p, stream);
+            return launch<true, false, Epi::Bias, float>(p, stream);
+        }
+        if (out == Elt::BF16) return launch<true, false, Epi::Store, bf16>(p, stream);
+        return launch<true, false, Epi::Store, float>(p, stream);
+    case Layout::NT:
+        if (epi == Epi::DGelu) {
+            if (out == Elt::BF16) return launch<true, true, Epi::DGelu, bf16>(p, stream);
+            return launch<true, true, Epi::DGelu, float>(p, stream);
+        }
+        if (out == Elt::BF16) return launch<true, true, Epi::Store, bf16>(p, stream);
+        return launch<true, true, Epi::Store, float>(p, stream);
+    case Layout::TN:
+        return launch<false, false, Epi::Store, float>(p, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace tpmlp

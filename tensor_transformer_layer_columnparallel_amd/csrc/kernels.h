@@ -16,9 +16,10 @@ enum class Layout { NN = 0, NT = 1, TN = 2 };
 hipError_t gemm_simple(const GemmArgs& p, Elt elt, Layout layout, Epi epi, Elt out,
                        hipStream_t stream);
 
-// 256 x 256-tile bf16 kernel (LDS-DMA, transposed LDS reads, XCD-aware).
-bool gemm_tile_supported(const GemmArgs& p, Layout layout);
-hipError_t gemm_tile(const GemmArgs& p, Layout layout, Epi epi, Elt out, hipStream_t stream);
+// 256 x 192-tile bf16 kernel: LDS-DMA into a ring of 4 stages of 32-deep
+// slabs, transposed LDS reads for M/N-contiguous operands, XCD-aware order.
+bool gemm_ring_supported(const GemmArgs& p, Layout layout);
+hipError_t gemm_ring(const GemmArgs& p, Layout layout, Epi epi, Elt out, hipStream_t stream);
 
 // out[e] = sum_{r=0}^{t-1} parts[r][e] (fp32, rank order); count % 8 == 0.
 hipError_t shard_sum(const void* parts, void* out, int64_t count, int t, Elt in, Elt out_elt,

@@ -60,8 +60,8 @@ hipError_t run_gemm(const void* A, const void* B, void* C, const void* bias, con
 {
     if (M == 0 || N == 0) return hipSuccess;
     GemmArgs p{A, B, C, bias, aux, save, M, N, K};
-    if (elt == Elt::BF16 && gemm_tile_supported(p, layout))
-        return gemm_tile(p, layout, epi, out, stream);
+    if (elt == Elt::BF16 && gemm_ring_supported(p, layout))
+        return gemm_ring(p, layout, epi, out, stream);
     return gemm_simple(p, elt, layout, epi, out, stream);
 }
 
