@@ -1,40 +1,51 @@
 // Large-shape bf16 MFMA GEMM for gfx950: C[M,N] = epi( op(A)[M,K] * op(B)[K,N] ).
 //
-// Tiles of 256 x 192 outputs, one workgroup of 8 waves (4 x 2, 64 x 96
-// outputs each, two waves per SIMD), v_mfma_f32_16x16x32_bf16 with fp32
+// Tiles of 256 x 192 outputs, one workgroup of 8 waves (two per SIMD), each
+// wave owning 256/WM x 192/(8/WM) outputs, v_mfma_f32_16x16x32_bf16 with fp32
 // accumulators and the B fragment in the first MFMA slot, so that each lane
 // ends with four consecutive columns of one row.  Tiles are numbered so that
 // consecutive workgroups (which the dispatcher spreads round-robin over the
 // 8 XCDs) map to neighbouring tiles on the same XCD and share its L2.
 //
-// K is walked in 32-deep slabs through a ring of 4 LDS stages.  Slabs are
-// copied L2 -> LDS by buffer_load_dwordx4 ... lds (DMA, no VGPR staging),
-// issued from inline assembly: the compiler's wait analysis cannot tell the
-// stages apart and would wait for a DMA just issued before any LDS read.  The
-// waits are explicit instead.  At slab k every wave
-//   1. waits until at most its loads of slabs k+2 and k+3 are outstanding
-//      (the vector memory counter retires loads in issue order), and for its
-//      own LDS reads of stage k;
-//   2. passes a barrier: slab k+1 is now in LDS for everybody, and nobody
-//      reads stage k any more;
-//   3. in four groups, each with one DMA instruction, the MFMAs of one A
-//      fragment and a share of the fragment reads: refills stage k with slab
-//      k+4, multiplies slab k (fragments read during slab k-1) and reads the
-//      fragments of slab k+1.
+// Operands are copied L2 -> LDS by buffer_load_dwordx4 ... lds (DMA, no VGPR
+// staging) into rings of buffers:
+//   - a K-contiguous A operand in units of 64 k: a unit row is one whole
+//     128-byte line (a 32-k slab would fetch half lines, and half-line DMA
+//     moves half the bytes per cycle); 3 units of 256 x 64 k (96 KiB);
+//   - an M-contiguous A operand and every B operand in 32-k slabs; 5 slabs
+//     each (80 KiB for A, 60 KiB for B).
+// The DMA is issued from inline assembly: the compiler's wait analysis cannot
+// tell the buffers apart and would wait for the DMA just issued before any
+// LDS read.  The waits are explicit instead.  Compute walks K in 32-k slabs;
+// at slab k every wave
+//   1. waits until its loads of slab k+1 have landed (the vector memory
+//      counter retires loads in issue order; every wave issues the same four
+//      DMA instructions per slab, so the counts are static) and until its own
+//      LDS reads of slab k have returned;
+//   2. passes a barrier: slab k+1 is in LDS for everybody and nobody reads
+//      slab k's buffers any more;
+//   3. in four groups, each with one DMA instruction, the MFMAs of a quarter
+//      of the A fragments and a share of the fragment reads: refills the
+//      freed buffers (5 slabs ahead, or half of the 64-k unit 2-3 slabs
+//      ahead), multiplies slab k (fragments read during slab k-1) and reads
+//      the fragments of slab k+1.
 // Spreading the memory instructions over the MFMAs keeps the waves of a SIMD
 // from stalling together on a burst of loads while the matrix pipe idles.
-// Loads for slabs past the end of K are issued with an invalid offset (they
-// read nothing and write zeros into stages that are never read), so every
-// wave issues the same number of loads per slab and the counts are static.
+// Loads of elements outside the operands (ragged M/N tails, k past K) use a
+// per-lane offset of 2^31, beyond any operand, which the buffer descriptor
+// turns into zeros without touching memory.
 //
 // LDS layouts (16-byte chunks permuted per row for conflict-free reads):
-//   K-major slab  [rows][32 k]: 4 chunks per row, chunk c of row r stored at
-//                 c ^ (((r >> 1) & 3) ^ ((r >> 3) & 1)); read with ds_read_b128.
+//   K-major 64-k unit [256][64 k]: chunk c of row r at c ^ swz8(r);
+//   K-major 32-k slab [rows][32 k]: chunk c of row r at c ^ swz4(r);
+//                 both read with ds_read_b128;
 //   MN-major slab [32 k][R cols]: chunk pairs rotated by k-row (R = 256, an A
 //                 operand) or XORed in blocks of four (R = 192, a B operand);
 //                 read with ds_read_b64_tr_b16 (lane i of a 16-lane group
 //                 receives halfword i % 4 of the 8-byte pieces of lanes
 //                 4e + i / 4).
+#include <type_traits>
+
 #include "common.h"
 #include "epilogue.h"
 #include "kernels.h"
@@ -44,9 +55,11 @@ namespace {
 
 constexpr int kBM = 256;
 constexpr int kBK = 32;
-constexpr int kStages = 4;
-constexpr int kWavesM = 4, kWavesN = 2;
-constexpr int kWaves = kWavesM * kWavesN;
+constexpr int kBN = 192;
+constexpr int kSlabBufs = 5;                // ring of 32-k slabs (A M-major, B)
+constexpr int kUnitBufs = 3;                // ring of 64-k units (A K-major)
+constexpr int kLead = 5;                    // DMA steps issued before the first slab
+constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kDmaPerOperand = 2;           // DMA instructions per wave per operand and slab
 constexpr int kDmaPerSlab = 2 * kDmaPerOperand;
@@ -98,7 +111,17 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p)
     return (uint32_t)reinterpret_cast<uintptr_t>((TP_LDS const void*)p);
 }
 
-__device__ __forceinline__ int swz_k(int row) { return ((row >> 1) & 3) ^ ((row >> 3) & 1); }
+// Chunk permutations of K-major buffers (XORs of row bits): any 8, 16 or 32
+// consecutive lanes reading 16 bytes each (row i, chunk g of the slab) hit
+// distinct banks of a 128-, 256- or 512-byte bank window.
+__device__ __forceinline__ int swz4(int row)
+{
+    return ((row >> 2) & 1) | ((((row >> 1) ^ (row >> 3)) & 1) << 1);
+}
+__device__ __forceinline__ int swz8(int row)
+{
+    return ((row >> 1) & 3) | (((row ^ (row >> 3)) & 1) << 2);
+}
 
 __device__ __forceinline__ int rot_mn(int krow) { return (krow & 3) + 4 * ((krow >> 3) & 1); }
 __device__ __forceinline__ int xor_mn(int krow)
@@ -130,24 +153,20 @@ __device__ __forceinline__ int mn_logical(int krow, int phys)
     return 2 * pair + (phys & 1);
 }
 
-// DMA plan of one operand: R rows (M or N) x 32 k per slab = R * 4 chunks =
+constexpr uint32_t kInvalid = 0x80000000u;   // per-lane offset past any operand
+
+// DMA plan of a 32-k slab stream: R rows (M or N) x 32 k = R * 4 chunks =
 // R / 16 instructions of 64 chunks; instruction idx = wave * 2 + j fills
 // chunks [idx * 64, idx * 64 + 64).  Instructions past R / 16 (R = 192) are
-// dummies that read nothing (invalid offset) into a junk LDS area.
-//
-// Only the per-lane offset is used to leave an operand: an element outside
-// it gets the offset 0x80000000, beyond any operand (< 2^31 bytes), and the
-// buffer descriptor returns zeros.  K-major operands advance along K with
-// the scalar offset (K is a multiple of 32, so in-range rows stay inside the
-// operand); slabs past the end reload the last slab into a stage that is
-// never read again.  MN-major operands advance with the per-lane offset, and
-// k-rows past K are invalidated.
+// dummies that read nothing into a junk LDS area.  K-major rows advance 64
+// bytes per slab (K is a multiple of 32); M/N-major slabs advance 32 rows of
+// the operand, and k-rows past K are invalidated.
 template <bool KMAJ, int R>
-struct DmaPlan {
+struct SlabPlan {
     static constexpr int kInstr = R / 16;
-    static constexpr uint32_t kInvalid = 0x80000000u;
+    static constexpr int kBufBytes = R * kBK * 2;
     uint32_t voff[kDmaPerOperand];
-    uint32_t dst[kDmaPerOperand];   // byte offset inside a stage (or the junk area)
+    uint32_t dst[kDmaPerOperand];   // byte offset inside a buffer (or the junk area)
     int krow[kDmaPerOperand];
     bool real[kDmaPerOperand];
     uint32_t kstep;
@@ -155,7 +174,7 @@ struct DmaPlan {
     int64_t K;
 
     __device__ __forceinline__ void init(int wave, int lane, int64_t r0, int64_t ld,
-                                         int64_t extent, int64_t K_, uint32_t operand_off)
+                                         int64_t extent, int64_t K_)
     {
         K = K_;
         nk = (int)((K_ + kBK - 1) / kBK);
@@ -170,7 +189,7 @@ struct DmaPlan {
                 voff[j] = kInvalid;
             } else if (KMAJ) {
                 const int row = linear >> 2;
-                const int chunk = (linear & 3) ^ swz_k(row);
+                const int chunk = (linear & 3) ^ swz4(row);
                 voff[j] = r0 + row < extent ? (uint32_t)(((r0 + row) * ld + chunk * 8) * 2)
                                             : kInvalid;
             } else {
@@ -180,13 +199,12 @@ struct DmaPlan {
                               ? (uint32_t)((krow[j] * ld + r0 + chunk * 8) * 2)
                               : kInvalid;
             }
-            dst[j] = real[j] ? operand_off + (uint32_t)idx * 1024u
+            dst[j] = real[j] ? (uint32_t)idx * 1024u
                              : (uint32_t)(idx - kInstr) / kDmaPerOperand * 1024u;
         }
     }
-    // Instruction j of slab `slab` into the stage at stage_base.  Slabs past
-    // the end of K read nothing (zeros land in a stage that is never used).
-    __device__ __forceinline__ void issue(int j, i32x4 desc, uint32_t stage_base,
+    // Instruction j of slab `slab` into its ring buffer.
+    __device__ __forceinline__ void issue(int j, i32x4 desc, uint32_t ring_base,
                                           uint32_t junk_base, int slab) const
     {
         uint32_t v;
@@ -196,47 +214,96 @@ struct DmaPlan {
             const bool ok = voff[j] != kInvalid && (int64_t)slab * kBK + krow[j] < K;
             v = ok ? voff[j] + (uint32_t)slab * kstep : kInvalid;
         }
+        const uint32_t buf = (uint32_t)(slab % kSlabBufs) * kBufBytes;
         const uint32_t lds = __builtin_amdgcn_readfirstlane(
-            (int)((real[j] ? stage_base : junk_base) + dst[j]));
+            (int)((real[j] ? ring_base + buf : junk_base) + dst[j]));
+        dma16(desc, lds, v, 0u);
+    }
+};
+
+// DMA plan of a K-major 64-k unit stream (A, 256 rows): 256 rows x 128 bytes
+// = 32 instructions of 8 rows; wave w owns instructions 4w .. 4w+3, issued
+// in two parts of two (part p: 4w + 2p + j) on consecutive slabs.  Unit u
+// covers k in [64u, 64u + 64); chunks past K are invalidated per lane.
+struct UnitPlan {
+    static constexpr int kBufBytes = kBM * 64 * 2;
+    uint32_t voff[2 * kDmaPerOperand];
+    int ulim[2 * kDmaPerOperand];   // units u < ulim hold this lane's chunk inside K
+
+    __device__ __forceinline__ void init(int wave, int lane, int64_t r0, int64_t ld,
+                                         int64_t extent, int64_t K)
+    {
+#pragma unroll
+        for (int q = 0; q < 2 * kDmaPerOperand; ++q) {
+            const int idx = wave * 2 * kDmaPerOperand + q;
+            const int row = idx * 8 + (lane >> 3);
+            const int chunk = (lane & 7) ^ swz8(row);
+            const bool ok = r0 + row < extent;
+            voff[q] = ok ? (uint32_t)(((r0 + row) * ld + chunk * 8) * 2) : kInvalid;
+            ulim[q] = ok ? (int)((K - chunk * 8 + 63) / 64) : 0;
+        }
+    }
+    // Instruction j of part `part` of unit `unit` into its ring buffer.
+    __device__ __forceinline__ void issue(int part, int j, int wave, i32x4 desc,
+                                          uint32_t ring_base, int unit) const
+    {
+        const int q = 2 * part + j;
+        const uint32_t v = unit < ulim[q] ? voff[q] + (uint32_t)unit * 128u : kInvalid;
+        const uint32_t buf = (uint32_t)(unit % kUnitBufs) * kBufBytes;
+        const uint32_t lds = __builtin_amdgcn_readfirstlane(
+            (int)(ring_base + buf + (uint32_t)(wave * 2 * kDmaPerOperand + q) * 1024u));
         dma16(desc, lds, v, 0u);
     }
 };
 
 // One fragment of a 32-k slab: 16 rows (M for A, N for B) starting at row0,
 // 8 bf16 per lane (lane l: row l % 16, k 8 (l / 16) .. 8 (l / 16) + 7).
-template <bool KMAJ, int R>
-__device__ __forceinline__ bf16x8 read_frag(const bf16* slab, int row0, int lane)
+// K-major 32-k slab buffer.
+__device__ __forceinline__ bf16x8 read_frag_k4(const bf16* buf, int row0, int lane)
 {
     const int i = lane & 15, g = lane >> 4;
-    if constexpr (KMAJ) {
-        const int chunk = g ^ swz_k(i);
-        return *reinterpret_cast<const bf16x8*>(slab + (row0 + i) * kBK + chunk * 8);
-    } else {
-        const int krow0 = g * 8 + (i >> 2);
-        const int col = row0 + 4 * (i & 3);
-        bf16x4 half[2];
+    return *reinterpret_cast<const bf16x8*>(buf + (row0 + i) * kBK + (g ^ swz4(i)) * 8);
+}
+// K-major 64-k unit buffer, slab half `half`.
+__device__ __forceinline__ bf16x8 read_frag_k8(const bf16* buf, int row0, int half, int lane)
+{
+    const int i = lane & 15, g = lane >> 4;
+    return *reinterpret_cast<const bf16x8*>(buf + (row0 + i) * 64 + ((4 * half + g) ^ swz8(i)) * 8);
+}
+// M/N-major 32-k slab buffer of R columns.
+template <int R>
+__device__ __forceinline__ bf16x8 read_frag_mn(const bf16* buf, int row0, int lane)
+{
+    const int i = lane & 15, g = lane >> 4;
+    const int krow0 = g * 8 + (i >> 2);
+    const int col = row0 + 4 * (i & 3);
+    bf16x4 half[2];
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-            const int krow = krow0 + 4 * hh;
-            const bf16* p = slab + krow * R + mn_phys<R>(krow, col >> 3) * 8 + (col & 7);
-            const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TP_LDS i16x4*)((TP_LDS bf16*)p));
-            half[hh] = __builtin_bit_cast(bf16x4, v);
-        }
-        return bf16x8{half[0][0], half[0][1], half[0][2], half[0][3],
-                      half[1][0], half[1][1], half[1][2], half[1][3]};
+    for (int hh = 0; hh < 2; ++hh) {
+        const int krow = krow0 + 4 * hh;
+        const bf16* p = buf + krow * R + mn_phys<R>(krow, col >> 3) * 8 + (col & 7);
+        const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TP_LDS i16x4*)((TP_LDS bf16*)p));
+        half[hh] = __builtin_bit_cast(bf16x4, v);
     }
+    return bf16x8{half[0][0], half[0][1], half[0][2], half[0][3],
+                  half[1][0], half[1][1], half[1][2], half[1][3]};
 }
 
-template <int BN, bool A_KMAJ, bool B_KMAJ, Epi EPI, typename OutT>
+template <int WM, bool A_KMAJ, bool B_KMAJ, Epi EPI, typename OutT>
 __global__ __launch_bounds__(kThreads, 1) void gemm_ring_kernel(GemmArgs p, int tiles_m,
                                                                 int tiles_n)
 {
+    constexpr int BN = kBN;
+    constexpr int kWavesM = WM, kWavesN = kWaves / WM;
     constexpr int kWaveM = kBM / kWavesM, kWaveN = BN / kWavesN;
     constexpr int kFragM = kWaveM / 16, kFragN = kWaveN / 16;
-    constexpr int kSlabA = kBM * kBK, kSlabB = BN * kBK;   // elements
-    constexpr int kStage = kSlabA + kSlabB;
-    constexpr int kJunkWaves = kWaves - DmaPlan<B_KMAJ, BN>::kInstr / kDmaPerOperand;
-    __shared__ __attribute__((aligned(1024))) bf16 smem[kStages * kStage];
+    using PlanA = SlabPlan<false, kBM>;   // used when A is M-contiguous
+    using PlanB = SlabPlan<B_KMAJ, BN>;
+    constexpr int kABytes = A_KMAJ ? kUnitBufs * UnitPlan::kBufBytes : kSlabBufs * PlanA::kBufBytes;
+    constexpr int kBBytes = kSlabBufs * PlanB::kBufBytes;
+    constexpr int kJunkWaves = kWaves - PlanB::kInstr / kDmaPerOperand;
+    __shared__ __attribute__((aligned(1024))) bf16 sa[kABytes / 2];
+    __shared__ __attribute__((aligned(1024))) bf16 sb[kBBytes / 2];
     __shared__ __attribute__((aligned(1024))) bf16 junk[(kJunkWaves > 0 ? kJunkWaves : 1) * 512];
 
     const int lane = threadIdx.x & 63;
@@ -251,12 +318,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_ring_kernel(GemmArgs p, int 
 
     const i32x4 da = make_desc(p.A, (uint32_t)(p.M * p.K * 2));
     const i32x4 db = make_desc(p.B, (uint32_t)(p.N * p.K * 2));
-    DmaPlan<A_KMAJ, kBM> pa;
-    DmaPlan<B_KMAJ, BN> pb;
-    pa.init(wave, lane, m0, A_KMAJ ? p.K : p.M, p.M, p.K, 0u);
-    pb.init(wave, lane, n0, B_KMAJ ? p.K : p.N, p.N, p.K, (uint32_t)(kSlabA * 2));
-    const uint32_t smem_base = lds_addr(smem);
-    const uint32_t junk_base = lds_addr(junk);
+    UnitPlan pu;   // A K-major
+    PlanA ps;      // A M-major
+    if constexpr (A_KMAJ) pu.init(wave, lane, m0, p.K, p.M, p.K);
+    else ps.init(wave, lane, m0, p.M, p.M, p.K);
+    PlanB pb;
+    pb.init(wave, lane, n0, B_KMAJ ? p.K : p.N, p.N, p.K);
+    const uint32_t a_base = lds_addr(sa), b_base = lds_addr(sb), junk_base = lds_addr(junk);
 
     const int wrow_a = wm * kWaveM, wrow_b = wn * kWaveN;
     f32x4 acc[kFragM][kFragN];
@@ -266,62 +334,89 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_ring_kernel(GemmArgs p, int 
         for (int b = 0; b < kFragN; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
     bf16x8 fa[2][kFragM], fb[2][kFragN];
 
-    // The work of one slab is cut into kGroups groups, each holding one DMA
-    // instruction, the MFMAs of one A fragment and a share of the fragment
-    // reads, so that the waves never stall on a burst of memory instructions
-    // while the matrix pipe idles.
-    static_assert(kFragM == kGroups, "one A fragment per group");
-    auto dma_op = [&](int g, int slab) {
-        const uint32_t stage_base = smem_base + (uint32_t)((slab % kStages) * kStage * 2);
-        if (g < kDmaPerOperand) pa.issue(g, da, stage_base, junk_base, slab);
-        else pb.issue(g - kDmaPerOperand, db, stage_base, junk_base, slab);
+    // DMA instruction g (0, 1: A; 2, 3: B) of step vs (negative in the
+    // prologue).  B and an M-major A refill slab vs + 5 (the buffer of slab
+    // vs, read for the last time during step vs - 1); a K-major A refills
+    // part (vs + 1) mod 2 of unit floor((vs + 1) / 2) + 2 (the buffer of the
+    // unit holding slabs vs - 1 and vs, or vs - 2 and vs - 1).
+    auto dma_op = [&](int g, int vs) {
+        if (g < kDmaPerOperand) {
+            if constexpr (A_KMAJ) pu.issue((vs + 1) & 1, g, wave, da, a_base, ((vs + 1) >> 1) + kUnitBufs - 1);
+            else ps.issue(g, da, a_base, junk_base, vs + kSlabBufs);
+        } else {
+            pb.issue(g - kDmaPerOperand, db, b_base, junk_base, vs + kSlabBufs);
+        }
     };
+    // The work of one slab is cut into kGroups groups, each holding one DMA
+    // instruction, the MFMAs of the A fragments a with a % kGroups == g and a
+    // share of the fragment reads, so that the waves never stall on a burst
+    // of memory instructions while the matrix pipe idles.
+    static_assert(kFragM % kGroups == 0, "whole A fragments per group");
     auto read_group = [&](int g, int slab, int buf) {
-        const bf16* st = smem + (slab % kStages) * kStage;
-        fa[buf][g] = read_frag<A_KMAJ, kBM>(st, wrow_a + g * 16, lane);
 #pragma unroll
-        for (int q = g; q < kFragN; q += kGroups)
-            fb[buf][q] = read_frag<B_KMAJ, BN>(st + kSlabA, wrow_b + q * 16, lane);
+        for (int a = g; a < kFragM; a += kGroups) {
+            if constexpr (A_KMAJ)
+                fa[buf][a] = read_frag_k8(sa + ((slab >> 1) % kUnitBufs) * (UnitPlan::kBufBytes / 2),
+                                          wrow_a + a * 16, slab & 1, lane);
+            else
+                fa[buf][a] = read_frag_mn<kBM>(sa + (slab % kSlabBufs) * (PlanA::kBufBytes / 2),
+                                               wrow_a + a * 16, lane);
+        }
+#pragma unroll
+        for (int q = g; q < kFragN; q += kGroups) {
+            const bf16* bb = sb + (slab % kSlabBufs) * (PlanB::kBufBytes / 2);
+            if constexpr (B_KMAJ) fb[buf][q] = read_frag_k4(bb, wrow_b + q * 16, lane);
+            else fb[buf][q] = read_frag_mn<BN>(bb, wrow_b + q * 16, lane);
+        }
     };
     auto mfma_group = [&](int g, int buf) {
 #pragma unroll
-        for (int b = 0; b < kFragN; ++b)
-            acc[g][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[buf][b], fa[buf][g], acc[g][b],
-                                                                0, 0, 0);
+        for (int a = g; a < kFragM; a += kGroups)
+#pragma unroll
+            for (int b = 0; b < kFragN; ++b)
+                acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[buf][b], fa[buf][a],
+                                                                    acc[a][b], 0, 0, 0);
     };
     // Slab kt: wait for slab kt+1 (own loads, then everybody's via the
-    // barrier, which also retires every wave's reads of stage kt), then refill
-    // stage kt with slab kt+kStages while multiplying slab kt (fragments read
-    // during the previous slab) and reading the fragments of slab kt+1.
-    auto slab_step = [&](int kt, int cbuf, int nbuf) {
-        wait_vmcnt<kDmaPerSlab * (kStages - 2)>();
+    // barrier, which also retires every wave's reads of slab kt), then refill
+    // while multiplying slab kt (fragments read during the previous slab) and
+    // reading the fragments of slab kt+1.  Slab kt+1's loads were issued at
+    // step kt-4 or earlier, except the second half of a K-major A unit
+    // starting at an even slab kt+1, issued at step kt-3: for odd kt only two
+    // steps of loads may stay outstanding, otherwise three.
+    auto slab_step = [&](auto odd, int kt, int cbuf, int nbuf) {
+        if constexpr (A_KMAJ && decltype(odd)::value) wait_vmcnt<kDmaPerSlab * 2>();
+        else wait_vmcnt<kDmaPerSlab * 3>();
         wait_lgkmcnt0();
         barrier();
 #pragma unroll
         for (int g = 0; g < kGroups; ++g) {
-            dma_op(g, kt + kStages);
+            dma_op(g, kt);
             read_group(g, kt + 1, nbuf);
             mfma_group(g, cbuf);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
+    using Even = std::integral_constant<bool, false>;
+    using Odd = std::integral_constant<bool, true>;
 
     const int nk = (int)((p.K + kBK - 1) / kBK);
     if (nk > 0) {
 #pragma unroll
-        for (int s = 0; s < kStages; ++s)
+        for (int vs = -kLead; vs < 0; ++vs)
 #pragma unroll
-            for (int g = 0; g < kGroups; ++g) dma_op(g, s);
-        wait_vmcnt<kDmaPerSlab * (kStages - 1)>();
+            for (int g = 0; g < kGroups; ++g) dma_op(g, vs);
+        // Slab 0 came with the first two prologue steps.
+        wait_vmcnt<kDmaPerSlab * (kLead - 2)>();
         barrier();
 #pragma unroll
         for (int g = 0; g < kGroups; ++g) read_group(g, 0, 0);
         int kt = 0;
         for (; kt + 1 < nk; kt += 2) {
-            slab_step(kt, 0, 1);
-            slab_step(kt + 1, 1, 0);
+            slab_step(Even{}, kt, 0, 1);
+            slab_step(Odd{}, kt + 1, 1, 0);
         }
-        if (kt < nk) slab_step(kt, 0, 1);
+        if (kt < nk) slab_step(Even{}, kt, 0, 1);
     }
     wait_vmcnt<0>();
     wait_lgkmcnt0();
@@ -378,22 +473,26 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_ring_kernel(GemmArgs p, int 
     }
 }
 
-template <int BN, bool AK, bool BK, Epi E, typename O>
-hipError_t launch_bn(const GemmArgs& p, hipStream_t stream)
-{
-    const int tm = (int)((p.M + kBM - 1) / kBM);
-    const int tn = (int)((p.N + BN - 1) / BN);
-    hipLaunchKernelGGL((gemm_ring_kernel<BN, AK, BK, E, O>), dim3((unsigned)(tm * tn)),
-                       dim3(kThreads), 0, stream, p, tm, tn);
-    return hipGetLastError();
-}
+#ifndef TPMLP_RING_WM_NN
+#define TPMLP_RING_WM_NN 2
+#endif
+#ifndef TPMLP_RING_WM_NT
+#define TPMLP_RING_WM_NT 4
+#endif
+#ifndef TPMLP_RING_WM_TN
+#define TPMLP_RING_WM_TN 4
+#endif
 
-// 256 x 192 tiles only: a 256-column tile needs more registers than two
-// waves per SIMD leave once the fragments are double-buffered.
+// WM waves along M (and 8 / WM along N).
 template <bool AK, bool BK, Epi E, typename O>
 hipError_t launch(const GemmArgs& p, hipStream_t stream)
 {
-    return launch_bn<192, AK, BK, E, O>(p, stream);
+    constexpr int WM = AK ? (BK ? TPMLP_RING_WM_NT : TPMLP_RING_WM_NN) : TPMLP_RING_WM_TN;
+    const int tm = (int)((p.M + kBM - 1) / kBM);
+    const int tn = (int)((p.N + kBN - 1) / kBN);
+    hipLaunchKernelGGL((gemm_ring_kernel<WM, AK, BK, E, O>), dim3((unsigned)(tm * tn)),
+                       dim3(kThreads), 0, stream, p, tm, tn);
+    return hipGetLastError();
 }
 
 }  // namespace

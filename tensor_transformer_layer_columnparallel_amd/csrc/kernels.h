@@ -21,6 +21,9 @@ hipError_t gemm_simple(const GemmArgs& p, Elt elt, Layout layout, Epi epi, Elt o
 bool gemm_ring_supported(const GemmArgs& p, Layout layout);
 hipError_t gemm_ring(const GemmArgs& p, Layout layout, Epi epi, Elt out, hipStream_t stream);
 
+// out[c][r] = in[r][c] for 16-bit elements, in [rows][cols] (cols % 8 == 0).
+hipError_t transpose16(const void* in, void* out, int64_t rows, int64_t cols, hipStream_t stream);
+
 // out[e] = sum_{r=0}^{t-1} parts[r][e] (fp32, rank order); count % 8 == 0.
 hipError_t shard_sum(const void* parts, void* out, int64_t count, int t, Elt in, Elt out_elt,
                      hipStream_t stream);

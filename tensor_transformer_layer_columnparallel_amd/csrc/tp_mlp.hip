@@ -54,6 +54,23 @@ int check_split(int64_t full, int t, int rank, int64_t* local)
 
 int status_of(hipError_t e) { return e == hipSuccess ? TP_OK : TP_ERR_HIP; }
 
+// The weight-gradient products x^T dy read both operands M/N-contiguous,
+// which the tile kernel can only do with transposing LDS reads of both.  With
+// bf16 operands, a token count that whole 32-deep slabs cover and room for
+// H_i^T (n x T bf16) in the fp32 dW1_i (h x n), the two activations are
+// transposed first (an HBM-bound pass) and the products run with a
+// K-contiguous first operand.
+bool use_transposed_operands(int64_t tokens, int64_t h, int64_t n, Elt e)
+{
+    if (e != Elt::BF16 || tokens == 0 || tokens % 32 != 0) return false;
+    if (2 * tokens > 4 * h) return false;   // H_i^T must fit in dW1_i
+    GemmArgs a{};
+    a.M = n; a.N = h; a.K = tokens;
+    GemmArgs b{};
+    b.M = h; b.N = n; b.K = tokens;
+    return gemm_ring_supported(a, Layout::NN) && gemm_ring_supported(b, Layout::NN);
+}
+
 hipError_t run_gemm(const void* A, const void* B, void* C, const void* bias, const void* aux,
                     void* save, int64_t M, int64_t N, int64_t K, Elt elt, Layout layout, Epi epi,
                     Elt out, hipStream_t stream)
@@ -173,14 +190,27 @@ int tp_mlp_shard_bwd(const void* X, const void* W1_i, const void* W2_i, const vo
     if ((err = run_gemm(dZ, W2_i, dY_i, nullptr, Y_i, nullptr, tokens, n, h, e, Layout::NT,
                         Epi::DGelu, e, s)) != hipSuccess)
         return TP_ERR_HIP;
-    // dW2_i = H_i^T dZ: H_i [T][n] is [K][M], dZ [T][h] is [K][N].
-    if ((err = run_gemm(H_i, dZ, dW2_i, nullptr, nullptr, nullptr, n, h, tokens, e, Layout::TN,
-                        Epi::Store, Elt::F32, s)) != hipSuccess)
-        return TP_ERR_HIP;
-    // dW1_i = X^T dY_i: X [T][h] is [K][M], dY_i [T][n] is [K][N].
-    if ((err = run_gemm(X, dY_i, dW1_i, nullptr, nullptr, nullptr, h, n, tokens, e, Layout::TN,
-                        Epi::Store, Elt::F32, s)) != hipSuccess)
-        return TP_ERR_HIP;
+    if (use_transposed_operands(tokens, h, n, e)) {
+        // The weight gradients as products with a K-contiguous first operand:
+        // H_i^T [n][T] is staged in dW1_i's memory (written only afterwards)
+        // and X^T [h][T] in dX_i's (written last).
+        if ((err = transpose16(H_i, dW1_i, tokens, n, s)) != hipSuccess ||
+            (err = run_gemm(dW1_i, dZ, dW2_i, nullptr, nullptr, nullptr, n, h, tokens, e,
+                            Layout::NN, Epi::Store, Elt::F32, s)) != hipSuccess ||
+            (err = transpose16(X, dX_i, tokens, h, s)) != hipSuccess ||
+            (err = run_gemm(dX_i, dY_i, dW1_i, nullptr, nullptr, nullptr, h, n, tokens, e,
+                            Layout::NN, Epi::Store, Elt::F32, s)) != hipSuccess)
+            return TP_ERR_HIP;
+    } else {
+        // dW2_i = H_i^T dZ: H_i [T][n] is [K][M], dZ [T][h] is [K][N].
+        if ((err = run_gemm(H_i, dZ, dW2_i, nullptr, nullptr, nullptr, n, h, tokens, e,
+                            Layout::TN, Epi::Store, Elt::F32, s)) != hipSuccess)
+            return TP_ERR_HIP;
+        // dW1_i = X^T dY_i: X [T][h] is [K][M], dY_i [T][n] is [K][N].
+        if ((err = run_gemm(X, dY_i, dW1_i, nullptr, nullptr, nullptr, h, n, tokens, e,
+                            Layout::TN, Epi::Store, Elt::F32, s)) != hipSuccess)
+            return TP_ERR_HIP;
+    }
     // dX_i = dY_i W1_i^T: W1_i [h][n] is the K-contiguous [N][K] operand.
     if ((err = run_gemm(dY_i, W1_i, dX_i, nullptr, nullptr, nullptr, tokens, h, n, e, Layout::NT,
                         Epi::Store, Elt::F32, s)) != hipSuccess)
