@@ -59,9 +59,11 @@ def stored_traffic():
     return None if b is None else int(round(b))
 
 
-COLUMN_KERNEL_KEYS = ("gemm_ring_kernelILi192ELb1ELb0ELNS_3EpiE2EDF16b",
-                      "gemm_ring_kernel<192, true, false, (tpmlp::Epi)2, __bf16>")
-COPY_KERNEL_KEYS = ("shard_concat_kernel",)
+# The column GEMM is the only bf16-output GEMM with the bias + GeLU epilogue
+# (mangled and demangled spellings; every part of a key must match).
+COLUMN_KERNEL_KEYS = (("gemm_ring_kernel", "ELNS_3EpiE2EDF16b"),
+                      ("gemm_ring_kernel<", "(tpmlp::Epi)2, __bf16>"))
+COPY_KERNEL_KEYS = (("shard_concat_kernel",),)
 
 
 def _counter_per_dispatch(csv_dir: str, counter: str, keys) -> float:
@@ -75,7 +77,7 @@ def _counter_per_dispatch(csv_dir: str, counter: str, keys) -> float:
             for row in csv.DictReader(f):
                 if row["Counter_Name"] != counter:
                     continue
-                if not any(k in row["Kernel_Name"] for k in keys):
+                if not any(all(k in row["Kernel_Name"] for k in key) for key in keys):
                     continue
                 per[row["Dispatch_Id"]] = per.get(row["Dispatch_Id"], 0.0) + float(row["Counter_Value"])
     if not per:
@@ -97,7 +99,7 @@ def ingest_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, comman
     w_scale = copy_bytes / (w_cp * 1024)
     read_b = f_col * 1024 * f_scale
     write_b = w_col * 1024 * w_scale
-    out = {"kernel": COLUMN_KERNEL_KEYS[1], "kernel_source_digest": kernel_source_digest(),
+    out = {"kernel": "gemm_ring_kernel: NN, bias + GeLU epilogue, bf16 output", "kernel_source_digest": kernel_source_digest(),
            "fetch_kib_raw": f_col, "write_kib_raw": w_col,
            "copy_bytes": copy_bytes, "copy_fetch_kib_raw": f_cp, "copy_write_kib_raw": w_cp,
            "fetch_scale": f_scale, "write_scale": w_scale,

@@ -138,9 +138,9 @@ TP_API int tp_mlp_shard_fwd(const void* X, const void* W1_i, const void* b1_i, c
  *            last two products), dW2_i [n,h], dW1_i [h,n], dX_i [tokens,h],
  *            db1_i [n] or NULL                     fp32
  * tokens == 0 is valid: the weight gradients are then written as zeros.
- * dW1_i and dX_i also serve as scratch space during the call (for transposed
- * copies of H_i and X) before they receive their results, so no output may
- * overlap an input.
+ * dW2_i, dW1_i and dX_i also serve as scratch space during the call (partial
+ * sums of db1_i; transposed copies of H_i and X) before they receive their
+ * results, so no output may overlap an input.
  */
 TP_API int tp_mlp_shard_bwd(const void* X, const void* W1_i, const void* W2_i,
                      const void* Y_i, const void* H_i, const void* dZ,

@@ -33,7 +33,9 @@ hipError_t shard_concat(const void* parts, void* out, int64_t rows, int64_t cols
                         Elt elt, hipStream_t stream);
 
 // out[j] = sum_m in[m][j] in fp32, fixed summation order: the bias gradient.
+// With scratch of at least ceil(rows / 64) * cols floats it sums row blocks
+// of 64 first (more parallel), otherwise one pass per column block.
 hipError_t column_sum(const void* in, float* out, int64_t rows, int64_t cols, Elt elt,
-                      hipStream_t stream);
+                      void* scratch, int64_t scratch_bytes, hipStream_t stream);
 
 }  // namespace tpmlp

@@ -130,6 +130,75 @@ __global__ __launch_bounds__(kThreads) void column_sum_kernel(const T* __restric
     }
 }
 
+// Two-level column sums for tall inputs: row blocks of kSumRows rows give
+// partial sums (512 columns x 64 rows per workgroup, so that every CU gets
+// work), then one thread per column adds the partials in row-block order.
+constexpr int kSumRows = 64;
+constexpr int kSumOcts = 64;                              // 512 columns per workgroup
+constexpr int kSumSub = kThreads / kSumOcts;              // 4 row subgroups
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void column_part_kernel(const T* __restrict__ in,
+                                                               float* __restrict__ part,
+                                                               int64_t rows, int64_t cols,
+                                                               int64_t col_blocks)
+{
+    __shared__ float red[kSumSub][kSumOcts * 8];
+    const int64_t rb = blockIdx.x / col_blocks, cb = blockIdx.x % col_blocks;
+    const int oct = threadIdx.x % kSumOcts, sub = threadIdx.x / kSumOcts;
+    const int64_t c0 = cb * kSumOcts * 8 + oct * 8;
+    Oct s{{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}};
+    if (c0 < cols) {
+        const int64_t m_end = (rb + 1) * kSumRows < rows ? (rb + 1) * kSumRows : rows;
+        int64_t m = rb * kSumRows + sub;
+        // Four rows' loads in flight at a time; the adds stay in row order.
+        for (; m + 3 * kSumSub < m_end; m += 4 * kSumSub) {
+            Oct x[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) x[u] = load8(in + (m + u * kSumSub) * cols + c0);
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) s.v[e] += x[u].v[e];
+        }
+        for (; m < m_end; m += kSumSub) {
+            const Oct x = load8(in + m * cols + c0);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) s.v[e] += x.v[e];
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) red[sub][oct * 8 + e] = s.v[e];
+    __syncthreads();
+    for (int c = threadIdx.x; c < kSumOcts * 8; c += kThreads) {
+        const int64_t col = cb * kSumOcts * 8 + c;
+        if (col >= cols) break;
+        float acc = 0.f;
+#pragma unroll
+        for (int g = 0; g < kSumSub; ++g) acc += red[g][c];
+        part[rb * cols + col] = acc;
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void column_final_kernel(const float* __restrict__ part,
+                                                                float* __restrict__ out,
+                                                                int64_t nrb, int64_t cols)
+{
+    const int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (c >= cols) return;
+    float acc = 0.f;
+    int64_t rb = 0;
+    for (; rb + 8 <= nrb; rb += 8) {   // eight loads in flight, adds in order
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = part[(rb + u) * cols + c];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc += v[u];
+    }
+    for (; rb < nrb; ++rb) acc += part[rb * cols + c];
+    out[c] = acc;
+}
+
 unsigned stream_grid(int64_t work_items)
 {
     const int64_t cap = 256 * 16;   // 16 workgroups per CU, grid-stride beyond
@@ -182,8 +251,23 @@ hipError_t shard_concat(const void* parts, void* out, int64_t rows, int64_t cols
 }
 
 hipError_t column_sum(const void* in, float* out, int64_t rows, int64_t cols, Elt elt,
-                      hipStream_t stream)
+                      void* scratch, int64_t scratch_bytes, hipStream_t stream)
 {
+    const int64_t nrb = (rows + kSumRows - 1) / kSumRows;
+    const int64_t col_blocks = (cols + kSumOcts * 8 - 1) / (kSumOcts * 8);
+    if (scratch && nrb > 1 && nrb * cols * 4 <= scratch_bytes && nrb * col_blocks <= INT32_MAX) {
+        float* part = static_cast<float*>(scratch);
+        const dim3 grid((unsigned)(nrb * col_blocks));
+        if (elt == Elt::F32)
+            hipLaunchKernelGGL((column_part_kernel<float>), grid, dim3(kThreads), 0, stream,
+                               static_cast<const float*>(in), part, rows, cols, col_blocks);
+        else
+            hipLaunchKernelGGL((column_part_kernel<bf16>), grid, dim3(kThreads), 0, stream,
+                               static_cast<const bf16*>(in), part, rows, cols, col_blocks);
+        hipLaunchKernelGGL(column_final_kernel, dim3((unsigned)((cols + kThreads - 1) / kThreads)),
+                           dim3(kThreads), 0, stream, part, out, nrb, cols);
+        return hipGetLastError();
+    }
     const unsigned grid = (unsigned)((cols + kColOcts * 8 - 1) / (kColOcts * 8));
     if (elt == Elt::F32)
         hipLaunchKernelGGL((column_sum_kernel<float>), dim3(grid), dim3(kThreads), 0, stream,

@@ -190,6 +190,11 @@ int tp_mlp_shard_bwd(const void* X, const void* W1_i, const void* W2_i, const vo
     if ((err = run_gemm(dZ, W2_i, dY_i, nullptr, Y_i, nullptr, tokens, n, h, e, Layout::NT,
                         Epi::DGelu, e, s)) != hipSuccess)
         return TP_ERR_HIP;
+    // db1_i = column sums of dY_i, with dW2_i (written only afterwards) as
+    // scratch for the partial sums.
+    if (db1_i && (err = column_sum(dY_i, static_cast<float*>(db1_i), tokens, n, e, dW2_i,
+                                   n * h * 4, s)) != hipSuccess)
+        return TP_ERR_HIP;
     if (use_transposed_operands(tokens, h, n, e)) {
         // The weight gradients as products with a K-contiguous first operand:
         // H_i^T [n][T] is staged in dW1_i's memory (written only afterwards)
@@ -215,8 +220,6 @@ int tp_mlp_shard_bwd(const void* X, const void* W1_i, const void* W2_i, const vo
     if ((err = run_gemm(dY_i, W1_i, dX_i, nullptr, nullptr, nullptr, tokens, h, n, e, Layout::NT,
                         Epi::Store, Elt::F32, s)) != hipSuccess)
         return TP_ERR_HIP;
-    if (db1_i)
-        return status_of(column_sum(dY_i, static_cast<float*>(db1_i), tokens, n, e, s));
     return TP_OK;
 }
 

@@ -1,74 +1,71 @@
-// out[c][r] = in[r][c] for a 16-bit matrix of rows x cols: 64 x 64 tiles
-// staged through LDS, so that both the reads and the writes move whole
-// 128-byte row segments.  Used to turn the x^T dy products of the backward
-// into products whose first operand is K-contiguous.
+// out[c][r] = in[r][c] for a 16-bit matrix of rows x cols.  Each lane moves an
+// 8 x 8 block through its registers (eight 16-byte row loads, 32 byte
+// permutes, eight 16-byte column stores); the eight lanes of a block row
+// cover 128 contiguous bytes on both sides, so reads and writes move whole
+// 128-byte segments.  Used to turn the x^T dy products of the backward into
+// products whose first operand is K-contiguous.
 #include "common.h"
 #include "kernels.h"
 
 namespace tpmlp {
 namespace {
 
-constexpr int kTile = 64;
 constexpr int kThreads = 256;
-constexpr int kPad = 2;   // row stride 66 elements: column reads spread over banks
+constexpr int kTile = 64;            // one wave: 64 x 64 elements, 8 x 8 blocks of 8 x 8
+constexpr int kWavesPerBlock = kThreads / 64;
 
-struct Vec16 {
-    uint32_t w[8];   // 16 consecutive 16-bit elements
-};
+__device__ __forceinline__ uint32_t lo_pair(uint32_t a, uint32_t b)
+{
+    return (a & 0xffffu) | (b << 16);   // low halves of a and b
+}
+__device__ __forceinline__ uint32_t hi_pair(uint32_t a, uint32_t b)
+{
+    return (a >> 16) | (b & 0xffff0000u);   // high halves of a and b
+}
 
 __global__ __launch_bounds__(kThreads) void transpose16_kernel(const uint16_t* __restrict__ in,
                                                                uint16_t* __restrict__ out,
                                                                int64_t rows, int64_t cols,
-                                                               int64_t tiles_c)
+                                                               int64_t tiles_c, int64_t ntiles)
 {
-    __shared__ __attribute__((aligned(16))) uint16_t t[kTile][kTile + kPad];
-    const int64_t tile = blockIdx.x;
-    const int64_t r0 = (tile / tiles_c) * kTile, c0 = (tile % tiles_c) * kTile;
-    const int tid = threadIdx.x;
+    const int lane = threadIdx.x & 63;
+    const int64_t tile = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+    if (tile >= ntiles) return;
+    // Lane -> 8 x 8 block: input rows 8 (lane % 8) .., input columns 8 (lane / 8) ..
+    const int64_t r = (tile / tiles_c) * kTile + 8 * (lane & 7);
+    const int64_t c = (tile % tiles_c) * kTile + 8 * (lane >> 3);
+    if (c >= cols) return;   // cols % 8 == 0: a block is all in or all out
 
-    // Read: thread -> row tid / 4, 16 columns from 16 (tid % 4).
-    {
-        const int r = tid >> 2, c = (tid & 3) * 16;
-        const int64_t gr = r0 + r, gc = c0 + c;
-        Vec16 v;
-        if (gr < rows && gc + 16 <= cols) {
-            const uint4* p = reinterpret_cast<const uint4*>(in + gr * cols + gc);
-            const uint4 a = p[0], b = p[1];
-            v = Vec16{{a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w}};
-        } else {
+    uint32_t w[8][4];   // w[i][k]: input row r + i, columns c + 2k, c + 2k + 1
+    if (r + 8 <= rows) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const uint32_t lo = (gr < rows && gc + 2 * j < cols) ? in[gr * cols + gc + 2 * j] : 0u;
-                const uint32_t hi =
-                    (gr < rows && gc + 2 * j + 1 < cols) ? in[gr * cols + gc + 2 * j + 1] : 0u;
-                v.w[j] = lo | (hi << 16);
-            }
+        for (int i = 0; i < 8; ++i) {
+            const uint4 v = *reinterpret_cast<const uint4*>(in + (r + i) * cols + c);
+            w[i][0] = v.x; w[i][1] = v.y; w[i][2] = v.z; w[i][3] = v.w;
         }
-        uint32_t* row = reinterpret_cast<uint32_t*>(&t[r][c]);
+    } else {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) row[j] = v.w[j];
+        for (int i = 0; i < 8; ++i) {
+            uint4 v = {0u, 0u, 0u, 0u};
+            if (r + i < rows) v = *reinterpret_cast<const uint4*>(in + (r + i) * cols + c);
+            w[i][0] = v.x; w[i][1] = v.y; w[i][2] = v.z; w[i][3] = v.w;
+        }
     }
-    __syncthreads();
-
-    // Write: thread -> output row (input column) tid / 4, 16 input rows from
-    // 16 (tid % 4).
-    {
-        const int c = tid >> 2, r = (tid & 3) * 16;
-        const int64_t gc = c0 + c, gr = r0 + r;
-        if (gc >= cols) return;
-        Vec16 v;
+    // Output row c + j holds input rows r .. r + 7 of column c + j.
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-            v.w[j] = (uint32_t)t[r + 2 * j][c] | ((uint32_t)t[r + 2 * j + 1][c] << 16);
-        uint16_t* q = out + gc * rows + gr;
-        if (gr + 16 <= rows && rows % 8 == 0) {
-            uint4* p = reinterpret_cast<uint4*>(q);
-            p[0] = uint4{v.w[0], v.w[1], v.w[2], v.w[3]};
-            p[1] = uint4{v.w[4], v.w[5], v.w[6], v.w[7]};
+    for (int j = 0; j < 8; ++j) {
+        uint32_t o[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+            o[m] = (j & 1) ? hi_pair(w[2 * m][j >> 1], w[2 * m + 1][j >> 1])
+                           : lo_pair(w[2 * m][j >> 1], w[2 * m + 1][j >> 1]);
+        uint16_t* q = out + (c + j) * rows + r;
+        if (r + 8 <= rows && rows % 8 == 0) {
+            *reinterpret_cast<uint4*>(q) = uint4{o[0], o[1], o[2], o[3]};
         } else {
 #pragma unroll
-            for (int j = 0; j < 16; ++j)
-                if (gr + j < rows) q[j] = (uint16_t)(v.w[j >> 1] >> (16 * (j & 1)));
+            for (int e = 0; e < 8; ++e)
+                if (r + e < rows) q[e] = (uint16_t)(o[e >> 1] >> (16 * (e & 1)));
         }
     }
 }
@@ -79,10 +76,12 @@ hipError_t transpose16(const void* in, void* out, int64_t rows, int64_t cols, hi
 {
     if (rows == 0 || cols == 0) return hipSuccess;
     const int64_t tiles_r = (rows + kTile - 1) / kTile, tiles_c = (cols + kTile - 1) / kTile;
-    if (tiles_r * tiles_c > INT32_MAX) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(transpose16_kernel, dim3((unsigned)(tiles_r * tiles_c)), dim3(kThreads), 0,
-                       stream, static_cast<const uint16_t*>(in), static_cast<uint16_t*>(out),
-                       rows, cols, tiles_c);
+    const int64_t ntiles = tiles_r * tiles_c;
+    const int64_t blocks = (ntiles + kWavesPerBlock - 1) / kWavesPerBlock;
+    if (blocks > INT32_MAX) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(transpose16_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream,
+                       static_cast<const uint16_t*>(in), static_cast<uint16_t*>(out), rows, cols,
+                       tiles_c, ntiles);
     return hipGetLastError();
 }
 
