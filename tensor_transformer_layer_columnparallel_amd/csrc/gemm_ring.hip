@@ -291,7 +291,7 @@ __device__ __forceinline__ bf16x8 read_frag_mn(const bf16* buf, int row0, int la
 
 template <int WM, bool A_KMAJ, bool B_KMAJ, Epi EPI, typename OutT>
 __global__ __launch_bounds__(kThreads, 1) void gemm_ring_kernel(GemmArgs p, int tiles_m,
-                                                                int tiles_n)
+                                                                int tiles_n, int group_m)
 {
     constexpr int BN = kBN;
     constexpr int kWavesM = WM, kWavesN = kWaves / WM;
@@ -313,7 +313,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_ring_kernel(GemmArgs p, int 
     const int ntiles = tiles_m * tiles_n;
     int tile = blockIdx.x;
     if (ntiles % kXcds == 0) tile = (tile % kXcds) * (ntiles / kXcds) + tile / kXcds;
-    const int tm = tile % tiles_m, tn = tile / tiles_m;
+    int tm = tile % tiles_m, tn = tile / tiles_m;
+    if (group_m > 0 && tiles_m % group_m == 0) {
+        // Tiles in groups of group_m tile rows, column by column inside a
+        // group, so that an XCD's run of tiles covers a group_m-row block.
+        const int per_group = group_m * tiles_n;
+        const int grp = tile / per_group, r = tile % per_group;
+        tm = grp * group_m + r % group_m;
+        tn = r / group_m;
+    }
     const int64_t m0 = (int64_t)tm * kBM, n0 = (int64_t)tn * BN;
 
     const i32x4 da = make_desc(p.A, (uint32_t)(p.M * p.K * 2));
@@ -490,8 +498,13 @@ hipError_t launch(const GemmArgs& p, hipStream_t stream)
     constexpr int WM = AK ? (BK ? TPMLP_RING_WM_NT : TPMLP_RING_WM_NN) : TPMLP_RING_WM_TN;
     const int tm = (int)((p.M + kBM - 1) / kBM);
     const int tn = (int)((p.N + kBN - 1) / kBN);
+    // Products with several waves of tiles (the weight gradients) walk an
+    // XCD's tiles in 4-row groups, which cut their time by about 4% on the
+    // device; one- and two-wave products keep the plain order, which measured
+    // as fast or faster for them.
+    const int group_m = tm * tn > 2 * kCUs ? 4 : 0;
     hipLaunchKernelGGL((gemm_ring_kernel<WM, AK, BK, E, O>), dim3((unsigned)(tm * tn)),
-                       dim3(kThreads), 0, stream, p, tm, tn);
+                       dim3(kThreads), 0, stream, p, tm, tn, group_m);
     return hipGetLastError();
 }
 
