@@ -129,6 +129,90 @@ def copy_calibration(reps: int):
     log(f"copy calibration: {reps} copies of {COPY_ROWS * COPY_COLS * 4} bytes")
 
 
+def max_engine_clock_mhz():
+    """The GPU agent's maximum engine clock as rocminfo reports it (None if
+    rocminfo is unavailable)."""
+    import subprocess
+    try:
+        txt = subprocess.run(["rocminfo"], capture_output=True, text=True, timeout=60).stdout
+    except (OSError, subprocess.SubprocessError):
+        return None
+    clock, is_gpu = None, False
+    for line in txt.splitlines():
+        line = line.strip()
+        if line.startswith("Device Type:"):
+            is_gpu = "GPU" in line
+        elif is_gpu and line.startswith("Max Clock Freq. (MHz):"):
+            clock = int(line.split(":")[1].split()[0])
+            break
+    return clock
+
+
+def vendor_matmul_context(T, h, n, reps=10):
+    """For context only (not the product path): torch.matmul (the vendor BLAS)
+    on the step's six products with bf16 outputs and no epilogue."""
+    import torch
+    bf, dev = torch.bfloat16, "cuda"
+    g = torch.Generator(device=dev).manual_seed(1)
+    r = lambda *sh: torch.randn(*sh, device=dev, generator=g).to(bf)
+    X, W1, H, W2, dZ, dY = r(T, h), r(h, n), r(T, n), r(n, h), r(T, h), r(T, n)
+    prods = [lambda: X @ W1, lambda: H @ W2, lambda: dZ @ W2.t(), lambda: H.t() @ dZ,
+             lambda: X.t() @ dY, lambda: dY @ W1.t()]
+    for f in prods:
+        f()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        for f in prods:
+            f()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    return {"what": "torch.matmul (vendor BLAS), same six products, bf16 out, no epilogue",
+            "ms_per_step": round(ms, 4), "tflops": round(12.0 * T * h * n / (ms * 1e-3) / 1e12, 2)}
+
+
+def attention_shard(B, aw, stream, sptr, reps=10):
+    """The attention block's two projections of one rank (QKV column-parallel
+    on head boundaries, output projection row-parallel with an fp32 partial)
+    at the GPT-3 shape, timed with HIP events on the launch stream."""
+    import torch
+    from tensor_transformer_layer_columnparallel_amd import synth
+    r = aw.ranks[0]
+    d = synth.make_attn_inputs(aw)
+    s = synth.attn_shard(aw, d, r)
+    dev = "cuda"
+    X, Wqkv, bqkv = d["X"].to(dev), s["Wqkv"].to(dev), s["bqkv"].to(dev)
+    O, Wo = s["O"].to(dev), s["Wo"].to(dev)
+    bf = torch.bfloat16
+    Y = torch.empty(aw.T, aw.qkv_width, dtype=bf, device=dev)
+    Z = torch.empty(aw.T, aw.h, dtype=torch.float32, device=dev)
+    qkv = lambda: B.tp_column_linear(X, Wqkv, bqkv, Y, None, aw.T, aw.h, 3 * aw.h, aw.t, r, bf,
+                                     bf, B.TP_ACT_NONE, stream=sptr)
+    proj = lambda: B.tp_row_linear(O, Wo, Z, aw.T, aw.h, aw.h, aw.t, r, bf, torch.float32,
+                                   stream=sptr)
+    times = []
+    for f in (qkv, proj):
+        f()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            f()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) / reps)
+    fl = aw.qkv_flops() + aw.out_flops()
+    return {"workload": f"gpt3-shaped attention projections, rank {r} of t={aw.t}: "
+                        f"QKV [{aw.T},{aw.h}]x[{aw.h},{aw.qkv_width}] + bias (head-boundary "
+                        f"shard), out-proj [{aw.T},{aw.w}]x[{aw.w},{aw.h}] -> fp32",
+            "qkv_ms": round(times[0], 4), "out_proj_ms": round(times[1], 4),
+            "qkv_tflops": round(aw.qkv_flops() / (times[0] * 1e-3) / 1e12, 2),
+            "out_proj_tflops": round(aw.out_flops() / (times[1] * 1e-3) / 1e12, 2),
+            "tflops": round(fl / ((times[0] + times[1]) * 1e-3) / 1e12, 2)}
+
+
 def cpu_baseline(w, d_h, seconds: float):
     """Times the fp64 oracle on a bounded sample: chunks of 32 token rows of
     the same workload, each chunk a full forward + backward (6 products) of
@@ -165,6 +249,10 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="wall-clock budget of the oracle baseline (0 disables it)")
     ap.add_argument("--no-reduce", action="store_true", help="skip the shard-sum measurement")
+    ap.add_argument("--no-attention", action="store_true",
+                    help="skip the attention-projection measurement")
+    ap.add_argument("--no-vendor", action="store_true",
+                    help="skip the vendor-BLAS context timing (torch.matmul)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="REPS",
                     help="only run the HBM-counter calibration copy REPS times")
     ap.add_argument("--ingest-counters", nargs=4,
@@ -191,8 +279,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     props = torch.cuda.get_device_properties(dev)
+    clock_mhz = max_engine_clock_mhz()
     log(f"device: {props.name}, {props.multi_processor_count} CUs, "
-        f"{props.total_memory / 2**30:.0f} GiB")
+        f"{props.total_memory / 2**30:.0f} GiB, max engine clock {clock_mhz} MHz")
 
     w = configs.GPT3_SHARD
     T, h, ffn, t, n = w.T, w.h, w.ffn, w.t, w.n
@@ -244,7 +333,10 @@ def main():
     wall = time.perf_counter() - wall0
     total_ms = start.elapsed_time(end)
     ms_step = total_ms / args.steps
-    col_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    col_list = sorted(e[0].elapsed_time(e[1]) for e in evs)
+    step_list = sorted(e[0].elapsed_time(e[3]) for e in evs)
+    col_med, step_med = col_list[len(col_list) // 2], step_list[len(step_list) // 2]
+    col_ms = sum(col_list) / args.steps
     row_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
     bwd_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
     log(f"timed {args.steps} steps: {ms_step:.3f} ms/step (wall {wall * 1e3 / args.steps:.3f}); "
@@ -271,8 +363,23 @@ def main():
            "pct_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
            "fwd_tflops": round(fwd_flops / ((col_ms + row_ms) * 1e-3) / 1e12, 2),
            "bwd_tflops": round(bwd_flops / (bwd_ms * 1e-3) / 1e12, 2),
-           "roofline": roofline}
+           "roofline": roofline,
+           "median": {"ms_per_step": round(step_med, 4), "column_gemm_ms": round(col_med, 4),
+                      "column_gemm_tflops": round(gemm / (col_med * 1e-3) / 1e12, 2)},
+           "device": {"name": props.name, "cus": props.multi_processor_count,
+                      "max_engine_clock_mhz": clock_mhz}}
     del H, Y, Z, dY, dW2, dW1, dX, db1
+
+    if not args.no_attention:
+        out["attention_shard"] = attention_shard(B, configs.ATTN_GPT3, stream, sptr)
+        a = out["attention_shard"]
+        log(f"attention shard: QKV {a['qkv_ms']:.4f} ms, out-proj {a['out_proj_ms']:.4f} ms, "
+            f"{a['tflops']:.1f} TFLOP/s")
+
+    if not args.no_vendor:
+        out["context_vendor_matmul"] = vendor_matmul_context(T, h, n)
+        log(f"vendor BLAS context: {out['context_vendor_matmul']['ms_per_step']:.3f} ms for "
+            f"the six products")
 
     if not args.no_reduce:
         wr = configs.FULL_LAYER_8

@@ -69,9 +69,63 @@ FULL_LAYER_8 = Workload("full_layer_emulation_t8", T=4096, h=8192, ffn=28672, t=
 ALL = {w.name: w for w in (TINY_F32, COLUMN_768, GPT3_SHARD, FULL_LAYER_8)}
 
 
+@dataclass(frozen=True)
+class AttnWorkload:
+    """One rank's share of an attention block's two projections: the QKV
+    projection split column-wise on head boundaries (rank r owns heads
+    [r*H/t, (r+1)*H/t) of Q, K and V) and the output projection split
+    row-wise (pages "PaddlePaddle张量并行", introduction; "张量并行实战",
+    section "扩展思考：适配Transformer模块"; "Tensor Parallelism原理与实践",
+    section 4.2).  The attention core between the two is not part of it."""
+    name: str
+    T: int           # tokens
+    h: int           # hidden size
+    heads: int       # attention heads
+    t: int           # tensor-parallel degree
+    dtype: str = "bf16"
+    ranks: tuple = (0,)
+    std_w: float = 0.02
+    note: str = field(default="", compare=False)
+
+    @property
+    def w(self) -> int:
+        """Columns of Q (or K, or V) a rank owns: heads/t heads of h/heads."""
+        assert self.h % self.heads == 0 and self.heads % self.t == 0
+        return self.h // self.t
+
+    @property
+    def qkv_width(self) -> int:
+        return 3 * self.w
+
+    def qkv_flops(self) -> float:
+        return 2.0 * self.T * self.h * self.qkv_width
+
+    def out_flops(self) -> float:
+        return 2.0 * self.T * self.w * self.h
+
+
+# Small attention shard for element-wise parity: 8 heads of 64, t=4.
+ATTN_SMALL = AttnWorkload("attn_shard_small_t4", T=300, h=512, heads=8, t=4, ranks=(0, 1, 2, 3),
+                          note="X[300,512], W_qkv_r[512,384], W_o_r[128,512]")
+
+# GPT-3-shaped attention shard: 96 heads of 128, t=8 (12 heads per rank).
+ATTN_GPT3 = AttnWorkload("gpt3_attn_shard_t8", T=2048, h=12288, heads=96, t=8, ranks=(3,),
+                         note="X[2048,12288], W_qkv_r[12288,4608], W_o_r[1536,12288]")
+
+
 def scaled(w: Workload, name: str, **kw) -> Workload:
     """A copy of ``w`` with some shape fields replaced (reduced parity cases)."""
     d = dict(w.__dict__)
     d.update(kw)
     d["name"] = name
     return Workload(**d)
+
+
+def scaled_attn(aw: AttnWorkload, name: str, **kw) -> AttnWorkload:
+    """A copy of ``aw`` with some shape fields replaced."""
+    d = dict(aw.__dict__)
+    d.update(kw)
+    d["name"] = name
+    if "ranks" not in kw:
+        d["ranks"] = tuple(range(d["t"]))
+    return AttnWorkload(**d)

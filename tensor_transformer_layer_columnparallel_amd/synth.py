@@ -20,9 +20,10 @@ from __future__ import annotations
 
 import torch
 
-from .configs import Workload
+from .configs import AttnWorkload, Workload
 
 TAG_X, TAG_W1, TAG_B1, TAG_W2, TAG_DZ = 1, 2, 3, 4, 5
+TAG_WQKV, TAG_BQKV, TAG_O, TAG_WO = 6, 7, 8, 9
 
 
 def _gen(seed: int, tag: int, rank: int = 0) -> torch.Generator:
@@ -64,3 +65,37 @@ def make_inputs(w: Workload, seed: int = 0, ranks=None, with_dz: bool | None = N
             out["W2"][r] = draw((w.n, w.h), w.std_w, seed, TAG_W2, r, dt)
     out["dZ"] = draw((w.T, w.h), 1.0, seed, TAG_DZ, 0, dt) if with_dz else None
     return out
+
+
+def make_attn_inputs(aw: AttnWorkload, seed: int = 0) -> dict:
+    """Host tensors for an attention-projection workload, unsharded:
+    ``{"X": [T,h], "Wqkv": [h,3h] = [Wq | Wk | Wv], "bqkv": [3h],
+    "O": [T,h] (the attention core's output, drawn), "Wo": [h,h]}``.
+    Same recipe as :func:`make_inputs` (std 1 for activations, std_w for
+    weights and biases, one bf16 rounding)."""
+    dt = torch.float32 if aw.dtype == "f32" else torch.bfloat16
+    h = aw.h
+    return {"X": draw((aw.T, h), 1.0, seed, TAG_X, 0, dt),
+            "Wqkv": draw((h, 3 * h), aw.std_w, seed, TAG_WQKV, 0, dt),
+            "bqkv": draw((3 * h,), aw.std_w, seed, TAG_BQKV, 0, dt),
+            "O": draw((aw.T, h), 1.0, seed, TAG_O, 0, dt),
+            "Wo": draw((h, h), aw.std_w, seed, TAG_WO, 0, dt)}
+
+
+def qkv_columns(aw: AttnWorkload, r: int) -> torch.Tensor:
+    """Column indices of [Wq | Wk | Wv] that rank r owns: its heads' columns
+    of Q, then of K, then of V (a head-boundary split, not a contiguous
+    block of the fused weight)."""
+    w = aw.w
+    return torch.cat([torch.arange(part * aw.h + r * w, part * aw.h + (r + 1) * w)
+                      for part in range(3)])
+
+
+def attn_shard(aw: AttnWorkload, full: dict, r: int) -> dict:
+    """Rank r's operands: W_qkv_r [h, 3h/t], b_qkv_r [3h/t], O_r [T, h/t]
+    (the columns of its heads) and W_o_r [h/t, h] (the matching rows)."""
+    cols = qkv_columns(aw, r)
+    w = aw.w
+    return {"Wqkv": full["Wqkv"][:, cols].contiguous(), "bqkv": full["bqkv"][cols].contiguous(),
+            "O": full["O"][:, r * w:(r + 1) * w].contiguous(),
+            "Wo": full["Wo"][r * w:(r + 1) * w, :].contiguous()}

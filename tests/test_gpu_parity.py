@@ -131,6 +131,68 @@ def test_row_linear_ragged_partials_sum(B):
     assert_close(Z, oracle.row_linear(Xf, Wf), "bf16", "row partial sum")
 
 
+# ------------------------------------- attention block: QKV and output proj
+
+def _attn_qkv_gpu(B, aw, d, s, r):
+    T, h = aw.T, aw.h
+    Y = torch.empty(T, aw.qkv_width, dtype=torch.bfloat16, device="cuda")
+    st = B.tp_column_linear(dev(d["X"]), dev(s["Wqkv"]), dev(s["bqkv"]), Y, None, T, h, 3 * h,
+                            aw.t, r, B.TP_BF16, B.TP_BF16, B.TP_ACT_NONE)
+    assert st == 0
+    return Y
+
+
+def test_attention_qkv_head_shards_small(B):
+    """Every rank's QKV projection (heads split on boundaries) vs the oracle."""
+    aw = configs.ATTN_SMALL
+    d = synth.make_attn_inputs(aw)
+    for r in aw.ranks:
+        _log(f"case {aw.name} qkv rank {r}")
+        s = synth.attn_shard(aw, d, r)
+        Y = _attn_qkv_gpu(B, aw, d, s, r)
+        torch.cuda.synchronize()
+        assert_close(Y, oracle.column_linear(d["X"], s["Wqkv"], s["bqkv"]), "bf16",
+                     f"{aw.name} QKV r{r}")
+
+
+def test_attention_output_projection_small(B):
+    """Row-parallel output projection of every rank, summed on the device,
+    vs the oracle's unsharded O W_o."""
+    aw = configs.ATTN_SMALL
+    d = synth.make_attn_inputs(aw)
+    T, h = aw.T, aw.h
+    parts = torch.empty(aw.t, T, h, dtype=torch.float32, device="cuda")
+    for r in range(aw.t):
+        _log(f"case {aw.name} out-proj rank {r}")
+        s = synth.attn_shard(aw, d, r)
+        assert B.tp_row_linear(dev(s["O"]), dev(s["Wo"]), parts[r], T, h, h, aw.t, r, B.TP_BF16,
+                               B.TP_F32) == 0
+    Z = torch.empty(T, h, dtype=torch.float32, device="cuda")
+    B.tp_shard_reduce(parts, Z, T, h, aw.t, B.TP_REDUCE_SUM, B.TP_F32, B.TP_F32)
+    torch.cuda.synchronize()
+    assert_close(Z, oracle.row_linear(d["O"], d["Wo"]), "bf16", f"{aw.name} O W_o")
+
+
+def test_attention_gpt3_shard_sampled(B):
+    """GPT-3-shaped attention shard (96 heads, t = 8, rank 3) at full size,
+    in the bench's launch configuration, on sampled rows."""
+    aw = configs.ATTN_GPT3
+    r = aw.ranks[0]
+    _log(f"case {aw.name} rank {r}")
+    d = synth.make_attn_inputs(aw)
+    s = synth.attn_shard(aw, d, r)
+    Y = _attn_qkv_gpu(B, aw, d, s, r)
+    Z = torch.empty(aw.T, aw.h, dtype=torch.float32, device="cuda")
+    assert B.tp_row_linear(dev(s["O"]), dev(s["Wo"]), Z, aw.T, aw.h, aw.h, aw.t, r, B.TP_BF16,
+                           B.TP_F32) == 0
+    torch.cuda.synchronize()
+    rows = sample_indices(aw.T, 4, seed=7)
+    assert_close(Y[rows], oracle.column_linear(d["X"][rows], s["Wqkv"], s["bqkv"]), "bf16",
+                 f"{aw.name} QKV rows")
+    assert_close(Z[rows], oracle.row_linear(s["O"][rows], s["Wo"]), "bf16",
+                 f"{aw.name} out-proj rows")
+
+
 # ------------------------------------------------- reduced MLP, full compare
 
 REDUCED = [

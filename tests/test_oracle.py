@@ -301,3 +301,41 @@ def test_shard_concat_then_slice_is_identity():
     out = oracle.shard_concat(parts)
     for r in range(3):
         assert np.array_equal(out[:, r * 5:(r + 1) * 5], parts[r])
+
+
+# ------------------------------------------------ attention-block projections
+
+def test_attention_qkv_head_shards_equal_unsharded_heads():
+    """QKV split on head boundaries (page "张量并行实战", section "扩展思考：
+    适配Transformer模块"; "Tensor Parallelism原理与实践" section 4.2): rank r's
+    column-parallel output is exactly the unsharded Q, K and V columns of its
+    heads, checked against a numpy float64 product of the fused weight."""
+    from tensor_transformer_layer_columnparallel_amd import configs, synth
+    aw = configs.scaled_attn(configs.ATTN_SMALL, "attn_pin", T=40, h=96, heads=6, t=3)
+    d = synth.make_attn_inputs(aw, seed=5)
+    X = d["X"].double().numpy()
+    full = X @ d["Wqkv"].double().numpy() + d["bqkv"].double().numpy()
+    hd = aw.h // aw.heads
+    for r in range(aw.t):
+        s = synth.attn_shard(aw, d, r)
+        got = oracle.column_linear(d["X"], s["Wqkv"], s["bqkv"])
+        assert got.shape == (aw.T, aw.qkv_width)
+        for part in range(3):   # Q, K, V
+            for j in range(aw.heads // aw.t):
+                head = r * (aw.heads // aw.t) + j
+                ref = full[:, part * aw.h + head * hd: part * aw.h + (head + 1) * hd]
+                g = got[:, part * aw.w + j * hd: part * aw.w + (j + 1) * hd]
+                np.testing.assert_allclose(g, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_attention_output_projection_partials_sum_to_unsharded():
+    """Row-parallel output projection: the t partials O_r W_o,r (O_r = the
+    columns of rank r's heads) add up to O W_o (the all_reduce of page
+    "张量并行实战", section "扩展思考：适配Transformer模块")."""
+    from tensor_transformer_layer_columnparallel_amd import configs, synth
+    aw = configs.scaled_attn(configs.ATTN_SMALL, "attn_pin", T=40, h=96, heads=6, t=3)
+    d = synth.make_attn_inputs(aw, seed=6)
+    parts = [oracle.row_linear(synth.attn_shard(aw, d, r)["O"], synth.attn_shard(aw, d, r)["Wo"])
+             for r in range(aw.t)]
+    ref = d["O"].double().numpy() @ d["Wo"].double().numpy()
+    np.testing.assert_allclose(oracle.shard_sum(np.stack(parts)), ref, rtol=1e-12, atol=1e-12)
