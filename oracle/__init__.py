@@ -67,6 +67,8 @@ def _load():
             "oracle_mlp_shard_bwd": [dp] * 11 + [i64, i64, i64],
             "oracle_shard_sum": [dp, dp, ctypes.c_int, i64],
             "oracle_shard_concat": [dp, dp, ctypes.c_int, i64, i64],
+            "oracle_reduce_scatter": [dp, dp, ctypes.c_int, i64, i64, ctypes.c_int],
+            "oracle_layernorm": [dp, dp, dp, dp, i64, i64, ctypes.c_double],
         }
         for name, args in sig.items():
             fn = getattr(lib, name)
@@ -180,6 +182,28 @@ def shard_concat(parts) -> np.ndarray:
     out = np.empty((rows, t * cols), dtype=np.float64)
     _load().oracle_shard_concat(_p(parts), _p(out), t, rows, cols)
     return out
+
+
+def reduce_scatter(parts, rank: int) -> np.ndarray:
+    """Rank ``rank``'s block of rows of Σ_r parts[r]; parts is [t, rows, cols]
+    with rows divisible by t."""
+    parts = _f64(parts)
+    t, rows, cols = parts.shape
+    assert rows % t == 0 and 0 <= rank < t
+    out = np.empty((rows // t, cols), dtype=np.float64)
+    _load().oracle_reduce_scatter(_p(parts), _p(out), t, rows, cols, rank)
+    return out
+
+
+def layernorm(x, gamma=None, beta=None, eps: float = 1e-5) -> np.ndarray:
+    """Row-wise layer normalisation of x [rows, cols] (biased variance)."""
+    x = _f64(x)
+    rows, cols = x.shape
+    g = None if gamma is None else _f64(gamma)
+    b = None if beta is None else _f64(beta)
+    y = np.empty_like(x)
+    _load().oracle_layernorm(_p(x), _p(g), _p(b), _p(y), rows, cols, float(eps))
+    return y
 
 
 # ---------------------------------------------------------------- sampling

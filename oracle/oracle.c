@@ -222,3 +222,53 @@ ORACLE_API void oracle_shard_concat(const double* parts, double* out, int t,
             memcpy(out + m * (t * cols) + (int64_t)r * cols,
                    parts + ((int64_t)r * rows + m) * cols, (size_t)cols * sizeof(double));
 }
+
+/* Sequence-parallel stand-ins.  Sequence parallelism extends tensor
+ * parallelism by splitting the token dimension [P2 "延伸阅读", "相关概念推荐"];
+ * the partial outputs are then combined by a ReduceScatter instead of an
+ * AllReduce [P1 introduction]: rank `rank` keeps only its block of
+ * rows / t tokens of the sum,
+ *   out[m][c] = sum_{r=0}^{t-1} parts[r][rank * rows / t + m][c],
+ * parts is [t][rows][cols], out is [rows / t][cols]; ranks added in order. */
+ORACLE_API void oracle_reduce_scatter(const double* parts, double* out, int t, int64_t rows,
+                                      int64_t cols, int rank)
+{
+    const int64_t rr = rows / t;
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < rr; ++m)
+        for (int64_t c = 0; c < cols; ++c) {
+            double s = 0.0;
+            for (int r = 0; r < t; ++r)
+                s += parts[((int64_t)r * rows + (int64_t)rank * rr + m) * cols + c];
+            out[m * cols + c] = s;
+        }
+}
+
+/* Layer normalisation of whole rows (a token shard holds every hidden
+ * column of its tokens, so the statistics need no exchange; the pages keep
+ * normalisations unsplit [P1 introduction] or exchange the statistics when
+ * the hidden dimension is split [P4 §4.2]):
+ *   mu = (1/cols) sum_c x[m][c];  var = (1/cols) sum_c (x[m][c] - mu)^2
+ *   y[m][c] = (x[m][c] - mu) / sqrt(var + eps) * gamma[c] + beta[c]
+ * gamma == NULL means 1, beta == NULL means 0. */
+ORACLE_API void oracle_layernorm(const double* x, const double* gamma, const double* beta,
+                                 double* y, int64_t rows, int64_t cols, double eps)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < rows; ++m) {
+        const double* xr = x + m * cols;
+        double mu = 0.0;
+        for (int64_t c = 0; c < cols; ++c) mu += xr[c];
+        mu /= (double)cols;
+        double var = 0.0;
+        for (int64_t c = 0; c < cols; ++c) var += (xr[c] - mu) * (xr[c] - mu);
+        var /= (double)cols;
+        const double inv = 1.0 / sqrt(var + eps);
+        for (int64_t c = 0; c < cols; ++c) {
+            double v = (xr[c] - mu) * inv;
+            if (gamma) v *= gamma[c];
+            if (beta) v += beta[c];
+            y[m * cols + c] = v;
+        }
+    }
+}

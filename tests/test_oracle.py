@@ -339,3 +339,53 @@ def test_attention_output_projection_partials_sum_to_unsharded():
              for r in range(aw.t)]
     ref = d["O"].double().numpy() @ d["Wo"].double().numpy()
     np.testing.assert_allclose(oracle.shard_sum(np.stack(parts)), ref, rtol=1e-12, atol=1e-12)
+
+
+# ------------------------------------------- sequence parallelism: RS and LN
+
+def test_layernorm_hand_worked_row():
+    # x = [1, 2, 3, 4]: mean 5/2, biased variance 5/4, so with eps = 0 the
+    # normalised row is (x - 5/2) / sqrt(5/4) = [-3, -1, 1, 3] / sqrt(5).
+    y = oracle.layernorm(np.array([[1.0, 2.0, 3.0, 4.0]]), eps=0.0)
+    np.testing.assert_allclose(y[0], np.array([-3.0, -1.0, 1.0, 3.0]) / np.sqrt(5.0),
+                               rtol=0, atol=1e-15)
+
+
+def test_layernorm_moments_closed_form_and_constant_rows():
+    rng = np.random.default_rng(3)
+    x = rng.normal(2.0, 3.0, size=(7, 96))
+    eps = 1e-5
+    y = oracle.layernorm(x, eps=eps)
+    var = x.var(axis=1)
+    np.testing.assert_allclose(y.mean(axis=1), 0.0, atol=1e-13)
+    np.testing.assert_allclose((y * y).mean(axis=1), var / (var + eps), rtol=1e-12)
+    beta = rng.normal(size=96)
+    yc = oracle.layernorm(np.full((3, 96), 4.25), gamma=rng.normal(size=96), beta=beta, eps=eps)
+    np.testing.assert_allclose(yc, np.broadcast_to(beta, (3, 96)), rtol=0, atol=1e-15)
+
+
+def test_layernorm_matches_torch_float64_and_is_affine_invariant():
+    g = torch.Generator().manual_seed(4)
+    x = torch.randn(9, 160, dtype=torch.float64, generator=g)
+    gamma = torch.randn(160, dtype=torch.float64, generator=g)
+    beta = torch.randn(160, dtype=torch.float64, generator=g)
+    ref = torch.nn.functional.layer_norm(x, (160,), gamma, beta, eps=1e-5).numpy()
+    np.testing.assert_allclose(oracle.layernorm(x.numpy(), gamma.numpy(), beta.numpy(), 1e-5),
+                               ref, rtol=1e-12, atol=1e-12)
+    xn = x.numpy()
+    np.testing.assert_allclose(oracle.layernorm(3.5 * xn - 7.0, eps=0.0),
+                               oracle.layernorm(xn, eps=0.0), rtol=1e-11, atol=1e-11)
+
+
+@pytest.mark.parametrize("t", [1, 2, 4, 8])
+def test_reduce_scatter_is_the_ranks_block_of_the_sum(t):
+    """ReduceScatter over tokens (page "PaddlePaddle张量并行", introduction):
+    rank r keeps rows [r*T/t, (r+1)*T/t) of the sum; integer-valued parts
+    make every sum exact, compared with numpy's sum."""
+    rng = np.random.default_rng(t)
+    T, cols = 8 * t, 24
+    parts = rng.integers(-1000, 1000, size=(t, T, cols)).astype(np.float64)
+    full = parts.sum(axis=0)
+    for r in range(t):
+        got = oracle.reduce_scatter(parts, r)
+        assert np.array_equal(got, full[r * (T // t):(r + 1) * (T // t)])
