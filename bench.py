@@ -213,6 +213,52 @@ def attention_shard(B, aw, stream, sptr, reps=10):
             "tflops": round(fl / ((times[0] + times[1]) * 1e-3) / 1e12, 2)}
 
 
+def sequence_parallel(B, stream, sptr, reps=10):
+    """The sequence-parallel stand-ins at the GPT-3 shape (t = 8, 2048
+    tokens, h = 12288), each HBM-bound and reported in GB/s: ReduceScatter of
+    the eight fp32 row-layer partials to one rank's 256 tokens, layer norm of
+    that shard (fp32 in, bf16 out), and the token AllGather of eight bf16
+    shards."""
+    import torch
+    T, h, t, r = 2048, 12288, 8, 0
+    Tr = T // t
+    parts = torch.randn(t, T, h, device="cuda")
+    rs = torch.empty(Tr, h, device="cuda")
+    gam = torch.ones(h, dtype=torch.bfloat16, device="cuda")
+    bet = torch.zeros(h, dtype=torch.bfloat16, device="cuda")
+    y = torch.empty(Tr, h, dtype=torch.bfloat16, device="cuda")
+    shards = torch.randn(t, Tr, h, device="cuda").bfloat16()
+    full = torch.empty(T, h, dtype=torch.bfloat16, device="cuda")
+    bf, f32 = torch.bfloat16, torch.float32
+    ops = {
+        "reduce_scatter": (lambda: B.tp_shard_reduce_scatter(parts, rs, T, h, t, r, f32, f32,
+                                                             stream=sptr),
+                           (t * Tr * h + Tr * h) * 4),
+        "layernorm": (lambda: B.tp_layernorm(rs, gam, bet, y, Tr, h, 1e-5, f32, bf, stream=sptr),
+                      Tr * h * 4 + Tr * h * 2 + 2 * h * 2),
+        "concat_tokens": (lambda: B.tp_shard_reduce(shards, full, Tr, h, t,
+                                                    B.TP_REDUCE_CONCAT_TOKENS, bf, bf,
+                                                    stream=sptr),
+                          2 * T * h * 2),
+    }
+    out = {"workload": f"t={t}, {T} tokens, h={h}: ReduceScatter of {t} fp32 partials to "
+                       f"{Tr} tokens; layer norm of the shard (fp32 -> bf16); token "
+                       f"AllGather of {t} bf16 shards", "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    for name, (f, nbytes) in ops.items():
+        f()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            f()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        out[name] = {"ms": round(ms, 4), "bytes": nbytes,
+                     "achieved": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+    return out
+
+
 def cpu_baseline(w, d_h, seconds: float):
     """Times the fp64 oracle on a bounded sample: chunks of 32 token rows of
     the same workload, each chunk a full forward + backward (6 products) of
@@ -249,6 +295,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="wall-clock budget of the oracle baseline (0 disables it)")
     ap.add_argument("--no-reduce", action="store_true", help="skip the shard-sum measurement")
+    ap.add_argument("--no-sp", action="store_true",
+                    help="skip the sequence-parallel stand-ins")
     ap.add_argument("--no-attention", action="store_true",
                     help="skip the attention-projection measurement")
     ap.add_argument("--no-vendor", action="store_true",
@@ -375,6 +423,13 @@ def main():
         a = out["attention_shard"]
         log(f"attention shard: QKV {a['qkv_ms']:.4f} ms, out-proj {a['out_proj_ms']:.4f} ms, "
             f"{a['tflops']:.1f} TFLOP/s")
+
+    if not args.no_sp:
+        out["sequence_parallel"] = sequence_parallel(B, stream, sptr)
+        sp = out["sequence_parallel"]
+        log("sequence parallel: " + ", ".join(f"{k} {sp[k]['ms']:.4f} ms {sp[k]['achieved']:.0f} GB/s"
+                                              for k in ("reduce_scatter", "layernorm",
+                                                        "concat_tokens")))
 
     if not args.no_vendor:
         out["context_vendor_matmul"] = vendor_matmul_context(T, h, n)

@@ -20,7 +20,11 @@
  *        "PyTorch 实现示例：自定义张量并行 Linear 层" (weight shard
  *        [in, out/t], x @ W + b, divisibility assert, rank-ordered concat).
  *   [P4] "Tensor Parallelism原理与实践：大模型训练的关键技术", §2.1 (block
- *        product, sum of partials), §3.1 (column and row backward).
+ *        product, sum of partials), §3.1 (column and row backward), §4.2
+ *        (split strategies per layer type: attention, layer normalisation).
+ * Sequence parallelism (the token dimension split as well) is named by [P2]
+ * section "延伸阅读" ("相关概念推荐") as the long-sequence extension of tensor
+ * parallelism; its ReduceScatter is [P1]'s alternative to the AllReduce.
  *
  * Conventions shared by every entry point:
  *   - Matrices are dense, row-major and contiguous.  Weights are stored
@@ -72,7 +76,7 @@ typedef enum {
 
 typedef enum { TP_F32 = 0, TP_BF16 = 1 } tp_dtype;
 typedef enum { TP_ACT_NONE = 0, TP_ACT_GELU_TANH = 1 } tp_act;
-typedef enum { TP_REDUCE_SUM = 0, TP_REDUCE_CONCAT = 1 } tp_reduce_op;
+typedef enum { TP_REDUCE_SUM = 0, TP_REDUCE_CONCAT = 1, TP_REDUCE_CONCAT_TOKENS = 2 } tp_reduce_op;
 
 /*
  * Column-parallel linear on one shard [P3; P4 §2.1; P1]:
@@ -158,10 +162,45 @@ TP_API int tp_mlp_shard_bwd(const void* X, const void* W1_i, const void* W2_i,
  *   TP_REDUCE_CONCAT (AllGather + concat along the last dim [P3; P1]):
  *                    out[m][r*cols + c] = parts[r][m][c], out
  *                    [tokens][t*cols]; requires out_dtype == in_dtype.
+ *   TP_REDUCE_CONCAT_TOKENS (AllGather of token shards before the column
+ *                    layer under sequence parallelism [P2 "延伸阅读"]):
+ *                    out[r*tokens + m][c] = parts[r][m][c], out
+ *                    [t*tokens][cols]; requires out_dtype == in_dtype.
  * cols must be a positive multiple of 8; parts and out must not overlap.
  */
 TP_API int tp_shard_reduce(const void* parts, void* out, int64_t tokens, int64_t cols, int t,
                     int op, int in_dtype, int out_dtype, void* stream);
+
+/*
+ * ReduceScatter over tokens, the sequence-parallel replacement of the
+ * AllReduce of row-parallel partials [P1 introduction; P2 "延伸阅读"]: rank
+ * `rank` keeps only its block of tokens / t rows of the sum,
+ *   out[m][c] = parts[0][rank*tokens/t + m][c] + ... + parts[t-1][...][c],
+ * added in fp32 in rank order 0..t-1.  parts is [t][tokens][cols] (type
+ * in_dtype), out [tokens/t][cols] (type out_dtype).  tokens % t != 0 ->
+ * TP_ERR_INDIVISIBLE; rank outside [0, t) -> TP_ERR_RANK; cols must be a
+ * positive multiple of 8; parts and out must not overlap.
+ */
+TP_API int tp_shard_reduce_scatter(const void* parts, void* out, int64_t tokens, int64_t cols,
+                                   int t, int rank, int in_dtype, int out_dtype, void* stream);
+
+/*
+ * Layer normalisation of whole rows, as a sequence-parallel rank applies it
+ * to its token shard: each row holds every hidden column, so its statistics
+ * need no exchange (the pages keep normalisations unsplit [P1 introduction]
+ * or exchange statistics when the hidden dimension itself is split [P4
+ * §4.2]):
+ *   mu = mean_c x[m][c];  var = mean_c (x[m][c] - mu)^2  (biased)
+ *   y[m][c] = (x[m][c] - mu) / sqrt(var + eps) * gamma[c] + beta[c]
+ * Statistics in fp32 with a fixed reduction order (bitwise reproducible).
+ * x [tokens][cols] of type in_dtype; y [tokens][cols] and gamma, beta [cols]
+ * of type out_dtype; gamma NULL means 1, beta NULL means 0.  eps must be
+ * finite and >= 0 (TP_ERR_ARG otherwise); cols a positive multiple of 8.
+ * x and y may be the same buffer only when in_dtype == out_dtype.
+ */
+TP_API int tp_layernorm(const void* x, const void* gamma, const void* beta, void* y,
+                        int64_t tokens, int64_t cols, float eps, int in_dtype, int out_dtype,
+                        void* stream);
 
 /* Static description of a status code (never NULL). */
 TP_API const char* tp_status_string(int status);

@@ -21,10 +21,11 @@ TP_ERR_NULL, TP_ERR_SHAPE, TP_ERR_INDIVISIBLE, TP_ERR_RANK = -1, -2, -3, -4
 TP_ERR_DTYPE, TP_ERR_ALIGN, TP_ERR_HIP, TP_ERR_ARG = -5, -6, -7, -8
 TP_F32, TP_BF16 = 0, 1
 TP_ACT_NONE, TP_ACT_GELU_TANH = 0, 1
-TP_REDUCE_SUM, TP_REDUCE_CONCAT = 0, 1
+TP_REDUCE_SUM, TP_REDUCE_CONCAT, TP_REDUCE_CONCAT_TOKENS = 0, 1, 2
 
 ABI_FUNCTIONS = ("tp_column_linear", "tp_row_linear", "tp_mlp_shard_fwd",
-                 "tp_mlp_shard_bwd", "tp_shard_reduce", "tp_status_string")
+                 "tp_mlp_shard_bwd", "tp_shard_reduce", "tp_shard_reduce_scatter",
+                 "tp_layernorm", "tp_status_string")
 
 
 class TPError(RuntimeError):
@@ -43,6 +44,8 @@ def load_library() -> ctypes.CDLL:
     lib.tp_mlp_shard_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, ci, ci, ci, vp]
     lib.tp_mlp_shard_bwd.argtypes = [vp] * 11 + [i64, i64, i64, ci, ci, ci, vp]
     lib.tp_shard_reduce.argtypes = [vp, vp, i64, i64, ci, ci, ci, ci, vp]
+    lib.tp_shard_reduce_scatter.argtypes = [vp, vp, i64, i64, ci, ci, ci, ci, vp]
+    lib.tp_layernorm.argtypes = [vp, vp, vp, vp, i64, i64, ctypes.c_float, ci, ci, vp]
     for name in ABI_FUNCTIONS[:-1]:
         getattr(lib, name).restype = ci
     lib.tp_status_string.argtypes = [ci]
@@ -124,6 +127,20 @@ def tp_shard_reduce(parts, out, tokens, cols, t, op, in_dtype, out_dtype, stream
     st = _lib.tp_shard_reduce(_ptr(parts), _ptr(out), tokens, cols, t, int(op), _dt(in_dtype),
                               _dt(out_dtype), _stream(stream))
     return _ret("tp_shard_reduce", st, check)
+
+
+def tp_shard_reduce_scatter(parts, out, tokens, cols, t, rank, in_dtype, out_dtype, stream=None,
+                            check=True) -> int:
+    st = _lib.tp_shard_reduce_scatter(_ptr(parts), _ptr(out), tokens, cols, t, rank,
+                                      _dt(in_dtype), _dt(out_dtype), _stream(stream))
+    return _ret("tp_shard_reduce_scatter", st, check)
+
+
+def tp_layernorm(x, gamma, beta, y, tokens, cols, eps, in_dtype, out_dtype, stream=None,
+                 check=True) -> int:
+    st = _lib.tp_layernorm(_ptr(x), _ptr(gamma), _ptr(beta), _ptr(y), tokens, cols, float(eps),
+                           _dt(in_dtype), _dt(out_dtype), _stream(stream))
+    return _ret("tp_layernorm", st, check)
 
 
 def tp_status_string(status: int) -> str:

@@ -24,9 +24,16 @@ hipError_t gemm_ring(const GemmArgs& p, Layout layout, Epi epi, Elt out, hipStre
 // out[c][r] = in[r][c] for 16-bit elements, in [rows][cols] (cols % 8 == 0).
 hipError_t transpose16(const void* in, void* out, int64_t rows, int64_t cols, hipStream_t stream);
 
-// out[e] = sum_{r=0}^{t-1} parts[r][e] (fp32, rank order); count % 8 == 0.
-hipError_t shard_sum(const void* parts, void* out, int64_t count, int t, Elt in, Elt out_elt,
-                     hipStream_t stream);
+// out[e] = sum_{r=0}^{t-1} parts[r][e] (fp32, rank order), parts[r] at
+// element offset r * stride; count % 8 == 0 and stride % 8 == 0.
+hipError_t shard_sum(const void* parts, void* out, int64_t count, int64_t stride, int t, Elt in,
+                     Elt out_elt, hipStream_t stream);
+
+// y[m][:] = (x[m][:] - mean) / sqrt(var + eps) * gamma + beta over each row
+// (biased variance, fp32 statistics, fixed reduction order); gamma and beta
+// (element type of y) may be null; cols % 8 == 0.
+hipError_t layernorm(const void* x, const void* gamma, const void* beta, void* y, int64_t rows,
+                     int64_t cols, float eps, Elt in, Elt out, hipStream_t stream);
 
 // out[m][r*cols + c] = parts[r][m][c]; cols % 8 == 0.
 hipError_t shard_concat(const void* parts, void* out, int64_t rows, int64_t cols, int t,

@@ -1,0 +1,207 @@
+// Layer normalisation of whole rows, the normalisation a sequence-parallel
+// rank applies to its token shard: one workgroup per row, fp32 statistics
+// (mean, then the biased variance around it), fixed reduction order (so the
+// result is bitwise reproducible), 16-byte vector loads and stores.  Rows of
+// up to kThreads * kMaxOcts * 8 columns are held in registers (one read of
+// HBM); longer rows are read three times, the later passes from L2.
+#include "common.h"
+#include "kernels.h"
+
+namespace tpmlp {
+namespace {
+
+constexpr int kThreads = 512;
+constexpr int kWaves = kThreads / 64;
+constexpr int kMaxOcts = 4;   // register-resident row: up to 16384 columns
+
+struct Oct {
+    float v[8];
+};
+
+__device__ __forceinline__ Oct load8(const float* p)
+{
+    const f32x4 a = *reinterpret_cast<const f32x4*>(p);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+    return Oct{{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]}};
+}
+__device__ __forceinline__ Oct load8(const bf16* p)
+{
+    const bf16x8 a = *reinterpret_cast<const bf16x8*>(p);
+    Oct o;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o.v[e] = (float)a[e];
+    return o;
+}
+__device__ __forceinline__ void store8(float* p, const Oct& o)
+{
+    *reinterpret_cast<f32x4*>(p) = f32x4{o.v[0], o.v[1], o.v[2], o.v[3]};
+    *reinterpret_cast<f32x4*>(p + 4) = f32x4{o.v[4], o.v[5], o.v[6], o.v[7]};
+}
+__device__ __forceinline__ void store8(bf16* p, const Oct& o)
+{
+    bf16x8 a;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) a[e] = (bf16)o.v[e];
+    *reinterpret_cast<bf16x8*>(p) = a;
+}
+
+// Sum over the workgroup: a butterfly inside each wave (every lane ends with
+// the same value, in a fixed order), then the wave totals in wave order.
+__device__ __forceinline__ float block_sum(float v, float* red)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0) red[wave] = v;
+    __syncthreads();
+    float s = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) s += red[w];
+    __syncthreads();   // red is reused by the next reduction
+    return s;
+}
+
+template <typename In, typename Out>
+__global__ __launch_bounds__(kThreads) void layernorm_kernel(const In* __restrict__ x,
+                                                             const Out* __restrict__ gamma,
+                                                             const Out* __restrict__ beta,
+                                                             Out* __restrict__ y, int64_t rows,
+                                                             int64_t cols, float eps)
+{
+    __shared__ float red[kWaves];
+    const int64_t m = blockIdx.x;
+    if (m >= rows) return;
+    const In* xr = x + m * cols;
+    Out* yr = y + m * cols;
+    const int64_t c8 = cols / 8;
+
+    float s = 0.f;
+    for (int64_t c = threadIdx.x; c < c8; c += kThreads) {
+        const Oct o = load8(xr + c * 8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s += o.v[e];
+    }
+    const float mean = block_sum(s, red) / (float)cols;
+
+    float q = 0.f;
+    for (int64_t c = threadIdx.x; c < c8; c += kThreads) {
+        const Oct o = load8(xr + c * 8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float d = o.v[e] - mean;
+            q += d * d;
+        }
+    }
+    const float var = block_sum(q, red) / (float)cols;
+    const float inv = 1.0f / sqrtf(var + eps);
+
+    for (int64_t c = threadIdx.x; c < c8; c += kThreads) {
+        Oct o = load8(xr + c * 8);
+        Oct g, b;
+        if (gamma) g = load8(gamma + c * 8);
+        if (beta) b = load8(beta + c * 8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float v = (o.v[e] - mean) * inv;
+            if (gamma) v *= g.v[e];
+            if (beta) v += b.v[e];
+            o.v[e] = v;
+        }
+        store8(yr + c * 8, o);
+    }
+}
+
+// Register-resident variant: thread i holds octets i, i + kThreads, ...
+template <typename In, typename Out, int NOCT>
+__global__ __launch_bounds__(kThreads) void layernorm_reg_kernel(const In* __restrict__ x,
+                                                                 const Out* __restrict__ gamma,
+                                                                 const Out* __restrict__ beta,
+                                                                 Out* __restrict__ y,
+                                                                 int64_t rows, int64_t cols,
+                                                                 float eps)
+{
+    __shared__ float red[kWaves];
+    const int64_t m = blockIdx.x;
+    if (m >= rows) return;
+    const In* xr = x + m * cols;
+    Out* yr = y + m * cols;
+    const int c8 = (int)(cols / 8);
+    Oct o[NOCT];
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < NOCT; ++j) {
+        const int c = threadIdx.x + j * kThreads;
+        if (c < c8) {
+            o[j] = load8(xr + (int64_t)c * 8);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) s += o[j].v[e];
+        }
+    }
+    const float mean = block_sum(s, red) / (float)cols;
+    float q = 0.f;
+#pragma unroll
+    for (int j = 0; j < NOCT; ++j) {
+        const int c = threadIdx.x + j * kThreads;
+        if (c < c8) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float d = o[j].v[e] - mean;
+                q += d * d;
+            }
+        }
+    }
+    const float var = block_sum(q, red) / (float)cols;
+    const float inv = 1.0f / sqrtf(var + eps);
+#pragma unroll
+    for (int j = 0; j < NOCT; ++j) {
+        const int c = threadIdx.x + j * kThreads;
+        if (c < c8) {
+            Oct g, b;
+            if (gamma) g = load8(gamma + (int64_t)c * 8);
+            if (beta) b = load8(beta + (int64_t)c * 8);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                float v = (o[j].v[e] - mean) * inv;
+                if (gamma) v *= g.v[e];
+                if (beta) v += b.v[e];
+                o[j].v[e] = v;
+            }
+            store8(yr + (int64_t)c * 8, o[j]);
+        }
+    }
+}
+
+template <typename In, typename Out>
+hipError_t launch(const void* x, const void* gamma, const void* beta, void* y, int64_t rows,
+                  int64_t cols, float eps, hipStream_t stream)
+{
+    const dim3 grid((unsigned)rows), block(kThreads);
+    const In* xi = static_cast<const In*>(x);
+    const Out *g = static_cast<const Out*>(gamma), *b = static_cast<const Out*>(beta);
+    Out* yo = static_cast<Out*>(y);
+    const int64_t c8 = cols / 8;
+    if (c8 <= kThreads)
+        hipLaunchKernelGGL((layernorm_reg_kernel<In, Out, 1>), grid, block, 0, stream, xi, g, b, yo, rows, cols, eps);
+    else if (c8 <= 2 * kThreads)
+        hipLaunchKernelGGL((layernorm_reg_kernel<In, Out, 2>), grid, block, 0, stream, xi, g, b, yo, rows, cols, eps);
+    else if (c8 <= kMaxOcts * kThreads)
+        hipLaunchKernelGGL((layernorm_reg_kernel<In, Out, kMaxOcts>), grid, block, 0, stream, xi, g, b, yo, rows, cols, eps);
+    else
+        hipLaunchKernelGGL((layernorm_kernel<In, Out>), grid, block, 0, stream, xi, g, b, yo, rows, cols, eps);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t layernorm(const void* x, const void* gamma, const void* beta, void* y, int64_t rows,
+                     int64_t cols, float eps, Elt in, Elt out, hipStream_t stream)
+{
+    if (rows == 0) return hipSuccess;
+    if (rows > INT32_MAX) return hipErrorInvalidValue;
+    if (in == Elt::F32 && out == Elt::F32) return launch<float, float>(x, gamma, beta, y, rows, cols, eps, stream);
+    if (in == Elt::F32 && out == Elt::BF16) return launch<float, bf16>(x, gamma, beta, y, rows, cols, eps, stream);
+    if (in == Elt::BF16 && out == Elt::F32) return launch<bf16, float>(x, gamma, beta, y, rows, cols, eps, stream);
+    return launch<bf16, bf16>(x, gamma, beta, y, rows, cols, eps, stream);
+}
+
+}  // namespace tpmlp

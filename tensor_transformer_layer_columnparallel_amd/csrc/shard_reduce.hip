@@ -43,21 +43,22 @@ __device__ __forceinline__ void store8(bf16* p, const Oct& o)
     *reinterpret_cast<bf16x8*>(p) = a;
 }
 
-// out[e] = parts[0][e] + ... + parts[t-1][e].  TT > 0: t == TT known at
-// compile time, so all t loads of a vector are issued before the adds.
+// out[e] = parts[0][e] + ... + parts[t-1][e], parts[r] starting `stride`
+// elements after parts[r-1].  TT > 0: t == TT known at compile time, so all t
+// loads of a vector are issued before the adds.
 template <typename In, typename Out, int TT>
 __global__ __launch_bounds__(kThreads) void shard_sum_kernel(const In* __restrict__ parts,
                                                              Out* __restrict__ out,
-                                                             int64_t nvec, int64_t count, int t)
+                                                             int64_t nvec, int64_t stride, int t)
 {
-    const int64_t stride = (int64_t)gridDim.x * kThreads;
-    for (int64_t v = (int64_t)blockIdx.x * kThreads + threadIdx.x; v < nvec; v += stride) {
+    const int64_t step = (int64_t)gridDim.x * kThreads;
+    for (int64_t v = (int64_t)blockIdx.x * kThreads + threadIdx.x; v < nvec; v += step) {
         const int64_t e0 = v * 8;
         Oct s;
         if constexpr (TT > 0) {
             Oct x[TT];
 #pragma unroll
-            for (int r = 0; r < TT; ++r) x[r] = load8(parts + (int64_t)r * count + e0);
+            for (int r = 0; r < TT; ++r) x[r] = load8(parts + (int64_t)r * stride + e0);
             s = x[0];
 #pragma unroll
             for (int r = 1; r < TT; ++r)
@@ -66,7 +67,7 @@ __global__ __launch_bounds__(kThreads) void shard_sum_kernel(const In* __restric
         } else {
             s = load8(parts + e0);
             for (int r = 1; r < t; ++r) {
-                const Oct x = load8(parts + (int64_t)r * count + e0);
+                const Oct x = load8(parts + (int64_t)r * stride + e0);
 #pragma unroll
                 for (int e = 0; e < 8; ++e) s.v[e] += x.v[e];
             }
@@ -207,32 +208,33 @@ unsigned stream_grid(int64_t work_items)
 }
 
 template <typename In, typename Out>
-hipError_t sum_launch(const void* parts, void* out, int64_t count, int t, hipStream_t s)
+hipError_t sum_launch(const void* parts, void* out, int64_t count, int64_t stride, int t,
+                      hipStream_t s)
 {
     const int64_t nvec = count / 8;
     const dim3 grid(stream_grid(nvec)), block(kThreads);
     const In* p = static_cast<const In*>(parts);
     Out* o = static_cast<Out*>(out);
     switch (t) {
-    case 1: hipLaunchKernelGGL((shard_sum_kernel<In, Out, 1>), grid, block, 0, s, p, o, nvec, count, t); break;
-    case 2: hipLaunchKernelGGL((shard_sum_kernel<In, Out, 2>), grid, block, 0, s, p, o, nvec, count, t); break;
-    case 4: hipLaunchKernelGGL((shard_sum_kernel<In, Out, 4>), grid, block, 0, s, p, o, nvec, count, t); break;
-    case 8: hipLaunchKernelGGL((shard_sum_kernel<In, Out, 8>), grid, block, 0, s, p, o, nvec, count, t); break;
-    default: hipLaunchKernelGGL((shard_sum_kernel<In, Out, 0>), grid, block, 0, s, p, o, nvec, count, t); break;
+    case 1: hipLaunchKernelGGL((shard_sum_kernel<In, Out, 1>), grid, block, 0, s, p, o, nvec, stride, t); break;
+    case 2: hipLaunchKernelGGL((shard_sum_kernel<In, Out, 2>), grid, block, 0, s, p, o, nvec, stride, t); break;
+    case 4: hipLaunchKernelGGL((shard_sum_kernel<In, Out, 4>), grid, block, 0, s, p, o, nvec, stride, t); break;
+    case 8: hipLaunchKernelGGL((shard_sum_kernel<In, Out, 8>), grid, block, 0, s, p, o, nvec, stride, t); break;
+    default: hipLaunchKernelGGL((shard_sum_kernel<In, Out, 0>), grid, block, 0, s, p, o, nvec, stride, t); break;
     }
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t shard_sum(const void* parts, void* out, int64_t count, int t, Elt in, Elt out_elt,
-                     hipStream_t stream)
+hipError_t shard_sum(const void* parts, void* out, int64_t count, int64_t stride, int t, Elt in,
+                     Elt out_elt, hipStream_t stream)
 {
     if (count <= 0) return hipSuccess;
-    if (in == Elt::F32 && out_elt == Elt::F32) return sum_launch<float, float>(parts, out, count, t, stream);
-    if (in == Elt::F32 && out_elt == Elt::BF16) return sum_launch<float, bf16>(parts, out, count, t, stream);
-    if (in == Elt::BF16 && out_elt == Elt::F32) return sum_launch<bf16, float>(parts, out, count, t, stream);
-    return sum_launch<bf16, bf16>(parts, out, count, t, stream);
+    if (in == Elt::F32 && out_elt == Elt::F32) return sum_launch<float, float>(parts, out, count, stride, t, stream);
+    if (in == Elt::F32 && out_elt == Elt::BF16) return sum_launch<float, bf16>(parts, out, count, stride, t, stream);
+    if (in == Elt::BF16 && out_elt == Elt::F32) return sum_launch<bf16, float>(parts, out, count, stride, t, stream);
+    return sum_launch<bf16, bf16>(parts, out, count, stride, t, stream);
 }
 
 hipError_t shard_concat(const void* parts, void* out, int64_t rows, int64_t cols, int t,

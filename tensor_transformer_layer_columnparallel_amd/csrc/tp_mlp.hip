@@ -226,18 +226,52 @@ int tp_mlp_shard_bwd(const void* X, const void* W1_i, const void* W2_i, const vo
 int tp_shard_reduce(const void* parts, void* out, int64_t tokens, int64_t cols, int t, int op,
                     int in_dtype, int out_dtype, void* stream)
 {
-    if (op != TP_REDUCE_SUM && op != TP_REDUCE_CONCAT) return TP_ERR_ARG;
+    if (op != TP_REDUCE_SUM && op != TP_REDUCE_CONCAT && op != TP_REDUCE_CONCAT_TOKENS)
+        return TP_ERR_ARG;
     if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return TP_ERR_DTYPE;
-    if (op == TP_REDUCE_CONCAT && in_dtype != out_dtype) return TP_ERR_DTYPE;
+    if (op != TP_REDUCE_SUM && in_dtype != out_dtype) return TP_ERR_DTYPE;
     int st = check_ptrs({parts, out}, {});
     if (st) return st;
     if (t < 1) return TP_ERR_RANK;
     if (tokens < 0 || !feature_dim_ok(cols)) return TP_ERR_SHAPE;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    const int64_t count = tokens * cols;
     if (op == TP_REDUCE_SUM)
-        return status_of(shard_sum(parts, out, tokens * cols, t, to_elt(in_dtype),
+        return status_of(shard_sum(parts, out, count, count, t, to_elt(in_dtype),
+                                   to_elt(out_dtype), s));
+    if (op == TP_REDUCE_CONCAT_TOKENS)   // [t][tokens][cols] is already [t*tokens][cols]
+        return status_of(shard_sum(parts, out, (int64_t)t * count, 0, 1, to_elt(in_dtype),
                                    to_elt(out_dtype), s));
     return status_of(shard_concat(parts, out, tokens, cols, t, to_elt(in_dtype), s));
+}
+
+int tp_shard_reduce_scatter(const void* parts, void* out, int64_t tokens, int64_t cols, int t,
+                            int rank, int in_dtype, int out_dtype, void* stream)
+{
+    if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return TP_ERR_DTYPE;
+    int st = check_ptrs({parts, out}, {});
+    if (st) return st;
+    if (t < 1 || rank < 0 || rank >= t) return TP_ERR_RANK;
+    if (tokens < 0 || !feature_dim_ok(cols)) return TP_ERR_SHAPE;
+    if (tokens % t != 0) return TP_ERR_INDIVISIBLE;
+    const int64_t rows = tokens / t;
+    const char* base = static_cast<const char*>(parts) + rank * rows * cols * elt_size(in_dtype);
+    return status_of(shard_sum(base, out, rows * cols, tokens * cols, t, to_elt(in_dtype),
+                               to_elt(out_dtype), static_cast<hipStream_t>(stream)));
+}
+
+int tp_layernorm(const void* x, const void* gamma, const void* beta, void* y, int64_t tokens,
+                 int64_t cols, float eps, int in_dtype, int out_dtype, void* stream)
+{
+    if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return TP_ERR_DTYPE;
+    int st = check_ptrs({x, y}, {gamma, beta});
+    if (st) return st;
+    if (tokens < 0 || !feature_dim_ok(cols)) return TP_ERR_SHAPE;
+    if (!(eps >= 0.0f) || eps == INFINITY) return TP_ERR_ARG;
+    if (x == y && in_dtype != out_dtype) return TP_ERR_ARG;
+    if (!fits(tokens, cols, 4)) return TP_ERR_SHAPE;
+    return status_of(layernorm(x, gamma, beta, y, tokens, cols, eps, to_elt(in_dtype),
+                               to_elt(out_dtype), static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -22,10 +22,10 @@ def B():
     return binding
 
 
-def test_header_declares_the_five_entry_points_and_status_string():
+def test_header_declares_the_entry_points_and_status_string():
     assert set(_declared_functions()) == {
         "tp_column_linear", "tp_row_linear", "tp_mlp_shard_fwd", "tp_mlp_shard_bwd",
-        "tp_shard_reduce", "tp_status_string"}
+        "tp_shard_reduce", "tp_shard_reduce_scatter", "tp_layernorm", "tp_status_string"}
 
 
 def test_library_exports_every_declared_symbol(B):
@@ -108,10 +108,40 @@ def test_shard_reduce_rejects(B):
     f = lambda **kw: B.tp_shard_reduce(**{**dict(
         parts=P, out=P2, tokens=4, cols=16, t=8, op=B.TP_REDUCE_SUM, in_dtype=B.TP_F32,
         out_dtype=B.TP_F32, stream=0, check=False), **kw})
-    assert f(op=2) == B.TP_ERR_ARG
+    assert f(op=3) == B.TP_ERR_ARG
     assert f(op=B.TP_REDUCE_CONCAT, out_dtype=B.TP_BF16) == B.TP_ERR_DTYPE
+    assert f(op=B.TP_REDUCE_CONCAT_TOKENS, out_dtype=B.TP_BF16) == B.TP_ERR_DTYPE
     assert f(parts=None) == B.TP_ERR_NULL
     assert f(out=MIS) == B.TP_ERR_ALIGN
     assert f(t=0) == B.TP_ERR_RANK
     assert f(cols=12) == B.TP_ERR_SHAPE
     assert f(tokens=-3) == B.TP_ERR_SHAPE
+
+
+def test_reduce_scatter_rejects(B):
+    f = lambda **kw: B.tp_shard_reduce_scatter(**{**dict(
+        parts=P, out=P2, tokens=16, cols=16, t=8, rank=3, in_dtype=B.TP_F32,
+        out_dtype=B.TP_BF16, stream=0, check=False), **kw})
+    assert f(parts=None) == B.TP_ERR_NULL
+    assert f(out=MIS) == B.TP_ERR_ALIGN
+    assert f(rank=8) == B.TP_ERR_RANK
+    assert f(rank=-1) == B.TP_ERR_RANK
+    assert f(t=0) == B.TP_ERR_RANK
+    assert f(tokens=12) == B.TP_ERR_INDIVISIBLE
+    assert f(cols=12) == B.TP_ERR_SHAPE
+    assert f(in_dtype=7) == B.TP_ERR_DTYPE
+
+
+def test_layernorm_rejects(B):
+    f = lambda **kw: B.tp_layernorm(**{**dict(
+        x=P, gamma=None, beta=None, y=P2, tokens=4, cols=16, eps=1e-5, in_dtype=B.TP_F32,
+        out_dtype=B.TP_BF16, stream=0, check=False), **kw})
+    assert f(x=None) == B.TP_ERR_NULL
+    assert f(gamma=MIS) == B.TP_ERR_ALIGN
+    assert f(cols=20) == B.TP_ERR_SHAPE
+    assert f(tokens=-1) == B.TP_ERR_SHAPE
+    assert f(eps=-1.0) == B.TP_ERR_ARG
+    assert f(eps=float("nan")) == B.TP_ERR_ARG
+    assert f(eps=float("inf")) == B.TP_ERR_ARG
+    assert f(y=P) == B.TP_ERR_ARG          # in place needs equal types
+    assert f(out_dtype=5) == B.TP_ERR_DTYPE

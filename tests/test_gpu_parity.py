@@ -443,3 +443,94 @@ def test_ragged_tails_touch_nothing_past_the_operands(B, shape):
     assert_close(outs["Z"], rZ, "bf16", "padded Z")
     for k in ("dY", "dW2", "dW1", "dX", "db1"):
         assert_close(outs[k], rg[k], "bf16", f"padded {k}")
+
+
+# ------------------------------------------- sequence parallelism: RS, LN, AG
+
+@pytest.mark.parametrize("t", [1, 2, 4, 8])
+@pytest.mark.parametrize("out_dt", ["f32", "bf16"])
+def test_reduce_scatter_each_rank(B, t, out_dt):
+    T, cols = 24 * t, 136
+    _log(f"case reduce-scatter t={t} out={out_dt}")
+    g = torch.Generator().manual_seed(20 + t)
+    parts_h = torch.randn(t, T, cols, generator=g)
+    parts = dev(parts_h)
+    odt = torch.float32 if out_dt == "f32" else torch.bfloat16
+    for r in range(t):
+        out = torch.empty(T // t, cols, dtype=odt, device="cuda")
+        B.tp_shard_reduce_scatter(parts, out, T, cols, t, r, B.TP_F32, odt)
+        torch.cuda.synchronize()
+        ref = oracle.reduce_scatter(parts_h, r)
+        if out_dt == "f32":
+            # fp32 adds in rank order: within t roundings of the exact sum
+            bound = t * 2.0**-24 * np.abs(to_np64(parts_h[:, r * (T // t):(r + 1) * (T // t)])).sum(0)
+            assert np.all(np.abs(to_np64(out) - ref) <= bound + 1e-30)
+        else:
+            assert_close(out, ref, "bf16", f"reduce-scatter t={t} r={r}")
+
+
+def test_concat_tokens_is_the_stacked_layout_bitexact(B):
+    t, Tr, cols = 8, 33, 200
+    _log("case concat tokens")
+    g = torch.Generator().manual_seed(31)
+    parts = dev(torch.randn(t, Tr, cols, generator=g).bfloat16())
+    out = torch.empty(t * Tr, cols, dtype=torch.bfloat16, device="cuda")
+    B.tp_shard_reduce(parts, out, Tr, cols, t, B.TP_REDUCE_CONCAT_TOKENS, B.TP_BF16, B.TP_BF16)
+    torch.cuda.synchronize()
+    assert torch.equal(out.cpu(), torch.cat([parts[r].cpu() for r in range(t)], dim=0))
+
+
+@pytest.mark.parametrize("in_dt,out_dt", [("f32", "f32"), ("f32", "bf16"), ("bf16", "bf16"),
+                                          ("bf16", "f32")])
+@pytest.mark.parametrize("T,cols", [(77, 520), (9, 6152), (9, 17008)])
+def test_layernorm_matches_oracle(B, in_dt, out_dt, T, cols):
+    # rows held in registers (520, 6152 columns) and rows read three times (17008)
+    _log(f"case layernorm {in_dt}->{out_dt} {T}x{cols}")
+    g = torch.Generator().manual_seed(41)
+    idt = torch.float32 if in_dt == "f32" else torch.bfloat16
+    odt = torch.float32 if out_dt == "f32" else torch.bfloat16
+    x_h = (3.0 * torch.randn(T, cols, generator=g) + 1.5).to(idt)
+    gam_h = (1.0 + 0.1 * torch.randn(cols, generator=g)).to(odt)
+    bet_h = (0.1 * torch.randn(cols, generator=g)).to(odt)
+    x_h[5 % T] = 2.0                   # a constant row: y = beta exactly
+    y = torch.empty(T, cols, dtype=odt, device="cuda")
+    B.tp_layernorm(dev(x_h), dev(gam_h), dev(bet_h), y, T, cols, 1e-5, idt, odt)
+    y2 = torch.empty_like(y)
+    B.tp_layernorm(dev(x_h), dev(gam_h), dev(bet_h), y2, T, cols, 1e-5, idt, odt)
+    torch.cuda.synchronize()
+    ref = oracle.layernorm(x_h, gam_h, bet_h, 1e-5)
+    if out_dt == "f32":
+        rf = np.linalg.norm(to_np64(y) - ref) / np.linalg.norm(ref)
+        assert rf <= 1e-5, rf
+    else:
+        assert_close(y, ref, "bf16", f"layernorm {in_dt}->{out_dt}")
+    assert torch.equal(y[5 % T].cpu(), bet_h)
+    assert torch.equal(y.cpu(), y2.cpu())          # fixed reduction order
+
+
+def test_sequence_parallel_chain_gpt3_sampled(B):
+    """Row-layer partials of t = 8 ranks at the GPT-3 shape -> ReduceScatter
+    to rank 3's 256 tokens (fp32) -> layer norm -> bf16 -> token AllGather
+    stand-in, against the oracle on sampled rows."""
+    T, h, t, r = 2048, 12288, 8, 3
+    _log("case sequence-parallel chain gpt3")
+    g = torch.Generator().manual_seed(51)
+    parts_h = torch.randn(t, T, h, generator=g)
+    gam_h = (1.0 + 0.1 * torch.randn(h, generator=g)).bfloat16()
+    bet_h = (0.1 * torch.randn(h, generator=g)).bfloat16()
+    parts = dev(parts_h)
+    rs = torch.empty(T // t, h, dtype=torch.float32, device="cuda")
+    B.tp_shard_reduce_scatter(parts, rs, T, h, t, r, B.TP_F32, B.TP_F32)
+    y = torch.empty(T // t, h, dtype=torch.bfloat16, device="cuda")
+    B.tp_layernorm(rs, dev(gam_h), dev(bet_h), y, T // t, h, 1e-5, B.TP_F32, B.TP_BF16)
+    shards = torch.empty(t, T // t, h, dtype=torch.bfloat16, device="cuda")
+    shards[r] = y
+    full = torch.empty(T, h, dtype=torch.bfloat16, device="cuda")
+    B.tp_shard_reduce(shards, full, T // t, h, t, B.TP_REDUCE_CONCAT_TOKENS, B.TP_BF16, B.TP_BF16)
+    torch.cuda.synchronize()
+    rows = sample_indices(T // t, 5, seed=9)
+    # rank r's sampled rows of the sum: rows r*T/t + rows of every partial
+    ref_rs = oracle.shard_sum(parts_h[:, r * (T // t) + torch.as_tensor(rows), :])
+    ref = oracle.layernorm(ref_rs, gam_h, bet_h, 1e-5)
+    assert_close(y[rows], ref, "bf16", "sp chain rows")
+    assert torch.equal(full[r * (T // t):(r + 1) * (T // t)].cpu(), y.cpu())
