@@ -59,11 +59,7 @@ constexpr int kBN = 192;
 constexpr int kSlabBufs = 5;                // ring of 32-k slabs (A M-major, B)
 constexpr int kUnitBufs = 3;                // ring of 64-k units (A K-major)
 constexpr int kLead = 5;                    // DMA steps issued before the first slab
-constexpr int kWaves = 8;
-constexpr int kThreads = 64 * kWaves;
-constexpr int kDmaPerOperand = 2;           // DMA instructions per wave per operand and slab
-constexpr int kDmaPerSlab = 2 * kDmaPerOperand;
-constexpr int kGroups = kDmaPerSlab;        // interleave groups per slab
+constexpr int kGroups = 4;                  // interleave groups per slab
 constexpr int kXcds = 8;
 constexpr int kCUs = 256;
 
@@ -156,19 +152,22 @@ __device__ __forceinline__ int mn_logical(int krow, int phys)
 constexpr uint32_t kInvalid = 0x80000000u;   // per-lane offset past any operand
 
 // DMA plan of a 32-k slab stream: R rows (M or N) x 32 k = R * 4 chunks =
-// R / 16 instructions of 64 chunks; instruction idx = wave * 2 + j fills
-// chunks [idx * 64, idx * 64 + 64).  Instructions past R / 16 (R = 192) are
-// dummies that read nothing into a junk LDS area.  K-major rows advance 64
+// R / 16 instructions of 64 chunks, kPer per wave (NW waves); instruction
+// idx = wave * kPer + j fills chunks [idx * 64, idx * 64 + 64).  Slots past
+// R / 16 (R = 192 with 8 waves) are dummies that read nothing into a junk
+// LDS area.  K-major rows advance 64
 // bytes per slab (K is a multiple of 32); M/N-major slabs advance 32 rows of
 // the operand, and k-rows past K are invalidated.
-template <bool KMAJ, int R>
+template <bool KMAJ, int R, int NW>
 struct SlabPlan {
     static constexpr int kInstr = R / 16;
+    static constexpr int kPer = (kInstr + NW - 1) / NW;   // per wave and slab
+    static constexpr int kJunkBytes = (NW * kPer - kInstr + kPer - 1) / kPer * 1024;
     static constexpr int kBufBytes = R * kBK * 2;
-    uint32_t voff[kDmaPerOperand];
-    uint32_t dst[kDmaPerOperand];   // byte offset inside a buffer (or the junk area)
-    int krow[kDmaPerOperand];
-    bool real[kDmaPerOperand];
+    uint32_t voff[kPer];
+    uint32_t dst[kPer];   // byte offset inside a buffer (or the junk area)
+    int krow[kPer];
+    bool real[kPer];
     uint32_t kstep;
     int nk;
     int64_t K;
@@ -180,8 +179,8 @@ struct SlabPlan {
         nk = (int)((K_ + kBK - 1) / kBK);
         kstep = KMAJ ? (uint32_t)(kBK * 2) : (uint32_t)(kBK * ld * 2);
 #pragma unroll
-        for (int j = 0; j < kDmaPerOperand; ++j) {
-            const int idx = wave * kDmaPerOperand + j;
+        for (int j = 0; j < kPer; ++j) {
+            const int idx = wave * kPer + j;
             real[j] = idx < kInstr;
             const int linear = idx * 64 + lane;
             krow[j] = 0;
@@ -200,7 +199,7 @@ struct SlabPlan {
                               : kInvalid;
             }
             dst[j] = real[j] ? (uint32_t)idx * 1024u
-                             : (uint32_t)(idx - kInstr) / kDmaPerOperand * 1024u;
+                             : (uint32_t)(idx - kInstr) / kPer * 1024u;
         }
     }
     // Instruction j of slab `slab` into its ring buffer.
@@ -222,20 +221,24 @@ struct SlabPlan {
 };
 
 // DMA plan of a K-major 64-k unit stream (A, 256 rows): 256 rows x 128 bytes
-// = 32 instructions of 8 rows; wave w owns instructions 4w .. 4w+3, issued
-// in two parts of two (part p: 4w + 2p + j) on consecutive slabs.  Unit u
+// = 32 instructions of 8 rows; wave w owns kPerUnit = 32 / NW of them,
+// issued in two parts of kPer (part p: w * kPerUnit + p * kPer + j) on
+// consecutive slabs.  Unit u
 // covers k in [64u, 64u + 64); chunks past K are invalidated per lane.
+template <int NW>
 struct UnitPlan {
     static constexpr int kBufBytes = kBM * 64 * 2;
-    uint32_t voff[2 * kDmaPerOperand];
-    int ulim[2 * kDmaPerOperand];   // units u < ulim hold this lane's chunk inside K
+    static constexpr int kPerUnit = 32 / NW;      // instructions per wave and unit
+    static constexpr int kPer = kPerUnit / 2;     // per wave and slab (half a unit)
+    uint32_t voff[kPerUnit];
+    int ulim[kPerUnit];   // units u < ulim hold this lane's chunk inside K
 
     __device__ __forceinline__ void init(int wave, int lane, int64_t r0, int64_t ld,
                                          int64_t extent, int64_t K)
     {
 #pragma unroll
-        for (int q = 0; q < 2 * kDmaPerOperand; ++q) {
-            const int idx = wave * 2 * kDmaPerOperand + q;
+        for (int q = 0; q < kPerUnit; ++q) {
+            const int idx = wave * kPerUnit + q;
             const int row = idx * 8 + (lane >> 3);
             const int chunk = (lane & 7) ^ swz8(row);
             const bool ok = r0 + row < extent;
@@ -247,11 +250,11 @@ struct UnitPlan {
     __device__ __forceinline__ void issue(int part, int j, int wave, i32x4 desc,
                                           uint32_t ring_base, int unit) const
     {
-        const int q = 2 * part + j;
+        const int q = kPer * part + j;
         const uint32_t v = unit < ulim[q] ? voff[q] + (uint32_t)unit * 128u : kInvalid;
         const uint32_t buf = (uint32_t)(unit % kUnitBufs) * kBufBytes;
         const uint32_t lds = __builtin_amdgcn_readfirstlane(
-            (int)(ring_base + buf + (uint32_t)(wave * 2 * kDmaPerOperand + q) * 1024u));
+            (int)(ring_base + buf + (uint32_t)(wave * kPerUnit + q) * 1024u));
         dma16(desc, lds, v, 0u);
     }
 };
@@ -289,22 +292,25 @@ __device__ __forceinline__ bf16x8 read_frag_mn(const bf16* buf, int row0, int la
                   half[1][0], half[1][1], half[1][2], half[1][3]};
 }
 
-template <int WM, bool A_KMAJ, bool B_KMAJ, Epi EPI, typename OutT>
-__global__ __launch_bounds__(kThreads, 1) void gemm_ring_kernel(GemmArgs p, int tiles_m,
-                                                                int tiles_n, int group_m)
+template <int NW, int WM, bool A_KMAJ, bool B_KMAJ, Epi EPI, typename OutT>
+__global__ __launch_bounds__(64 * NW, 1) void gemm_ring_kernel(GemmArgs p, int tiles_m,
+                                                               int tiles_n, int group_m)
 {
     constexpr int BN = kBN;
-    constexpr int kWavesM = WM, kWavesN = kWaves / WM;
+    constexpr int kWavesM = WM, kWavesN = NW / WM;
     constexpr int kWaveM = kBM / kWavesM, kWaveN = BN / kWavesN;
     constexpr int kFragM = kWaveM / 16, kFragN = kWaveN / 16;
-    using PlanA = SlabPlan<false, kBM>;   // used when A is M-contiguous
-    using PlanB = SlabPlan<B_KMAJ, BN>;
-    constexpr int kABytes = A_KMAJ ? kUnitBufs * UnitPlan::kBufBytes : kSlabBufs * PlanA::kBufBytes;
+    using PlanU = UnitPlan<NW>;              // used when A is K-contiguous
+    using PlanA = SlabPlan<false, kBM, NW>;  // used when A is M-contiguous
+    using PlanB = SlabPlan<B_KMAJ, BN, NW>;
+    constexpr int kABytes = A_KMAJ ? kUnitBufs * PlanU::kBufBytes : kSlabBufs * PlanA::kBufBytes;
     constexpr int kBBytes = kSlabBufs * PlanB::kBufBytes;
-    constexpr int kJunkWaves = kWaves - PlanB::kInstr / kDmaPerOperand;
+    constexpr int kPerA = A_KMAJ ? PlanU::kPer : PlanA::kPer;   // DMA per wave and slab
+    constexpr int kPerB = PlanB::kPer;
+    constexpr int kDmaStep = kPerA + kPerB;
     __shared__ __attribute__((aligned(1024))) bf16 sa[kABytes / 2];
     __shared__ __attribute__((aligned(1024))) bf16 sb[kBBytes / 2];
-    __shared__ __attribute__((aligned(1024))) bf16 junk[(kJunkWaves > 0 ? kJunkWaves : 1) * 512];
+    __shared__ __attribute__((aligned(1024))) bf16 junk[(PlanB::kJunkBytes > 0 ? PlanB::kJunkBytes : 1024) / 2];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -326,7 +332,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_ring_kernel(GemmArgs p, int 
 
     const i32x4 da = make_desc(p.A, (uint32_t)(p.M * p.K * 2));
     const i32x4 db = make_desc(p.B, (uint32_t)(p.N * p.K * 2));
-    UnitPlan pu;   // A K-major
+    PlanU pu;      // A K-major
     PlanA ps;      // A M-major
     if constexpr (A_KMAJ) pu.init(wave, lane, m0, p.K, p.M, p.K);
     else ps.init(wave, lane, m0, p.M, p.M, p.K);
@@ -342,29 +348,30 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_ring_kernel(GemmArgs p, int 
         for (int b = 0; b < kFragN; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
     bf16x8 fa[2][kFragM], fb[2][kFragN];
 
-    // DMA instruction g (0, 1: A; 2, 3: B) of step vs (negative in the
+    // DMA instruction d (A below kPerA, then B) of step vs (negative in the
     // prologue).  B and an M-major A refill slab vs + 5 (the buffer of slab
     // vs, read for the last time during step vs - 1); a K-major A refills
     // part (vs + 1) mod 2 of unit floor((vs + 1) / 2) + 2 (the buffer of the
     // unit holding slabs vs - 1 and vs, or vs - 2 and vs - 1).
-    auto dma_op = [&](int g, int vs) {
-        if (g < kDmaPerOperand) {
-            if constexpr (A_KMAJ) pu.issue((vs + 1) & 1, g, wave, da, a_base, ((vs + 1) >> 1) + kUnitBufs - 1);
-            else ps.issue(g, da, a_base, junk_base, vs + kSlabBufs);
+    auto dma_op = [&](int d, int vs) {
+        if (d < kPerA) {
+            if constexpr (A_KMAJ) pu.issue((vs + 1) & 1, d, wave, da, a_base, ((vs + 1) >> 1) + kUnitBufs - 1);
+            else ps.issue(d, da, a_base, junk_base, vs + kSlabBufs);
         } else {
-            pb.issue(g - kDmaPerOperand, db, b_base, junk_base, vs + kSlabBufs);
+            pb.issue(d - kPerA, db, b_base, junk_base, vs + kSlabBufs);
         }
     };
-    // The work of one slab is cut into kGroups groups, each holding one DMA
-    // instruction, the MFMAs of the A fragments a with a % kGroups == g and a
-    // share of the fragment reads, so that the waves never stall on a burst
-    // of memory instructions while the matrix pipe idles.
+    // The work of one slab is cut into kGroups groups, each holding the DMA
+    // instructions d with d % kGroups == g, the MFMAs of the A fragments a
+    // with a % kGroups == g and a share of the fragment reads, so that the
+    // waves never stall on a burst of memory instructions while the matrix
+    // pipe idles.
     static_assert(kFragM % kGroups == 0, "whole A fragments per group");
     auto read_group = [&](int g, int slab, int buf) {
 #pragma unroll
         for (int a = g; a < kFragM; a += kGroups) {
             if constexpr (A_KMAJ)
-                fa[buf][a] = read_frag_k8(sa + ((slab >> 1) % kUnitBufs) * (UnitPlan::kBufBytes / 2),
+                fa[buf][a] = read_frag_k8(sa + ((slab >> 1) % kUnitBufs) * (PlanU::kBufBytes / 2),
                                           wrow_a + a * 16, slab & 1, lane);
             else
                 fa[buf][a] = read_frag_mn<kBM>(sa + (slab % kSlabBufs) * (PlanA::kBufBytes / 2),
@@ -393,13 +400,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_ring_kernel(GemmArgs p, int 
     // starting at an even slab kt+1, issued at step kt-3: for odd kt only two
     // steps of loads may stay outstanding, otherwise three.
     auto slab_step = [&](auto odd, int kt, int cbuf, int nbuf) {
-        if constexpr (A_KMAJ && decltype(odd)::value) wait_vmcnt<kDmaPerSlab * 2>();
-        else wait_vmcnt<kDmaPerSlab * 3>();
+        if constexpr (A_KMAJ && decltype(odd)::value) wait_vmcnt<kDmaStep * 2>();
+        else wait_vmcnt<kDmaStep * 3>();
         wait_lgkmcnt0();
         barrier();
 #pragma unroll
         for (int g = 0; g < kGroups; ++g) {
-            dma_op(g, kt);
+#pragma unroll
+            for (int d = g; d < kDmaStep; d += kGroups) dma_op(d, kt);
             read_group(g, kt + 1, nbuf);
             mfma_group(g, cbuf);
             __builtin_amdgcn_sched_barrier(0);
@@ -413,9 +421,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_ring_kernel(GemmArgs p, int 
 #pragma unroll
         for (int vs = -kLead; vs < 0; ++vs)
 #pragma unroll
-            for (int g = 0; g < kGroups; ++g) dma_op(g, vs);
+            for (int d = 0; d < kDmaStep; ++d) dma_op(d, vs);
         // Slab 0 came with the first two prologue steps.
-        wait_vmcnt<kDmaPerSlab * (kLead - 2)>();
+        wait_vmcnt<kDmaStep * (kLead - 2)>();
         barrier();
 #pragma unroll
         for (int g = 0; g < kGroups; ++g) read_group(g, 0, 0);
@@ -481,20 +489,33 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_ring_kernel(GemmArgs p, int 
     }
 }
 
+#ifndef TPMLP_RING_NW_NN
+#define TPMLP_RING_NW_NN 8
+#endif
 #ifndef TPMLP_RING_WM_NN
 #define TPMLP_RING_WM_NN 2
 #endif
+#ifndef TPMLP_RING_NW_NT
+#define TPMLP_RING_NW_NT 8
+#endif
 #ifndef TPMLP_RING_WM_NT
 #define TPMLP_RING_WM_NT 4
+#endif
+#ifndef TPMLP_RING_NW_TN
+#define TPMLP_RING_NW_TN 8
 #endif
 #ifndef TPMLP_RING_WM_TN
 #define TPMLP_RING_WM_TN 4
 #endif
 
-// WM waves along M (and 8 / WM along N).
+// NW waves per workgroup, WM of them along M (and NW / WM along N).  Four
+// waves (one per SIMD, 256 x 48 or 128 x 96 outputs each) read less LDS per
+// flop but measured about 35% slower than eight: with one wave per SIMD
+// nothing covers a wave's own waits.
 template <bool AK, bool BK, Epi E, typename O>
 hipError_t launch(const GemmArgs& p, hipStream_t stream)
 {
+    constexpr int NW = AK ? (BK ? TPMLP_RING_NW_NT : TPMLP_RING_NW_NN) : TPMLP_RING_NW_TN;
     constexpr int WM = AK ? (BK ? TPMLP_RING_WM_NT : TPMLP_RING_WM_NN) : TPMLP_RING_WM_TN;
     const int tm = (int)((p.M + kBM - 1) / kBM);
     const int tn = (int)((p.N + kBN - 1) / kBN);
@@ -503,8 +524,8 @@ hipError_t launch(const GemmArgs& p, hipStream_t stream)
     // device; one- and two-wave products keep the plain order, which measured
     // as fast or faster for them.
     const int group_m = tm * tn > 2 * kCUs ? 4 : 0;
-    hipLaunchKernelGGL((gemm_ring_kernel<WM, AK, BK, E, O>), dim3((unsigned)(tm * tn)),
-                       dim3(kThreads), 0, stream, p, tm, tn, group_m);
+    hipLaunchKernelGGL((gemm_ring_kernel<NW, WM, AK, BK, E, O>), dim3((unsigned)(tm * tn)),
+                       dim3(64 * NW), 0, stream, p, tm, tn, group_m);
     return hipGetLastError();
 }
 
