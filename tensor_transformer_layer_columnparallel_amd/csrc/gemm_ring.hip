@@ -308,8 +308,9 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_ring_kernel(GemmArgs p, int t
     constexpr int kPerA = A_KMAJ ? PlanU::kPer : PlanA::kPer;   // DMA per wave and slab
     constexpr int kPerB = PlanB::kPer;
     constexpr int kDmaStep = kPerA + kPerB;
-    __shared__ __attribute__((aligned(1024))) bf16 sa[kABytes / 2];
-    __shared__ __attribute__((aligned(1024))) bf16 sb[kBBytes / 2];
+    __shared__ __attribute__((aligned(1024))) bf16 smem[(kABytes + kBBytes) / 2];
+    bf16* const sa = smem;                  // A ring
+    bf16* const sb = smem + kABytes / 2;    // B ring
     __shared__ __attribute__((aligned(1024))) bf16 junk[(PlanB::kJunkBytes > 0 ? PlanB::kJunkBytes : 1024) / 2];
 
     const int lane = threadIdx.x & 63;
@@ -441,8 +442,59 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_ring_kernel(GemmArgs p, int t
     // of every 16 x 16 fragment.
     const bf16* bias = static_cast<const bf16*>(p.bias);
     const bf16* aux = static_cast<const bf16*>(p.aux);
-    bf16* save = static_cast<bf16*>(p.save);
     OutT* C = static_cast<OutT*>(p.C);
+    if constexpr (sizeof(OutT) == 4 && (EPI == Epi::Store || EPI == Epi::Bias)) {
+        // Plain fp32 results (the row-layer partials and the backward's
+        // gradients) go through LDS (the ring is free now) so that the stores
+        // to HBM are whole 16-byte chunks of consecutive columns, one row
+        // segment per group of lanes, instead of 16 rows x 64 bytes per store
+        // instruction: 3-4% faster on those products.  (For the bf16 outputs
+        // the extra LDS passes cost more than they saved.)
+        constexpr int kRowBytes = BN * 4;
+        constexpr int kPitch = kRowBytes + 16;   // rows 16 bytes apart in bank space
+        constexpr int kRows = kBM * kPitch <= kABytes + kBBytes ? kBM : kBM / 2;
+        static_assert(kRows * kPitch <= kABytes + kBBytes, "staging exceeds the ring");
+        constexpr int kChunks = kRows * (kRowBytes / 16);
+        char* stage = reinterpret_cast<char*>(smem);
+        barrier();   // every wave's loads have landed and no wave reads the ring
+#pragma unroll
+        for (int b = 0; b < kFragN; ++b) {
+            const int64_t gcol = n0 + wrow_b + b * 16 + 4 * (lane >> 4);
+            if constexpr (EPI == Epi::Bias) {
+                if (bias && gcol < p.N) {
+                    const bf16x4 t4 = *reinterpret_cast<const bf16x4*>(bias + gcol);
+#pragma unroll
+                    for (int a = 0; a < kFragM; ++a)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) acc[a][b][e] += (float)t4[e];
+                }
+            }
+        }
+#pragma unroll
+        for (int r0 = 0; r0 < kBM; r0 += kRows) {
+#pragma unroll
+            for (int a = 0; a < kFragM; ++a) {
+                const int row = wrow_a + a * 16 + (lane & 15) - r0;
+                if (row < 0 || row >= kRows) continue;   // uniform per (wave, a)
+#pragma unroll
+                for (int b = 0; b < kFragN; ++b) {
+                    const int col = wrow_b + b * 16 + 4 * (lane >> 4);
+                    *reinterpret_cast<f32x4*>(stage + row * kPitch + col * 4) = acc[a][b];
+                }
+            }
+            barrier();
+            for (int c = threadIdx.x; c < kChunks; c += 64 * NW) {
+                const int row = c / (kRowBytes / 16), ch = c % (kRowBytes / 16);
+                const int64_t grow = m0 + r0 + row, gcol = n0 + (int64_t)ch * 4;
+                if (grow < p.M && gcol < p.N)
+                    *reinterpret_cast<i32x4*>(C + grow * p.N + gcol) =
+                        *reinterpret_cast<const i32x4*>(stage + row * kPitch + ch * 16);
+            }
+            barrier();
+        }
+        return;
+    }
+    bf16* save = static_cast<bf16*>(p.save);
 #pragma unroll
     for (int b = 0; b < kFragN; ++b) {
         const int64_t col = n0 + wrow_b + b * 16 + 4 * (lane >> 4);

@@ -113,6 +113,24 @@ def test_column_linear_ragged(B, act, out_dt):
     assert_close(Y, ref, "bf16", f"column ragged act={act}")
 
 
+@pytest.mark.parametrize("act", [0, 1])
+@pytest.mark.parametrize("out_dt", ["bf16", "f32"])
+def test_column_linear_tile_kernel_epilogues(B, act, out_dt):
+    # Shapes the tile kernel takes (M >= 256, N >= 192, K % 32 == 0) with a
+    # ragged M and N tail: the bias and bias + GeLU epilogues into bf16 and
+    # into fp32 (the fp32 plain/bias results are staged through LDS).
+    w = configs.scaled(configs.GPT3_SHARD, "col_tile", T=300, h=512, ffn=1600, t=4)
+    _log(f"case column tile act={act} out={out_dt}")
+    d_h = synth.make_inputs(w, with_dz=False)
+    X, W, b = dev(d_h["X"]), dev(d_h["W1"][0]), dev(d_h["b1"][0])
+    odt = torch.bfloat16 if out_dt == "bf16" else torch.float32
+    Y = torch.empty(w.T, w.n, dtype=odt, device="cuda")
+    B.tp_column_linear(X, W, b, Y, None, w.T, w.h, w.ffn, w.t, 0, B.TP_BF16, odt, act)
+    torch.cuda.synchronize()
+    ref = oracle.column_linear(d_h["X"], d_h["W1"][0], d_h["b1"][0], gelu=bool(act))
+    assert_close(Y, ref, "bf16", f"column tile act={act} out={out_dt}")
+
+
 def test_row_linear_ragged_partials_sum(B):
     # row-parallel partials of t = 4 ranks, summed on the device
     T, n_full, hout, t = 77, 512, 136, 4
