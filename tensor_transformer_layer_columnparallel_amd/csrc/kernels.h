@@ -16,8 +16,9 @@ enum class Layout { NN = 0, NT = 1, TN = 2 };
 hipError_t gemm_simple(const GemmArgs& p, Elt elt, Layout layout, Epi epi, Elt out,
                        hipStream_t stream);
 
-// 256 x 192-tile bf16 kernel: LDS-DMA into a ring of 4 stages of 32-deep
-// slabs, transposed LDS reads for M/N-contiguous operands, XCD-aware order.
+// 256 x 192-tile bf16 kernel: LDS-DMA into rings of 64-deep units (a
+// K-contiguous A) and 32-deep slabs (the other operands), transposed LDS
+// reads for M/N-contiguous operands, XCD-aware tile order.
 bool gemm_ring_supported(const GemmArgs& p, Layout layout);
 hipError_t gemm_ring(const GemmArgs& p, Layout layout, Epi epi, Elt out, hipStream_t stream);
 
