@@ -1,7 +1,7 @@
 // Large-shape bf16 MFMA GEMM for gfx950: C[M,N] = epi( op(A)[M,K] * op(B)[K,N] ).
 //
-// Tiles of 256 x 192 outputs, one workgroup of 8 waves (two per SIMD), each
-// wave owning 256/WM x 192/(8/WM) outputs, v_mfma_f32_16x16x32_bf16 with fp32
+// Tiles of 256 x 192 outputs, one workgroup of NW = 8 waves (two per SIMD),
+// each wave owning 256/WM x 192/(NW/WM) outputs, v_mfma_f32_16x16x32_bf16 with fp32
 // accumulators and the B fragment in the first MFMA slot, so that each lane
 // ends with four consecutive columns of one row.  Tiles are numbered so that
 // consecutive workgroups (which the dispatcher spreads round-robin over the
@@ -19,13 +19,14 @@
 // LDS read.  The waits are explicit instead.  Compute walks K in 32-k slabs;
 // at slab k every wave
 //   1. waits until its loads of slab k+1 have landed (the vector memory
-//      counter retires loads in issue order; every wave issues the same four
-//      DMA instructions per slab, so the counts are static) and until its own
-//      LDS reads of slab k have returned;
+//      counter retires loads in issue order; every wave issues the same
+//      number of DMA instructions per slab, so the counts are static) and
+//      until its own LDS reads of slab k have returned;
 //   2. passes a barrier: slab k+1 is in LDS for everybody and nobody reads
 //      slab k's buffers any more;
-//   3. in four groups, each with one DMA instruction, the MFMAs of a quarter
-//      of the A fragments and a share of the fragment reads: refills the
+//   3. in four groups, each with a share of the DMA instructions, the MFMAs
+//      of a quarter of the A fragments and a share of the fragment reads:
+//      refills the
 //      freed buffers (5 slabs ahead, or half of the 64-k unit 2-3 slabs
 //      ahead), multiplies slab k (fragments read during slab k-1) and reads
 //      the fragments of slab k+1.
@@ -34,6 +35,9 @@
 // Loads of elements outside the operands (ragged M/N tails, k past K) use a
 // per-lane offset of 2^31, beyond any operand, which the buffer descriptor
 // turns into zeros without touching memory.
+// Plain fp32 results are staged through the (then free) LDS ring so that the
+// stores to HBM cover whole row segments; other results are stored from the
+// registers, four consecutive columns per lane.
 //
 // LDS layouts (16-byte chunks permuted per row for conflict-free reads):
 //   K-major 64-k unit [256][64 k]: chunk c of row r at c ^ swz8(r);

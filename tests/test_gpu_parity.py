@@ -211,6 +211,26 @@ def test_attention_gpt3_shard_sampled(B):
                  f"{aw.name} out-proj rows")
 
 
+def test_row_partials_in_bf16_then_summed_in_fp32(B):
+    # Low-precision exchange (page "Tensor Parallelism原理与实践" §4.1 keeps fp32
+    # for the reduction itself): each rank's row-parallel partial stored as
+    # bf16, the t partials summed in fp32 in rank order.
+    T, n_full, hout, t = 300, 1024, 392, 4
+    _log("case row partials bf16 -> fp32 sum")
+    g = torch.Generator().manual_seed(12)
+    Xf = torch.randn(T, n_full, generator=g).bfloat16()
+    Wf = (0.02 * torch.randn(n_full, hout, generator=g)).bfloat16()
+    k = n_full // t
+    parts = torch.empty(t, T, hout, dtype=torch.bfloat16, device="cuda")
+    for r in range(t):
+        B.tp_row_linear(dev(Xf[:, r * k:(r + 1) * k]), dev(Wf[r * k:(r + 1) * k]), parts[r], T,
+                        n_full, hout, t, r, B.TP_BF16, B.TP_BF16)
+    Z = torch.empty(T, hout, dtype=torch.float32, device="cuda")
+    B.tp_shard_reduce(parts, Z, T, hout, t, B.TP_REDUCE_SUM, B.TP_BF16, B.TP_F32)
+    torch.cuda.synchronize()
+    assert_close(Z, oracle.row_linear(Xf, Wf), "bf16", "bf16 partials summed")
+
+
 # ------------------------------------------------- reduced MLP, full compare
 
 REDUCED = [
