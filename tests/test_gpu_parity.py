@@ -323,6 +323,25 @@ def test_deterministic_rerun(B):
         assert torch.equal(a, b)
 
 
+def test_side_stream_matches_default_stream(B):
+    # Calls only enqueue on the stream they are given: a forward + backward on
+    # a separate stream gives the same bytes as on the default stream.
+    w = configs.scaled(configs.GPT3_SHARD, "stream", T=260, h=512, ffn=2048, t=4)
+    _log("case side stream")
+    d = to_device(synth.make_inputs(w))
+    Y0, H0, Z0 = gpu_shard_fwd(B, w, d, 0)
+    g0 = gpu_shard_bwd(B, w, d, 0, Y0, H0)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        Y1, H1, Z1 = gpu_shard_fwd(B, w, d, 0, stream=side.cuda_stream)
+        g1 = gpu_shard_bwd(B, w, d, 0, Y1, H1, stream=side.cuda_stream)
+    side.synchronize()
+    for a, b in zip([Y0, H0, Z0] + [g0[k] for k in ("dY", "dW2", "dW1", "dX", "db1")],
+                    [Y1, H1, Z1] + [g1[k] for k in ("dY", "dW2", "dW1", "dX", "db1")]):
+        assert torch.equal(a, b)
+
+
 def test_all_ones_and_identity(B):
     _log("case all-ones / identity")
     T, h, n = 64, 768, 256
