@@ -439,29 +439,41 @@ def main():
     if not args.no_reduce:
         wr = configs.FULL_LAYER_8
         count = wr.T * wr.h
-        parts = torch.randn(wr.t, wr.T, wr.h, device=dev)
         Zs = torch.empty(wr.T, wr.h, device=dev)
-        for _ in range(2):
-            B.tp_shard_reduce(parts, Zs, wr.T, wr.h, wr.t, B.TP_REDUCE_SUM, torch.float32,
-                              torch.float32, stream=sptr)
-        reps = 10
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for _ in range(reps):
-            B.tp_shard_reduce(parts, Zs, wr.T, wr.h, wr.t, B.TP_REDUCE_SUM, torch.float32,
-                              torch.float32, stream=sptr)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / reps
-        nbytes = (wr.t + 1) * count * 4
-        gbs = nbytes / (ms * 1e-3) / 1e9
+
+        def time_sum(parts):
+            def call():
+                B.tp_shard_reduce(parts, Zs, wr.T, wr.h, wr.t, B.TP_REDUCE_SUM, parts.dtype,
+                                  torch.float32, stream=sptr)
+            for _ in range(2):
+                call()
+            reps = 10
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(reps):
+                call()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / reps
+            nbytes = wr.t * count * parts.element_size() + count * 4
+            return ms, nbytes, nbytes / (ms * 1e-3) / 1e9
+
+        parts = torch.randn(wr.t, wr.T, wr.h, device=dev)
+        ms, nbytes, gbs = time_sum(parts)
+        # The same exchange with bf16 partials (half the bytes on the wire),
+        # summed in fp32.
+        ms16, nbytes16, gbs16 = time_sum(parts.to(torch.bfloat16))
         out["shard_reduce"] = {"workload": "sum of 8 fp32 partials [4096, 8192]",
                                "ms": round(ms, 4), "achieved": round(gbs, 1),
                                "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                "frac": round(gbs / PEAK_HBM_GBS, 4),
-                               "bytes_per_launch": nbytes}
-        log(f"shard reduce: {ms:.4f} ms, {gbs:.0f} GB/s")
+                               "bytes_per_launch": nbytes,
+                               "bf16_partials": {"ms": round(ms16, 4), "achieved": round(gbs16, 1),
+                                                 "frac": round(gbs16 / PEAK_HBM_GBS, 4),
+                                                 "bytes_per_launch": nbytes16}}
+        log(f"shard reduce: {ms:.4f} ms, {gbs:.0f} GB/s; bf16 partials {ms16:.4f} ms, "
+            f"{gbs16:.0f} GB/s")
         del parts, Zs
 
     if args.cpu_seconds > 0:

@@ -50,6 +50,9 @@ struct GemmArgs {
     const void* aux;    // DGelu: pre-activation [M][N]; BiasGelu: unused
     void* save;         // BiasGelu: pre-activation output [M][N]; may be null
     int64_t M, N, K;
+    // DGelu, tile kernel only: column sums of C over each 256-row block of
+    // tiles, fp32 [ceil(M / 256)][N], summed in a fixed order; may be null.
+    float* colsum;
 };
 
 }  // namespace tpmlp

@@ -301,6 +301,8 @@ __device__ __forceinline__ bf16x8 read_frag_mn(const bf16* buf, int row0, int la
                   half[1][0], half[1][1], half[1][2], half[1][3]};
 }
 
+static_assert(kBM == kGemmRingTileRows, "row blocks of GemmArgs::colsum");
+
 template <int NW, int WM, bool A_KMAJ, bool B_KMAJ, Epi EPI, typename OutT>
 __global__ __launch_bounds__(64 * NW, 1) void gemm_ring_kernel(GemmArgs p, int tiles_m,
                                                                int tiles_n, int group_m)
@@ -491,6 +493,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_ring_kernel(GemmArgs p, int t
                     *reinterpret_cast<f32x4*>(stage + row * kPitch + col * 4) = acc[a][b];
                 }
             }
+            wait_lgkmcnt0();   // s_barrier itself does not wait for LDS stores
             barrier();
             for (int c = threadIdx.x; c < kChunks; c += 64 * NW) {
                 const int row = c / (kRowBytes / 16), ch = c % (kRowBytes / 16);
@@ -504,6 +507,11 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_ring_kernel(GemmArgs p, int t
         return;
     }
     bf16* save = static_cast<bf16*>(p.save);
+    float cs[kFragN][4];   // DGelu: this lane's share of the tile's column sums
+#pragma unroll
+    for (int b = 0; b < kFragN; ++b)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) cs[b][e] = 0.f;
 #pragma unroll
     for (int b = 0; b < kFragN; ++b) {
         const int64_t col = n0 + wrow_b + b * 16 + 4 * (lane >> 4);
@@ -538,13 +546,47 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_ring_kernel(GemmArgs p, int t
             } else if constexpr (EPI == Epi::DGelu) {
                 const bf16x4 y4 = *reinterpret_cast<const bf16x4*>(aux + off);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] *= gelu_tanh_grad((float)y4[e]);
+                for (int e = 0; e < 4; ++e) {
+                    v[e] *= gelu_tanh_grad((float)y4[e]);
+                    cs[b][e] += v[e];
+                }
             }
             if constexpr (sizeof(OutT) == 4) {
                 *reinterpret_cast<f32x4*>(C + off) = f32x4{v[0], v[1], v[2], v[3]};
             } else {
                 *reinterpret_cast<bf16x4*>(C + off) =
                     bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+            }
+        }
+    }
+    if constexpr (EPI == Epi::DGelu) {
+        if (p.colsum) {
+            // Column sums of the tile's fp32 results (the bias gradient's
+            // partials), in a fixed order: each lane's rows, then the 16
+            // lanes that share a column (a butterfly; every lane ends with
+            // the same value), then the wave rows in order.  Rows past M
+            // were skipped above.
+            float* red = reinterpret_cast<float*>(smem);   // [kWavesM][BN]
+            barrier();   // no wave still reads the ring
+#pragma unroll
+            for (int b = 0; b < kFragN; ++b) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    float v = cs[b][e];
+#pragma unroll
+                    for (int off = 1; off < 16; off <<= 1) v += __shfl_xor(v, off, 64);
+                    if ((lane & 15) == 0)
+                        red[wm * BN + wrow_b + b * 16 + 4 * (lane >> 4) + e] = v;
+                }
+            }
+            wait_lgkmcnt0();
+            barrier();
+            const int c = threadIdx.x;
+            if (c < BN && n0 + c < p.N) {
+                float v = 0.f;
+#pragma unroll
+                for (int w = 0; w < kWavesM; ++w) v += red[w * BN + c];
+                p.colsum[(int64_t)tm * p.N + n0 + c] = v;
             }
         }
     }

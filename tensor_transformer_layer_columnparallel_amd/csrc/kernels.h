@@ -21,6 +21,8 @@ hipError_t gemm_simple(const GemmArgs& p, Elt elt, Layout layout, Epi epi, Elt o
 // reads for M/N-contiguous operands, XCD-aware tile order.
 bool gemm_ring_supported(const GemmArgs& p, Layout layout);
 hipError_t gemm_ring(const GemmArgs& p, Layout layout, Epi epi, Elt out, hipStream_t stream);
+// Rows of C per tile of the tile kernel (the row blocks of GemmArgs::colsum).
+constexpr int64_t kGemmRingTileRows = 256;
 
 // out[c][r] = in[r][c] for 16-bit elements, in [rows][cols] (cols % 8 == 0).
 hipError_t transpose16(const void* in, void* out, int64_t rows, int64_t cols, hipStream_t stream);
@@ -45,5 +47,10 @@ hipError_t shard_concat(const void* parts, void* out, int64_t rows, int64_t cols
 // of 64 first (more parallel), otherwise one pass per column block.
 hipError_t column_sum(const void* in, float* out, int64_t rows, int64_t cols, Elt elt,
                       void* scratch, int64_t scratch_bytes, hipStream_t stream);
+
+// out[j] = sum_r part[r][j] for r = 0 .. nparts - 1 in order: the last step of
+// a column sum whose row-block partials another kernel wrote.
+hipError_t column_finish(const float* part, float* out, int64_t nparts, int64_t cols,
+                         hipStream_t stream);
 
 }  // namespace tpmlp

@@ -280,4 +280,13 @@ hipError_t column_sum(const void* in, float* out, int64_t rows, int64_t cols, El
     return hipGetLastError();
 }
 
+hipError_t column_finish(const float* part, float* out, int64_t nparts, int64_t cols,
+                         hipStream_t stream)
+{
+    if (cols <= 0) return hipSuccess;
+    hipLaunchKernelGGL(column_final_kernel, dim3((unsigned)((cols + kThreads - 1) / kThreads)),
+                       dim3(kThreads), 0, stream, part, out, nparts, cols);
+    return hipGetLastError();
+}
+
 }  // namespace tpmlp

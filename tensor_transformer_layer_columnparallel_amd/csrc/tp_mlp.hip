@@ -71,14 +71,22 @@ bool use_transposed_operands(int64_t tokens, int64_t h, int64_t n, Elt e)
     return gemm_ring_supported(a, Layout::NN) && gemm_ring_supported(b, Layout::NN);
 }
 
+// True when a product of this shape runs on the tile kernel.
+bool ring_path(int64_t M, int64_t N, int64_t K, Elt elt, Layout layout)
+{
+    GemmArgs p{};
+    p.M = M; p.N = N; p.K = K;
+    return elt == Elt::BF16 && M > 0 && N > 0 && gemm_ring_supported(p, layout);
+}
+
+// colsum (DGelu on the tile kernel only): per-256-row-block column sums of C.
 hipError_t run_gemm(const void* A, const void* B, void* C, const void* bias, const void* aux,
                     void* save, int64_t M, int64_t N, int64_t K, Elt elt, Layout layout, Epi epi,
-                    Elt out, hipStream_t stream)
+                    Elt out, hipStream_t stream, float* colsum = nullptr)
 {
     if (M == 0 || N == 0) return hipSuccess;
-    GemmArgs p{A, B, C, bias, aux, save, M, N, K};
-    if (elt == Elt::BF16 && gemm_ring_supported(p, layout))
-        return gemm_ring(p, layout, epi, out, stream);
+    GemmArgs p{A, B, C, bias, aux, save, M, N, K, colsum};
+    if (ring_path(M, N, K, elt, layout)) return gemm_ring(p, layout, epi, out, stream);
     return gemm_simple(p, elt, layout, epi, out, stream);
 }
 
@@ -187,14 +195,25 @@ int tp_mlp_shard_bwd(const void* X, const void* W1_i, const void* W2_i, const vo
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t err;
     // dY_i = (dZ W2_i^T) * g'(Y_i): W2_i [n][h] is the K-contiguous [N][K] operand.
+    // db1_i = column sums of dY_i.  On the tile kernel the product's epilogue
+    // sums each 256-row block of its fp32 results and one pass adds the
+    // blocks in order; otherwise a column-sum pass reads dY_i back.  Either
+    // way dW2_i (written only afterwards) holds the partial sums.
+    const int64_t row_blocks = (tokens + kGemmRingTileRows - 1) / kGemmRingTileRows;
+    float* colsum = nullptr;
+    if (db1_i && ring_path(tokens, n, h, e, Layout::NT) && row_blocks <= h)
+        colsum = static_cast<float*>(dW2_i);
     if ((err = run_gemm(dZ, W2_i, dY_i, nullptr, Y_i, nullptr, tokens, n, h, e, Layout::NT,
-                        Epi::DGelu, e, s)) != hipSuccess)
+                        Epi::DGelu, e, s, colsum)) != hipSuccess)
         return TP_ERR_HIP;
-    // db1_i = column sums of dY_i, with dW2_i (written only afterwards) as
-    // scratch for the partial sums.
-    if (db1_i && (err = column_sum(dY_i, static_cast<float*>(db1_i), tokens, n, e, dW2_i,
-                                   n * h * 4, s)) != hipSuccess)
+    if (colsum) {
+        if ((err = column_finish(colsum, static_cast<float*>(db1_i), row_blocks, n, s)) !=
+            hipSuccess)
+            return TP_ERR_HIP;
+    } else if (db1_i && (err = column_sum(dY_i, static_cast<float*>(db1_i), tokens, n, e,
+                                          dW2_i, n * h * 4, s)) != hipSuccess) {
         return TP_ERR_HIP;
+    }
     if (use_transposed_operands(tokens, h, n, e)) {
         // The weight gradients as products with a K-contiguous first operand:
         // H_i^T [n][T] is staged in dW1_i's memory (written only afterwards)
