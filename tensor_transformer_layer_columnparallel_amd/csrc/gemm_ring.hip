@@ -116,12 +116,18 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p)
     return (uint32_t)reinterpret_cast<uintptr_t>((TP_LDS const void*)p);
 }
 
-// Chunk permutations of K-major buffers (XORs of row bits): any 8, 16 or 32
-// consecutive lanes reading 16 bytes each (row i, chunk g of the slab) hit
-// distinct banks of a 128-, 256- or 512-byte bank window.
+// Chunk permutations of K-major buffers (XORs of row bits) for the fragment
+// reads (lane l: row l % 16, chunk l / 16, 16 bytes).
+// swz4 (32-k slabs, 64-byte rows) was chosen by measuring ds_read_b128 with
+// all 256 two-bit XOR forms on the device: only how row bits 2 and 3 enter
+// matters.  With d1 and d2 the chunk XORs of rows 4 and 8 (relative to row
+// 0), reads run at full rate (about 190 B/clk/CU) when d1 != d2 and neither
+// is 1, at 2/3 of it for most other forms (d1 = 1, d2 = 2 ran at 118
+// B/clk/CU and showed as LDS bank-conflict cycles in the NT products), and
+// at 1/3 for d1 = d2 = 1.  This one has d1 = 0, d2 = 2 and measured fastest.
 __device__ __forceinline__ int swz4(int row)
 {
-    return ((row >> 2) & 1) | ((((row >> 1) ^ (row >> 3)) & 1) << 1);
+    return (row & 1) | ((((row >> 1) ^ (row >> 3)) & 1) << 1);
 }
 __device__ __forceinline__ int swz8(int row)
 {
