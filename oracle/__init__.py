@@ -211,14 +211,14 @@ def layernorm(x, gamma=None, beta=None, eps: float = 1e-5) -> np.ndarray:
 def mlp_shard_fwd_rows(X, W1_i, b1_i, W2_i, rows):
     """(Y_i, H_i, Z_i) restricted to token rows ``rows``."""
     rows = np.asarray(rows)
-    return mlp_shard_fwd(_f64(X)[rows], W1_i, b1_i, W2_i)
+    return mlp_shard_fwd(_f64(X[rows]), W1_i, b1_i, W2_i)
 
 
 def mlp_shard_bwd_rows(X, W1_i, b1_i, W2_i, dZ, rows):
     """dY_i[rows, :] and dX_i[rows, :]: the backward on the token subset
     (the dW entries such a run returns are partial sums and are dropped)."""
     rows = np.asarray(rows)
-    g = mlp_shard_bwd(_f64(X)[rows], W1_i, b1_i, W2_i, _f64(dZ)[rows])
+    g = mlp_shard_bwd(_f64(X[rows]), W1_i, b1_i, W2_i, _f64(dZ[rows]))
     return {"dY": g["dY"], "dX": g["dX"]}
 
 

@@ -434,6 +434,77 @@ def test_gpt3_shard_backward_sampled(gpt3_run):
     assert_close(out["db1"][cols], gc["db1"], "bf16", "gpt3 db1")
 
 
+MAX_OPERAND_BYTES = 2**31 - 1   # the boundary rejects any larger operand
+
+
+def test_largest_accepted_activation_column_sampled(B):
+    # X [65535, 16384] bf16 is 32 KiB under 2^31 bytes: the tile kernel's
+    # 32-bit buffer offsets reach their largest values; 65535 rows leave a
+    # 255-row last tile.  One more token is rejected.
+    w = configs.scaled(configs.GPT3_SHARD, "largest_x", T=65535, h=16384, ffn=256, t=1,
+                       backward=False)
+    assert w.T * w.h * 2 <= MAX_OPERAND_BYTES < (w.T + 1) * w.h * 2
+    _log(f"case {w.name}: generating inputs")
+    d_h = synth.make_inputs(w, with_dz=False)
+    X, W, b = dev(d_h["X"]), dev(d_h["W1"][0]), dev(d_h["b1"][0])
+    H = torch.empty(w.T, w.n, dtype=torch.bfloat16, device="cuda")
+    Y = torch.empty(w.T, w.n, dtype=torch.bfloat16, device="cuda")
+    _log(f"case {w.name}: column layer")
+    B.tp_column_linear(X, W, b, H, Y, w.T, w.h, w.ffn, w.t, 0, B.TP_BF16, B.TP_BF16,
+                       B.TP_ACT_GELU_TANH)
+    torch.cuda.synchronize()
+    assert B.tp_column_linear(X, W, b, H, Y, w.T + 1, w.h, w.ffn, w.t, 0, B.TP_BF16, B.TP_BF16,
+                              B.TP_ACT_GELU_TANH, check=False) == B.TP_ERR_SHAPE
+    rows = sample_indices(w.T, 8, seed=5)
+    rows = np.union1d(rows, np.arange(w.T - 255, w.T, 37))   # the ragged last tile
+    _log(f"case {w.name} rows {rows.tolist()}")
+    Xr = d_h["X"][torch.from_numpy(rows)]
+    rY = oracle.column_linear(Xr, d_h["W1"][0], d_h["b1"][0], gelu=False)
+    rH = oracle.column_linear(Xr, d_h["W1"][0], d_h["b1"][0], gelu=True)
+    idx = torch.from_numpy(rows).cuda()
+    assert_close(Y[idx], rY, "bf16", "largest X: Y rows")
+    assert_close(H[idx], rH, "bf16", "largest X: H rows")
+
+
+def test_largest_accepted_fp32_outputs_fwd_bwd_sampled(B):
+    # Z and dX [32736, 16384] fp32 are just under 2^31 bytes; T % 32 == 0, so
+    # the weight gradients take the transposed-operand products (X^T of 1 GiB
+    # staged in dX).  T = 32768 is rejected.
+    w = configs.scaled(configs.GPT3_SHARD, "largest_fp32_out", T=32736, h=16384, ffn=256, t=1)
+    assert w.T * w.h * 4 <= MAX_OPERAND_BYTES < 32768 * w.h * 4
+    _log(f"case {w.name}: generating inputs")
+    d_h = synth.make_inputs(w)
+    d = to_device(d_h)
+    _log(f"case {w.name}: forward + backward")
+    Y, H, Z = gpu_shard_fwd(B, w, d, 0)
+    g = gpu_shard_bwd(B, w, d, 0, Y, H)
+    torch.cuda.synchronize()
+    assert B.tp_mlp_shard_fwd(d["X"], d["W1"][0], d["b1"][0], d["W2"][0], H, Y, Z, 32768, w.h,
+                              w.ffn, w.t, 0, B.TP_BF16, check=False) == B.TP_ERR_SHAPE
+    out = {"Y": Y.cpu(), "H": H.cpu(), "Z": Z.cpu()}
+    out.update({k: v.cpu() for k, v in g.items()})
+    del d, Y, H, Z, g
+    torch.cuda.empty_cache()
+    rows = sample_indices(w.T, 4, seed=6)
+    cols = np.array([0, w.n - 1])
+    _log(f"case {w.name} rows {rows.tolist()} cols {cols.tolist()}")
+    rY, rH, rZ = oracle.mlp_shard_fwd_rows(d_h["X"], d_h["W1"][0], d_h["b1"][0], d_h["W2"][0],
+                                           rows)
+    assert_close(out["Y"][rows], rY, "bf16", "largest fp32: Y rows")
+    assert_close(out["H"][rows], rH, "bf16", "largest fp32: H rows")
+    assert_close(out["Z"][rows], rZ, "bf16", "largest fp32: Z rows")
+    gr = oracle.mlp_shard_bwd_rows(d_h["X"], d_h["W1"][0], d_h["b1"][0], d_h["W2"][0],
+                                   d_h["dZ"], rows)
+    assert_close(out["dY"][rows], gr["dY"], "bf16", "largest fp32: dY rows")
+    assert_close(out["dX"][rows], gr["dX"], "bf16", "largest fp32: dX rows")
+    _log(f"case {w.name}: oracle column subset")
+    gc = oracle.mlp_shard_bwd_cols(d_h["X"], d_h["W1"][0], d_h["b1"][0], d_h["W2"][0],
+                                   d_h["dZ"], cols)
+    assert_close(out["dW1"][:, cols], gc["dW1"], "bf16", "largest fp32: dW1 cols")
+    assert_close(out["dW2"][cols, :], gc["dW2"], "bf16", "largest fp32: dW2 rows")
+    assert_close(out["db1"][cols], gc["db1"], "bf16", "largest fp32: db1")
+
+
 def test_full_layer_emulation_8_shards_sampled(B):
     w = configs.FULL_LAYER_8
     _log(f"case {w.name}: generating inputs")
