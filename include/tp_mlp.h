@@ -142,6 +142,10 @@ TP_API int tp_mlp_shard_fwd(const void* X, const void* W1_i, const void* b1_i, c
  *            last two products), dW2_i [n,h], dW1_i [h,n], dX_i [tokens,h],
  *            db1_i [n] or NULL                     fp32
  * tokens == 0 is valid: the weight gradients are then written as zeros.
+ * db1_i is summed in fp32 in a fixed order (run-to-run deterministic); its
+ * summands are the dY product's fp32 results before rounding to `dtype` when
+ * that product runs on the tile kernel (bf16, tokens >= 256, n >= 192,
+ * h % 32 == 0), else the stored dY_i.
  * dW2_i, dW1_i and dX_i also serve as scratch space during the call (partial
  * sums of db1_i; transposed copies of H_i and X) before they receive their
  * results, so no output may overlap an input.

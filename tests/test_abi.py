@@ -22,6 +22,17 @@ def B():
     return binding
 
 
+@pytest.fixture(scope="module")
+def Bfake(B):
+    """The binding, for calls with fake addresses.  Those calls must fail
+    validation; should one of them not, it would launch on a bogus address,
+    so they run only where no GPU is visible."""
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("fake-address validation tests run only without a visible GPU")
+    return B
+
+
 def test_header_declares_the_entry_points_and_status_string():
     assert set(_declared_functions()) == {
         "tp_column_linear", "tp_row_linear", "tp_mlp_shard_fwd", "tp_mlp_shard_bwd",
@@ -47,7 +58,8 @@ P2 = 0x20000
 MIS = 0x10008
 
 
-def test_column_linear_rejects(B):
+def test_column_linear_rejects(Bfake):
+    B = Bfake
     f = lambda **kw: B.tp_column_linear(**{**dict(
         X=P, W_i=P, b_i=None, Y_i=P, pre_save=None, tokens=32, in_features=768, out_features=3072, t=4,
         rank=0, dtype=B.TP_BF16, out_dtype=B.TP_BF16, act=B.TP_ACT_NONE, stream=0,
@@ -74,7 +86,8 @@ def test_column_linear_rejects(B):
     assert f(tokens=1 << 20, in_features=1 << 10) == B.TP_ERR_SHAPE
 
 
-def test_row_linear_rejects(B):
+def test_row_linear_rejects(Bfake):
+    B = Bfake
     f = lambda **kw: B.tp_row_linear(**{**dict(
         X_i=P, W_i=P, Z_i=P, tokens=8, in_features=64, out_features=32, t=2, rank=1,
         dtype=B.TP_BF16, out_dtype=B.TP_F32, stream=0, check=False), **kw})
@@ -85,7 +98,8 @@ def test_row_linear_rejects(B):
     assert f(out_features=36) == B.TP_ERR_SHAPE
 
 
-def test_mlp_fwd_bwd_reject(B):
+def test_mlp_fwd_bwd_reject(Bfake):
+    B = Bfake
     fwd = lambda **kw: B.tp_mlp_shard_fwd(**{**dict(
         X=P, W1_i=P, b1_i=None, W2_i=P, H_i=P, Y_i_save=None, Z_i=P, tokens=16, h=64,
         ffn=256, t=8, rank=0, dtype=B.TP_BF16, stream=0, check=False), **kw})
@@ -104,7 +118,8 @@ def test_mlp_fwd_bwd_reject(B):
     assert bwd(h=60) == B.TP_ERR_SHAPE
 
 
-def test_shard_reduce_rejects(B):
+def test_shard_reduce_rejects(Bfake):
+    B = Bfake
     f = lambda **kw: B.tp_shard_reduce(**{**dict(
         parts=P, out=P2, tokens=4, cols=16, t=8, op=B.TP_REDUCE_SUM, in_dtype=B.TP_F32,
         out_dtype=B.TP_F32, stream=0, check=False), **kw})
@@ -118,7 +133,8 @@ def test_shard_reduce_rejects(B):
     assert f(tokens=-3) == B.TP_ERR_SHAPE
 
 
-def test_reduce_scatter_rejects(B):
+def test_reduce_scatter_rejects(Bfake):
+    B = Bfake
     f = lambda **kw: B.tp_shard_reduce_scatter(**{**dict(
         parts=P, out=P2, tokens=16, cols=16, t=8, rank=3, in_dtype=B.TP_F32,
         out_dtype=B.TP_BF16, stream=0, check=False), **kw})
@@ -132,7 +148,8 @@ def test_reduce_scatter_rejects(B):
     assert f(in_dtype=7) == B.TP_ERR_DTYPE
 
 
-def test_layernorm_rejects(B):
+def test_layernorm_rejects(Bfake):
+    B = Bfake
     f = lambda **kw: B.tp_layernorm(**{**dict(
         x=P, gamma=None, beta=None, y=P2, tokens=4, cols=16, eps=1e-5, in_dtype=B.TP_F32,
         out_dtype=B.TP_BF16, stream=0, check=False), **kw})
@@ -145,3 +162,38 @@ def test_layernorm_rejects(B):
     assert f(eps=float("inf")) == B.TP_ERR_ARG
     assert f(y=P) == B.TP_ERR_ARG          # in place needs equal types
     assert f(out_dtype=5) == B.TP_ERR_DTYPE
+
+
+def test_binding_checks_tensor_arguments(Bfake):
+    B = Bfake
+    # The binding refuses tensors the library would misread, before the call:
+    # wrong element size, too few elements, non-contiguous, not on the device.
+    # The other arguments are plain (unchecked) addresses.
+    import torch
+    bf, f32 = torch.bfloat16, torch.float32
+    T, h, ffn, t = 32, 64, 256, 2
+    n = ffn // t
+    call = lambda **kw: B.tp_column_linear(**{**dict(
+        X=P, W_i=P, b_i=None, Y_i=P, pre_save=None, tokens=T, in_features=h, out_features=ffn,
+        t=t, rank=0, dtype=bf, out_dtype=bf, act=B.TP_ACT_NONE, stream=0), **kw})
+    with pytest.raises(ValueError, match="X: element size"):
+        call(X=torch.zeros(T, h, dtype=f32))
+    with pytest.raises(ValueError, match="X: holds"):
+        call(X=torch.zeros(T, h, dtype=bf), tokens=T + 1)
+    with pytest.raises(ValueError, match="Y_i: holds"):
+        call(Y_i=torch.zeros(T, n - 8, dtype=bf))
+    with pytest.raises(ValueError, match="Y_i: element size"):
+        call(Y_i=torch.zeros(T, n, dtype=bf), out_dtype=f32)
+    with pytest.raises(ValueError, match="X: must be contiguous"):
+        call(X=torch.zeros(h, T, dtype=bf).t())
+    with pytest.raises(ValueError, match="X: must be a device tensor"):
+        call(X=torch.zeros(T, h, dtype=bf))
+    with pytest.raises(ValueError, match="Z_i: element size"):
+        B.tp_mlp_shard_fwd(P, P, None, P, P, None, torch.zeros(T, h, dtype=bf), T, h, ffn, t, 0,
+                           bf, stream=0)
+    with pytest.raises(ValueError, match="out: holds"):
+        B.tp_shard_reduce(P, torch.zeros(T, h), T, h, 2, B.TP_REDUCE_CONCAT, f32, f32, stream=0)
+    # shapes the library rejects itself skip the size check and return its status
+    assert (ffn + 8) % 5 != 0
+    assert B.tp_column_linear(P, P, None, P, None, T, h, ffn + 8, 5, 0, bf, bf,
+                              B.TP_ACT_NONE, stream=0, check=False) == B.TP_ERR_INDIVISIBLE

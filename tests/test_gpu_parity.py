@@ -271,13 +271,14 @@ def test_empty_tokens(B):
     # Empty tensors have no storage; pass an aligned placeholder wherever the
     # ABI requires a pointer to a [0, *] array.
     ph = torch.empty(8, dtype=torch.bfloat16, device="cuda")
+    phf = torch.empty(8, dtype=torch.float32, device="cuda")
     W1 = torch.randn(h, n, device="cuda").bfloat16()
     W2 = torch.randn(n, h, device="cuda").bfloat16()
-    B.tp_mlp_shard_fwd(ph, W1, None, W2, ph, None, ph, 0, h, ffn, t, 0, B.TP_BF16)
+    B.tp_mlp_shard_fwd(ph, W1, None, W2, ph, None, phf, 0, h, ffn, t, 0, B.TP_BF16)
     dW2 = torch.full((n, h), 7.0, device="cuda")
     dW1 = torch.full((h, n), 7.0, device="cuda")
     db1 = torch.full((n,), 7.0, device="cuda")
-    B.tp_mlp_shard_bwd(ph, W1, W2, ph, ph, ph, ph, dW2, dW1, ph, db1, 0, h, ffn, t, 0,
+    B.tp_mlp_shard_bwd(ph, W1, W2, ph, ph, ph, ph, dW2, dW1, phf, db1, 0, h, ffn, t, 0,
                        B.TP_BF16)
     torch.cuda.synchronize()
     assert torch.count_nonzero(dW2) == 0 and torch.count_nonzero(dW1) == 0
@@ -453,7 +454,9 @@ def test_largest_accepted_activation_column_sampled(B):
     B.tp_column_linear(X, W, b, H, Y, w.T, w.h, w.ffn, w.t, 0, B.TP_BF16, B.TP_BF16,
                        B.TP_ACT_GELU_TANH)
     torch.cuda.synchronize()
-    assert B.tp_column_linear(X, W, b, H, Y, w.T + 1, w.h, w.ffn, w.t, 0, B.TP_BF16, B.TP_BF16,
+    # raw addresses: the library's own size check, not the binding's
+    ptrs = [x.data_ptr() for x in (X, W, b, H, Y)]
+    assert B.tp_column_linear(*ptrs, w.T + 1, w.h, w.ffn, w.t, 0, B.TP_BF16, B.TP_BF16,
                               B.TP_ACT_GELU_TANH, check=False) == B.TP_ERR_SHAPE
     rows = sample_indices(w.T, 8, seed=5)
     rows = np.union1d(rows, np.arange(w.T - 255, w.T, 37))   # the ragged last tile
@@ -479,8 +482,9 @@ def test_largest_accepted_fp32_outputs_fwd_bwd_sampled(B):
     Y, H, Z = gpu_shard_fwd(B, w, d, 0)
     g = gpu_shard_bwd(B, w, d, 0, Y, H)
     torch.cuda.synchronize()
-    assert B.tp_mlp_shard_fwd(d["X"], d["W1"][0], d["b1"][0], d["W2"][0], H, Y, Z, 32768, w.h,
-                              w.ffn, w.t, 0, B.TP_BF16, check=False) == B.TP_ERR_SHAPE
+    ptrs = [x.data_ptr() for x in (d["X"], d["W1"][0], d["b1"][0], d["W2"][0], H, Y, Z)]
+    assert B.tp_mlp_shard_fwd(*ptrs, 32768, w.h, w.ffn, w.t, 0, B.TP_BF16,
+                              check=False) == B.TP_ERR_SHAPE
     out = {"Y": Y.cpu(), "H": H.cpu(), "Z": Z.cpu()}
     out.update({k: v.cpu() for k, v in g.items()})
     del d, Y, H, Z, g
