@@ -86,7 +86,9 @@ typedef enum { TP_REDUCE_SUM = 0, TP_REDUCE_CONCAT = 1, TP_REDUCE_CONCAT_TOKENS 
  *   b_i [out_features / t] or NULL (= 0)   element type `dtype`
  *   Y_i [tokens, out_features / t]         element type `out_dtype`
  *   pre_save [tokens, out_features / t] or NULL: receives the pre-activation
- *            (element type `dtype`), the value the backward's g'() needs
+ *            (element type `dtype`), the value the backward's g'() needs;
+ *            must be NULL with TP_ACT_NONE, where Y_i is the pre-activation
+ *            itself (TP_ERR_ARG otherwise)
  * act: TP_ACT_NONE or TP_ACT_GELU_TANH, g(y) = 0.5 y (1 + tanh(sqrt(2/pi)
  * (y + 0.044715 y^3))).  dtype TP_F32 requires out_dtype TP_F32; dtype
  * TP_BF16 allows either.  out_features % t != 0 -> TP_ERR_INDIVISIBLE.
