@@ -149,8 +149,8 @@ TP_API int tp_mlp_shard_fwd(const void* X, const void* W1_i, const void* b1_i, c
  * that product runs on the tile kernel (bf16, tokens >= 256, n >= 192,
  * h % 32 == 0), else the stored dY_i.
  * dW2_i, dW1_i and dX_i also serve as scratch space during the call (partial
- * sums of db1_i; transposed copies of H_i and X) before they receive their
- * results, so no output may overlap an input.
+ * sums of db1_i; transposed copies of H_i and of dY_i or X) before they
+ * receive their results, so no output may overlap an input.
  */
 TP_API int tp_mlp_shard_bwd(const void* X, const void* W1_i, const void* W2_i,
                      const void* Y_i, const void* H_i, const void* dZ,

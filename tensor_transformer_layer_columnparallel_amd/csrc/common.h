@@ -25,6 +25,7 @@ enum class Epi {
     Bias = 1,       // C = acc + bias[col]
     BiasGelu = 2,   // Y = acc + bias[col] (optionally saved), C = g(Y)
     DGelu = 3,      // C = acc * g'(aux[row][col])
+    StoreT = 4,     // C^T = acc: C is [N][M] (fp32 results only)
 };
 
 template <Elt E> struct EltType;

@@ -460,6 +460,49 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_ring_kernel(GemmArgs p, int t
     const bf16* bias = static_cast<const bf16*>(p.bias);
     const bf16* aux = static_cast<const bf16*>(p.aux);
     OutT* C = static_cast<OutT*>(p.C);
+    if constexpr (EPI == Epi::StoreT) {
+        // C is [N][M]: column c of the tile is row n0 + c of C, the tile's
+        // 256 rows contiguous in it.  Staged through LDS in two passes of
+        // half the tile's columns, transposed on the way in (4-byte stores;
+        // a pitch of kBM + 4 words puts the four column groups of a store on
+        // distinct banks), then copied out as 16-byte chunks of whole rows.
+        static_assert(sizeof(OutT) == 4, "transposed results are fp32");
+        constexpr int kColsPass = BN / 2;
+        constexpr int kPitchT = kBM + 4;   // words
+        constexpr int kChunksRow = kBM / 4;
+        static_assert(kColsPass * kPitchT * 4 <= kABytes + kBBytes, "staging exceeds the ring");
+        static_assert(kColsPass % kWaveN == 0, "a wave's columns lie in one pass");
+        float* stage = reinterpret_cast<float*>(smem);
+        barrier();   // every wave's loads have landed and no wave reads the ring
+#pragma unroll
+        for (int pass = 0; pass < 2; ++pass) {
+            const int c0 = pass * kColsPass;
+            if (wrow_b >= c0 && wrow_b < c0 + kColsPass) {   // uniform per wave
+#pragma unroll
+                for (int a = 0; a < kFragM; ++a) {
+                    const int r = wrow_a + a * 16 + (lane & 15);
+#pragma unroll
+                    for (int b = 0; b < kFragN; ++b)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int c = wrow_b + b * 16 + 4 * (lane >> 4) + e - c0;
+                            stage[c * kPitchT + r] = acc[a][b][e];
+                        }
+                }
+            }
+            wait_lgkmcnt0();   // s_barrier itself does not wait for LDS stores
+            barrier();
+            for (int q = threadIdx.x; q < kColsPass * kChunksRow; q += 64 * NW) {
+                const int row = q / kChunksRow, ch = q % kChunksRow;
+                const int64_t gn = n0 + c0 + row, gm = m0 + (int64_t)ch * 4;
+                if (gn < p.N && gm < p.M)   // M % 4 == 0: a chunk is all in or all out
+                    *reinterpret_cast<i32x4*>(C + gn * p.M + gm) =
+                        *reinterpret_cast<const i32x4*>(stage + row * kPitchT + ch * 4);
+            }
+            barrier();
+        }
+        return;
+    }
     if constexpr (sizeof(OutT) == 4 && (EPI == Epi::Store || EPI == Epi::Bias)) {
         // Plain fp32 results (the row-layer partials and the backward's
         // gradients) go through LDS (the ring is free now) so that the stores
@@ -662,6 +705,11 @@ hipError_t gemm_ring(const GemmArgs& p, Layout layout, Epi epi, Elt out, hipStre
         if (epi == Epi::Bias) {
             if (out == Elt::BF16) return launch<true, false, Epi::Bias, bf16>(p, stream);
             return launch<true, false, Epi::Bias, float>(p, stream);
+        }
+        if (epi == Epi::StoreT) {
+            // stored in 16-byte chunks of 4 consecutive rows
+            if (out != Elt::F32 || p.M % 4 != 0) return hipErrorInvalidValue;
+            return launch<true, false, Epi::StoreT, float>(p, stream);
         }
         if (out == Elt::BF16) return launch<true, false, Epi::Store, bf16>(p, stream);
         return launch<true, false, Epi::Store, float>(p, stream);

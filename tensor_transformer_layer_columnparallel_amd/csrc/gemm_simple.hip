@@ -197,7 +197,7 @@ __global__ __launch_bounds__(kThreads) void gemm_simple_kernel(GemmArgs p)
             for (int e = 0; e < 4; ++e) {
                 const int64_t row = m0 + wm * WM + i * 16 + (lane >> 4) * 4 + e;
                 if (row >= p.M) continue;
-                const int64_t off = row * p.N + col;
+                const int64_t off = EPI == Epi::StoreT ? col * p.M + row : row * p.N + col;
                 float v = acc[i][j][e];
                 if constexpr (EPI == Epi::Bias) {
                     v += bcol;
@@ -237,6 +237,7 @@ hipError_t gemm_simple(const GemmArgs& p, Elt elt, Layout layout, Epi epi, Elt o
         case Layout::NN:
             if (epi == Epi::BiasGelu) TP_CASE(float, true, false, Epi::BiasGelu, float);
             if (epi == Epi::Bias) TP_CASE(float, true, false, Epi::Bias, float);
+            if (epi == Epi::StoreT) TP_CASE(float, true, false, Epi::StoreT, float);
             TP_CASE(float, true, false, Epi::Store, float);
         case Layout::NT:
             if (epi == Epi::DGelu) TP_CASE(float, true, true, Epi::DGelu, float);
@@ -254,6 +255,10 @@ hipError_t gemm_simple(const GemmArgs& p, Elt elt, Layout layout, Epi epi, Elt o
             if (epi == Epi::Bias) {
                 if (out == Elt::BF16) TP_CASE(bf16, true, false, Epi::Bias, bf16);
                 TP_CASE(bf16, true, false, Epi::Bias, float);
+            }
+            if (epi == Epi::StoreT) {
+                if (out != Elt::F32) return hipErrorInvalidValue;
+                TP_CASE(bf16, true, false, Epi::StoreT, float);
             }
             if (out == Elt::BF16) TP_CASE(bf16, true, false, Epi::Store, bf16);
             TP_CASE(bf16, true, false, Epi::Store, float);

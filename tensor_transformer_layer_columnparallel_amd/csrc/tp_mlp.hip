@@ -57,9 +57,10 @@ int status_of(hipError_t e) { return e == hipSuccess ? TP_OK : TP_ERR_HIP; }
 // The weight-gradient products x^T dy read both operands M/N-contiguous,
 // which the tile kernel can only do with transposing LDS reads of both.  With
 // bf16 operands, a token count that whole 32-deep slabs cover and room for
-// H_i^T (n x T bf16) in the fp32 dW1_i (h x n), the two activations are
-// transposed first (an HBM-bound pass) and the products run with a
-// K-contiguous first operand.
+// H_i^T (n x T bf16) in the fp32 dW1_i (h x n), one activation per product
+// is transposed first (an HBM-bound pass) and the products run with a
+// K-contiguous first operand: H_i^T dZ, and dY_i^T X stored transposed (or
+// X^T dY_i where dY_i^T does not fit in dX_i).
 bool use_transposed_operands(int64_t tokens, int64_t h, int64_t n, Elt e)
 {
     if (e != Elt::BF16 || tokens == 0 || tokens % 32 != 0) return false;
@@ -215,16 +216,28 @@ int tp_mlp_shard_bwd(const void* X, const void* W1_i, const void* W2_i, const vo
         return TP_ERR_HIP;
     }
     if (use_transposed_operands(tokens, h, n, e)) {
-        // The weight gradients as products with a K-contiguous first operand:
-        // H_i^T [n][T] is staged in dW1_i's memory (written only afterwards)
-        // and X^T [h][T] in dX_i's (written last).
+        // The weight gradients as products with a K-contiguous first operand.
+        // dW2_i = (H_i^T) dZ, with H_i^T [n][T] staged in dW1_i's memory
+        // (written only afterwards).
         if ((err = transpose16(H_i, dW1_i, tokens, n, s)) != hipSuccess ||
             (err = run_gemm(dW1_i, dZ, dW2_i, nullptr, nullptr, nullptr, n, h, tokens, e,
-                            Layout::NN, Epi::Store, Elt::F32, s)) != hipSuccess ||
-            (err = transpose16(X, dX_i, tokens, h, s)) != hipSuccess ||
-            (err = run_gemm(dX_i, dY_i, dW1_i, nullptr, nullptr, nullptr, h, n, tokens, e,
                             Layout::NN, Epi::Store, Elt::F32, s)) != hipSuccess)
             return TP_ERR_HIP;
+        if (n <= 2 * h) {
+            // dW1_i^T = (dY_i^T) X, stored transposed into dW1_i: dY_i^T
+            // [n][T] (half the bytes of X^T when n = h / 2) is staged in
+            // dX_i's memory (written last).
+            if ((err = transpose16(dY_i, dX_i, tokens, n, s)) != hipSuccess ||
+                (err = run_gemm(dX_i, X, dW1_i, nullptr, nullptr, nullptr, n, h, tokens, e,
+                                Layout::NN, Epi::StoreT, Elt::F32, s)) != hipSuccess)
+                return TP_ERR_HIP;
+        } else {
+            // dW1_i = (X^T) dY_i with X^T [h][T] staged in dX_i's memory.
+            if ((err = transpose16(X, dX_i, tokens, h, s)) != hipSuccess ||
+                (err = run_gemm(dX_i, dY_i, dW1_i, nullptr, nullptr, nullptr, h, n, tokens, e,
+                                Layout::NN, Epi::Store, Elt::F32, s)) != hipSuccess)
+                return TP_ERR_HIP;
+        }
     } else {
         // dW2_i = H_i^T dZ: H_i [T][n] is [K][M], dZ [T][h] is [K][N].
         if ((err = run_gemm(H_i, dZ, dW2_i, nullptr, nullptr, nullptr, n, h, tokens, e,

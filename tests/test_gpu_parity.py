@@ -243,6 +243,7 @@ REDUCED = [
     (270, 328, 2624, 8),     # K = 328 not a multiple of 64; ragged K = 270 in x^T dy
     (520, 768, 4096, 8),     # two 256-row tiles + 8 rows, 512-wide shard
     (64, 4096, 8192, 2),     # 4096 x 4096 weight gradients: 256-wide tiles
+    (288, 256, 1024, 1),     # n = 4h: dW1 from X^T (dY^T would not fit in dX's memory)
     (288, 544, 2304, 8),     # K = 544 and K = T = 288: an odd number of 32-deep slabs
                              # in the tile kernel (half of the last 64-deep unit past K),
                              # in the forward and in the transposed weight gradients
