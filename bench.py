@@ -315,8 +315,8 @@ def main():
         copy_calibration(args.copy_calibration)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build runs one tensor-parallel rank's "
-              "shard per GPU and has no multi-GPU exchange; run with --gpus 1.", flush=True)
+        print("bench.py measures one GPU only: the library computes one tensor-parallel rank's "
+              "shard per GPU and has no exchange between GPUs; run with --gpus 1.", flush=True)
         sys.exit(2)
 
     import torch
