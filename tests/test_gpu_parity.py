@@ -344,6 +344,48 @@ def test_side_stream_matches_default_stream(B):
         assert torch.equal(a, b)
 
 
+def test_step_captured_in_a_hip_graph_replays_bit_identical(B):
+    # The library enqueues only kernels (no allocation, memset or copy), so a
+    # whole forward + backward can be captured in a HIP graph.  Each replay
+    # (outputs cleared by eager work in between) must give the eager bytes.
+    w = configs.scaled(configs.GPT3_SHARD, "graph", T=288, h=544, ffn=2304, t=8)
+    _log(f"case {w.name}: eager run, capture, three replays")
+    d = to_device(synth.make_inputs(w))
+    T, h, n = w.T, w.h, w.n
+    bf = torch.bfloat16
+    H = torch.empty(T, n, dtype=bf, device="cuda")
+    Y = torch.empty(T, n, dtype=bf, device="cuda")
+    Z = torch.empty(T, h, device="cuda")
+    dY = torch.empty(T, n, dtype=bf, device="cuda")
+    dW2 = torch.empty(n, h, device="cuda")
+    dW1 = torch.empty(h, n, device="cuda")
+    dX = torch.empty(T, h, device="cuda")
+    db1 = torch.empty(n, device="cuda")
+    outs = (H, Y, Z, dY, dW2, dW1, dX, db1)
+
+    def step():
+        B.tp_mlp_shard_fwd(d["X"], d["W1"][0], d["b1"][0], d["W2"][0], H, Y, Z, T, h, w.ffn,
+                           w.t, 0, bf)
+        B.tp_mlp_shard_bwd(d["X"], d["W1"][0], d["W2"][0], Y, H, d["dZ"], dY, dW2, dW1, dX,
+                           db1, T, h, w.ffn, w.t, 0, bf)
+
+    step()
+    torch.cuda.synchronize()
+    eager = [o.clone() for o in outs]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for o in outs:
+            o.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, o, e in zip(("H", "Y", "Z", "dY", "dW2", "dW1", "dX", "db1"), outs, eager):
+            assert torch.equal(o, e), f"replay {rep}: {name} differs from the eager run"
+
+
 def test_all_ones_and_identity(B):
     _log("case all-ones / identity")
     T, h, n = 64, 768, 256
