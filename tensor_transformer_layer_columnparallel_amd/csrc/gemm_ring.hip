@@ -671,11 +671,11 @@ hipError_t launch(const GemmArgs& p, hipStream_t stream)
     constexpr int WM = AK ? (BK ? TPMLP_RING_WM_NT : TPMLP_RING_WM_NN) : TPMLP_RING_WM_TN;
     const int tm = (int)((p.M + kBM - 1) / kBM);
     const int tn = (int)((p.N + kBN - 1) / kBN);
-    // Products with several waves of tiles (the weight gradients) walk an
-    // XCD's tiles in 4-row groups, which cut their time by about 4% on the
-    // device; one- and two-wave products keep the plain order, which measured
-    // as fast or faster for them.
-    const int group_m = tm * tn > 2 * kCUs ? 4 : 0;
+    // Products with several waves of tiles walk an XCD's tiles in 4-row
+    // groups: the weight gradients (six waves) about 4% faster, the two-wave
+    // NN row-layer product about 2%.  One-wave products and the two-wave NT
+    // product keep the plain order, which measured as fast or faster for them.
+    const int group_m = tm * tn > 2 * kCUs || (!BK && tm * tn >= 2 * kCUs) ? 4 : 0;
     hipLaunchKernelGGL((gemm_ring_kernel<NW, WM, AK, BK, E, O>), dim3((unsigned)(tm * tn)),
                        dim3(64 * NW), 0, stream, p, tm, tn, group_m);
     return hipGetLastError();
