@@ -259,6 +259,44 @@ def test_reduced_mlp_fwd_bwd_bf16(B, shape):
     _full_check(B, w)
 
 
+def _random_shapes(count, seed):
+    """Seeded (T, h, ffn, t) with feature widths that are multiples of 8:
+    mixes tile-kernel and general-kernel products, ragged tails in every
+    dimension, K % 32 != 0, token counts that take the transposed weight
+    gradients (T % 32 == 0) and shard widths on both sides of 2h."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < count:
+        t = int(rng.choice([1, 2, 3, 4, 8]))
+        # mostly K % 32 == 0 (the tile kernel's K-contiguous operands)
+        h = int(32 * rng.integers(2, 26) if rng.random() < 0.75 else 8 * rng.integers(4, 100))
+        u = rng.random()
+        n = int(32 * rng.integers(6, 28) if u < 0.5 else
+                8 * rng.integers(24, 110) if u < 0.85 else 8 * rng.integers(4, 24))
+        u = rng.random()
+        T = int(rng.integers(1, 256) if u < 0.25 else
+                rng.integers(256, 760) if u < 0.6 else 32 * rng.integers(8, 24))
+        out.append((T, h, n * t, t))
+    return out
+
+
+@pytest.mark.parametrize("shape", _random_shapes(32, seed=11), ids=lambda s: "x".join(map(str, s)))
+def test_random_shapes_fwd_bwd_bf16(B, shape):
+    T, h, ffn, t = shape
+    w = configs.scaled(configs.GPT3_SHARD, "random_bf16", T=T, h=h, ffn=ffn, t=t, ranks=(t - 1,))
+    _log(f"case random bf16 {shape}")
+    _full_check(B, w, seed=T + h)
+
+
+@pytest.mark.parametrize("shape", _random_shapes(6, seed=12), ids=lambda s: "x".join(map(str, s)))
+def test_random_shapes_fwd_bwd_f32(B, shape):
+    T, h, ffn, t = shape
+    w = configs.scaled(configs.TINY_F32, "random_f32", T=T, h=h, ffn=ffn, t=t, ranks=(0,),
+                       bias_zero=False)
+    _log(f"case random f32 {shape}")
+    _full_check(B, w, seed=T + h)
+
+
 def test_reduced_mlp_fwd_bwd_f32(B):
     w = configs.scaled(configs.TINY_F32, "reduced_f32", T=150, h=136, ffn=544, t=2)
     _log("case reduced f32")
