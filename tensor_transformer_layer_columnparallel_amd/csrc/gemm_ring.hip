@@ -651,7 +651,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_ring_kernel(GemmArgs p, int t
 #define TPMLP_RING_NW_NT 8
 #endif
 #ifndef TPMLP_RING_WM_NT
-#define TPMLP_RING_WM_NT 4
+#define TPMLP_RING_WM_NT 2
 #endif
 #ifndef TPMLP_RING_NW_TN
 #define TPMLP_RING_NW_TN 8
