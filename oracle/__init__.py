@@ -65,6 +65,7 @@ def _load():
             "oracle_row_linear": [dp, dp, dp, i64, i64, i64],
             "oracle_mlp_shard_fwd": [dp, dp, dp, dp, dp, dp, dp, i64, i64, i64],
             "oracle_mlp_shard_bwd": [dp] * 11 + [i64, i64, i64],
+            "oracle_linear_bwd": [dp] * 6 + [i64, i64, i64],
             "oracle_shard_sum": [dp, dp, ctypes.c_int, i64],
             "oracle_shard_concat": [dp, dp, ctypes.c_int, i64, i64],
             "oracle_reduce_scatter": [dp, dp, ctypes.c_int, i64, i64, ctypes.c_int],
@@ -204,6 +205,19 @@ def layernorm(x, gamma=None, beta=None, eps: float = 1e-5) -> np.ndarray:
     y = np.empty_like(x)
     _load().oracle_layernorm(_p(x), _p(g), _p(b), _p(y), rows, cols, float(eps))
     return y
+
+
+def linear_bwd(X, W, dY, with_db: bool = True) -> dict:
+    """dict(dX, dW, db) of one linear shard Y = X W + b (db None unless
+    with_db): dX = dY W^T, dW = X^T dY, db = column sums of dY."""
+    X, W, dY = _f64(X), _f64(W), _f64(dY)
+    T, k = X.shape
+    k2, n = W.shape
+    assert k == k2 and dY.shape == (T, n)
+    dX = np.empty((T, k)); dW = np.empty((k, n))
+    db = np.empty(n) if with_db else None
+    _load().oracle_linear_bwd(_p(X), _p(W), _p(dY), _p(dX), _p(dW), _p(db), T, k, n)
+    return {"dX": dX, "dW": dW, "db": db}
 
 
 # ---------------------------------------------------------------- sampling

@@ -197,6 +197,43 @@ ORACLE_API void oracle_mlp_shard_bwd(const double* X, const double* W1_i, const 
     }
 }
 
+/* Backward of one linear shard Y = X W + b, the two gradients of the page
+ * "Tensor Parallelism原理与实践" §3.1 written for a single shard (the column
+ * layer's weight gradient X^T dL/dY and the input gradient dL/dY W^T) plus
+ * the bias gradient (the chain rule through the bias):
+ *   dX[m][k] = sum_j dY[m][j] W[k][j]
+ *   dW[k][j] = sum_m X[m][k] dY[m][j]
+ *   db[j]    = sum_m dY[m][j]              (db may be NULL)
+ * Shapes: X [T,in]; W [in,out]; dY [T,out]; dX [T,in]; dW [in,out]; db [out]. */
+ORACLE_API void oracle_linear_bwd(const double* X, const double* W, const double* dY,
+                                  double* dX, double* dW, double* db, int64_t T, int64_t in,
+                                  int64_t out)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < T; ++m) {
+        for (int64_t k = 0; k < in; ++k) {
+            double s = 0.0;
+            for (int64_t j = 0; j < out; ++j) s += dY[m * out + j] * W[k * out + j];
+            dX[m * in + k] = s;
+        }
+    }
+#pragma omp parallel for schedule(static)
+    for (int64_t k = 0; k < in; ++k) {
+        double* w = dW + k * out;
+        for (int64_t j = 0; j < out; ++j) w[j] = 0.0;
+        for (int64_t m = 0; m < T; ++m) {
+            const double a = X[m * in + k];
+            const double* g = dY + m * out;
+            for (int64_t j = 0; j < out; ++j) w[j] += a * g[j];
+        }
+    }
+    if (db) {
+        for (int64_t j = 0; j < out; ++j) db[j] = 0.0;
+        for (int64_t m = 0; m < T; ++m)
+            for (int64_t j = 0; j < out; ++j) db[j] += dY[m * out + j];
+    }
+}
+
 /* Stand-in for AllReduce(SUM) over t ranks [P4 §2.1, §2.2]:
  *   out[e] = parts[0][e] + parts[1][e] + ... + parts[t-1][e]   (rank order)
  * parts is [t][count] contiguous. */

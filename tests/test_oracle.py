@@ -263,6 +263,53 @@ def test_backward_adjoint_identities():
     assert abs(np.sum(g["dX"] * X) - s2) <= 1e-12 * abs(s2)
 
 
+def test_linear_backward_hand_worked():
+    # X [2,3], W [3,2], dY [2,2] small integers, worked by hand:
+    # dX = dY W^T, dW = X^T dY, db = column sums of dY.
+    X = np.array([[1., 2., 0.], [-1., 3., 2.]])
+    W = np.array([[2., -1.], [0., 1.], [1., 3.]])
+    dY = np.array([[1., -2.], [3., 1.]])
+    g = oracle.linear_bwd(X, W, dY)
+    # row 0 of dX: [1*2 + -2*-1, 1*0 + -2*1, 1*1 + -2*3] = [4, -2, -5]
+    # row 1 of dX: [3*2 + 1*-1, 3*0 + 1*1, 3*1 + 1*3] = [5, 1, 6]
+    assert np.array_equal(g["dX"], np.array([[4., -2., -5.], [5., 1., 6.]]))
+    # dW[k][j] = X[0][k] dY[0][j] + X[1][k] dY[1][j]
+    assert np.array_equal(g["dW"], np.array([[-2., -3.], [11., -1.], [6., 2.]]))
+    assert np.array_equal(g["db"], np.array([4., -1.]))
+
+
+def test_linear_backward_matches_torch_autograd_and_adjoints():
+    rng = np.random.default_rng(21)
+    T, k, n = 9, 24, 40
+    X, W, b = rng.standard_normal((T, k)), rng.standard_normal((k, n)), rng.standard_normal(n)
+    dY = rng.standard_normal((T, n))
+    tX, tW, tb = (torch.from_numpy(a).requires_grad_() for a in (X, W, b))
+    ((tX @ tW + tb) * torch.from_numpy(dY)).sum().backward()
+    g = oracle.linear_bwd(X, W, dY)
+    for a, ref in ((g["dX"], tX.grad), (g["dW"], tW.grad), (g["db"], tb.grad)):
+        ref = ref.numpy()
+        assert np.max(np.abs(a - ref)) <= 1e-13 * max(1.0, np.max(np.abs(ref)))
+    # <dW, W> = <dY, X W> = <dX, X>: a transposed operand breaks one of them
+    s = np.sum(dY * oracle.matmul(X, W))
+    assert abs(np.sum(g["dW"] * W) - s) <= 1e-12 * abs(s)
+    assert abs(np.sum(g["dX"] * X) - s) <= 1e-12 * abs(s)
+    assert oracle.linear_bwd(X, W, dY, with_db=False)["db"] is None
+
+
+def test_linear_backward_composes_the_mlp_backward():
+    # The MLP shard's weight gradients are the linear backward of each layer:
+    # the column layer with dY_i, the row layer (input H_i) with dZ.
+    X, W1, b1, W2, dZ = _mlp_inputs(T=5, h=16, ffn=24, seed=8)
+    Y, H, Z = oracle.mlp_shard_fwd(X, W1, b1, W2)
+    g = oracle.mlp_shard_bwd(X, W1, b1, W2, dZ)
+    col = oracle.linear_bwd(X, W1, g["dY"])
+    row = oracle.linear_bwd(H, W2, dZ, with_db=False)
+    assert np.allclose(col["dW"], g["dW1"], rtol=0, atol=1e-13)
+    assert np.allclose(col["dX"], g["dX"], rtol=0, atol=1e-13)
+    assert np.allclose(col["db"], g["db1"], rtol=0, atol=1e-13)
+    assert np.allclose(row["dW"], g["dW2"], rtol=0, atol=1e-13)
+
+
 def test_sampled_rows_and_cols_equal_full():
     X, W1, b1, W2, dZ = _mlp_inputs(T=10, h=16, ffn=24, seed=7)
     Y, H, Z = oracle.mlp_shard_fwd(X, W1, b1, W2)
