@@ -192,8 +192,23 @@ def attention_shard(B, aw, stream, sptr, reps=10):
                                      bf, B.TP_ACT_NONE, stream=sptr)
     proj = lambda: B.tp_row_linear(O, Wo, Z, aw.T, aw.h, aw.h, aw.t, r, bf, torch.float32,
                                    stream=sptr)
+    # backward of both projections (dX, dW, and db for QKV), from drawn
+    # output gradients
+    g = synth.make_attn_grads(aw)
+    dQ = g["dQKV"][:, synth.qkv_columns(aw, r)].contiguous().to(dev)
+    dZ = g["dZ"].to(dev)
+    f32 = torch.float32
+    dX = torch.empty(aw.T, aw.h, dtype=f32, device=dev)
+    dWq = torch.empty(aw.h, aw.qkv_width, dtype=f32, device=dev)
+    dbq = torch.empty(aw.qkv_width, dtype=f32, device=dev)
+    dO = torch.empty(aw.T, aw.w, dtype=f32, device=dev)
+    dWo = torch.empty(aw.w, aw.h, dtype=f32, device=dev)
+    qkv_bwd = lambda: B.tp_linear_bwd(X, Wqkv, dQ, dX, dWq, dbq, aw.T, aw.h, aw.qkv_width, bf,
+                                      stream=sptr)
+    proj_bwd = lambda: B.tp_linear_bwd(O, Wo, dZ, dO, dWo, None, aw.T, aw.w, aw.h, bf,
+                                       stream=sptr)
     times = []
-    for f in (qkv, proj):
+    for f in (qkv, proj, qkv_bwd, proj_bwd):
         f()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -210,7 +225,11 @@ def attention_shard(B, aw, stream, sptr, reps=10):
             "qkv_ms": round(times[0], 4), "out_proj_ms": round(times[1], 4),
             "qkv_tflops": round(aw.qkv_flops() / (times[0] * 1e-3) / 1e12, 2),
             "out_proj_tflops": round(aw.out_flops() / (times[1] * 1e-3) / 1e12, 2),
-            "tflops": round(fl / ((times[0] + times[1]) * 1e-3) / 1e12, 2)}
+            "tflops": round(fl / ((times[0] + times[1]) * 1e-3) / 1e12, 2),
+            "backward": {"what": "tp_linear_bwd of both projections: dX, dW (and db for QKV), "
+                                 "two products each",
+                         "qkv_ms": round(times[2], 4), "out_proj_ms": round(times[3], 4),
+                         "tflops": round(2 * fl / ((times[2] + times[3]) * 1e-3) / 1e12, 2)}}
 
 
 def sequence_parallel(B, stream, sptr, reps=10):

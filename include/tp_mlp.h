@@ -159,6 +159,27 @@ TP_API int tp_mlp_shard_bwd(const void* X, const void* W1_i, const void* W2_i,
                      int dtype, void* stream);
 
 /*
+ * Backward of one linear shard Y = X W (+ b), from the gradient dY of its
+ * output: the column layer's weight gradient and the input gradient of
+ * [P4 §3.1] for a single shard, plus the bias gradient:
+ *   dX = dY W^T    [tokens, in_features]           fp32
+ *   dW = X^T dY    [in_features, out_features]     fp32
+ *   db = sum over tokens of dY  [out_features]     fp32 (only if db != NULL)
+ *   X [tokens, in_features], W [in_features, out_features],
+ *   dY [tokens, out_features]                      element type `dtype`
+ * The dimensions are the shard's own: for a column shard in_features = h and
+ * out_features = n (its dX is this rank's partial, summed over ranks); for a
+ * row shard in_features = n and out_features = h.  It serves every linear
+ * layer of the path on its own (the attention projections, the column-only
+ * layer).  dW and dX also serve as scratch during the call (partial sums of
+ * db; a transposed copy of dY or X), so no output may overlap an input.
+ * tokens == 0 writes a zero dW (and db).
+ */
+TP_API int tp_linear_bwd(const void* X, const void* W, const void* dY, void* dX, void* dW,
+                         void* db, int64_t tokens, int64_t in_features, int64_t out_features,
+                         int dtype, void* stream);
+
+/*
  * Stand-in for the collective between ranks, over the t shards held on one
  * GPU.  parts is [t][tokens][cols], contiguous, element type in_dtype.
  *   TP_REDUCE_SUM    (AllReduce of row-parallel partials [P4 §2.1, §2.2]):

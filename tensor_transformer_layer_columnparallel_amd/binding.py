@@ -33,8 +33,8 @@ TP_ACT_NONE, TP_ACT_GELU_TANH = 0, 1
 TP_REDUCE_SUM, TP_REDUCE_CONCAT, TP_REDUCE_CONCAT_TOKENS = 0, 1, 2
 
 ABI_FUNCTIONS = ("tp_column_linear", "tp_row_linear", "tp_mlp_shard_fwd",
-                 "tp_mlp_shard_bwd", "tp_shard_reduce", "tp_shard_reduce_scatter",
-                 "tp_layernorm", "tp_status_string")
+                 "tp_mlp_shard_bwd", "tp_linear_bwd", "tp_shard_reduce",
+                 "tp_shard_reduce_scatter", "tp_layernorm", "tp_status_string")
 
 
 class TPError(RuntimeError):
@@ -52,6 +52,7 @@ def load_library() -> ctypes.CDLL:
     lib.tp_row_linear.argtypes = [vp, vp, vp, i64, i64, i64, ci, ci, ci, ci, vp]
     lib.tp_mlp_shard_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, ci, ci, ci, vp]
     lib.tp_mlp_shard_bwd.argtypes = [vp] * 11 + [i64, i64, i64, ci, ci, ci, vp]
+    lib.tp_linear_bwd.argtypes = [vp] * 6 + [i64, i64, i64, ci, vp]
     lib.tp_shard_reduce.argtypes = [vp, vp, i64, i64, ci, ci, ci, ci, vp]
     lib.tp_shard_reduce_scatter.argtypes = [vp, vp, i64, i64, ci, ci, ci, ci, vp]
     lib.tp_layernorm.argtypes = [vp, vp, vp, vp, i64, i64, ctypes.c_float, ci, ci, vp]
@@ -173,6 +174,18 @@ def tp_mlp_shard_bwd(X, W1_i, W2_i, Y_i, H_i, dZ, dY_i, dW2_i, dW1_i, dX_i, db1_
                                _ptr(db1_i, "db1_i", TP_F32, n),
                                tokens, h, ffn, t, rank, dt, _stream(stream))
     return _ret("tp_mlp_shard_bwd", st, check)
+
+
+def tp_linear_bwd(X, W, dY, dX, dW, db, tokens, in_features, out_features, dtype, stream=None,
+                  check=True) -> int:
+    dt = _dt(dtype)
+    Tk, Tn, kn = (_prod(tokens, in_features), _prod(tokens, out_features),
+                  _prod(in_features, out_features))
+    st = _lib.tp_linear_bwd(_ptr(X, "X", dt, Tk), _ptr(W, "W", dt, kn), _ptr(dY, "dY", dt, Tn),
+                            _ptr(dX, "dX", TP_F32, Tk), _ptr(dW, "dW", TP_F32, kn),
+                            _ptr(db, "db", TP_F32, out_features), tokens, in_features,
+                            out_features, dt, _stream(stream))
+    return _ret("tp_linear_bwd", st, check)
 
 
 def tp_shard_reduce(parts, out, tokens, cols, t, op, in_dtype, out_dtype, stream=None,

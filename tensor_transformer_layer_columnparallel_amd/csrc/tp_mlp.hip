@@ -255,6 +255,53 @@ int tp_mlp_shard_bwd(const void* X, const void* W1_i, const void* W2_i, const vo
     return TP_OK;
 }
 
+int tp_linear_bwd(const void* X, const void* W, const void* dY, void* dX, void* dW, void* db,
+                  int64_t tokens, int64_t in_features, int64_t out_features, int dtype,
+                  void* stream)
+{
+    if (!valid_dtype(dtype)) return TP_ERR_DTYPE;
+    int st = check_ptrs({X, W, dY, dX, dW}, {db});
+    if (st) return st;
+    if (tokens < 0 || !feature_dim_ok(in_features) || !feature_dim_ok(out_features))
+        return TP_ERR_SHAPE;
+    const int64_t k = in_features, n = out_features;
+    const int es = elt_size(dtype);
+    if (!fits(tokens, k, es) || !fits(k, n, es) || !fits(tokens, n, es) || !fits(tokens, k, 4) ||
+        !fits(k, n, 4))
+        return TP_ERR_SHAPE;
+    const Elt e = to_elt(dtype);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t err;
+    // db = column sums of dY, with dW (written only afterwards) as scratch for
+    // the partial sums.
+    if (db && (err = column_sum(dY, static_cast<float*>(db), tokens, n, e, dW, k * n * 4, s)) !=
+                  hipSuccess)
+        return TP_ERR_HIP;
+    // dW = X^T dY.  Both operands are M/N-contiguous; with bf16 and whole
+    // 32-deep slabs of tokens the smaller activation is transposed into dX's
+    // memory (written last) first, so that the tile kernel reads a
+    // K-contiguous first operand: dW^T = (dY^T) X stored transposed when
+    // out <= in, else (X^T) dY.
+    const bool slabs = e == Elt::BF16 && tokens > 0 && tokens % 32 == 0;
+    if (slabs && n <= k && ring_path(n, k, tokens, e, Layout::NN)) {
+        if ((err = transpose16(dY, dX, tokens, n, s)) != hipSuccess ||
+            (err = run_gemm(dX, X, dW, nullptr, nullptr, nullptr, n, k, tokens, e, Layout::NN,
+                            Epi::StoreT, Elt::F32, s)) != hipSuccess)
+            return TP_ERR_HIP;
+    } else if (slabs && ring_path(k, n, tokens, e, Layout::NN)) {
+        if ((err = transpose16(X, dX, tokens, k, s)) != hipSuccess ||
+            (err = run_gemm(dX, dY, dW, nullptr, nullptr, nullptr, k, n, tokens, e, Layout::NN,
+                            Epi::Store, Elt::F32, s)) != hipSuccess)
+            return TP_ERR_HIP;
+    } else if ((err = run_gemm(X, dY, dW, nullptr, nullptr, nullptr, k, n, tokens, e, Layout::TN,
+                               Epi::Store, Elt::F32, s)) != hipSuccess) {
+        return TP_ERR_HIP;
+    }
+    // dX = dY W^T: W [k][n] is the K-contiguous [N][K] operand.
+    return status_of(run_gemm(dY, W, dX, nullptr, nullptr, nullptr, tokens, k, n, e, Layout::NT,
+                              Epi::Store, Elt::F32, s));
+}
+
 int tp_shard_reduce(const void* parts, void* out, int64_t tokens, int64_t cols, int t, int op,
                     int in_dtype, int out_dtype, void* stream)
 {

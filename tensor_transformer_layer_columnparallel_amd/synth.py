@@ -24,6 +24,7 @@ from .configs import AttnWorkload, Workload
 
 TAG_X, TAG_W1, TAG_B1, TAG_W2, TAG_DZ = 1, 2, 3, 4, 5
 TAG_WQKV, TAG_BQKV, TAG_O, TAG_WO = 6, 7, 8, 9
+TAG_DQKV, TAG_DZO = 10, 11
 
 
 def _gen(seed: int, tag: int, rank: int = 0) -> torch.Generator:
@@ -80,6 +81,15 @@ def make_attn_inputs(aw: AttnWorkload, seed: int = 0) -> dict:
             "bqkv": draw((3 * h,), aw.std_w, seed, TAG_BQKV, 0, dt),
             "O": draw((aw.T, h), 1.0, seed, TAG_O, 0, dt),
             "Wo": draw((h, h), aw.std_w, seed, TAG_WO, 0, dt)}
+
+
+def make_attn_grads(aw: AttnWorkload, seed: int = 0) -> dict:
+    """Output gradients for the attention projections' backward, unsharded:
+    ``{"dQKV": [T,3h] (of [Q | K | V]), "dZ": [T,h] (of the output
+    projection)}``, drawn N(0, 1) and rounded once like the activations."""
+    dt = torch.float32 if aw.dtype == "f32" else torch.bfloat16
+    return {"dQKV": draw((aw.T, 3 * aw.h), 1.0, seed, TAG_DQKV, 0, dt),
+            "dZ": draw((aw.T, aw.h), 1.0, seed, TAG_DZO, 0, dt)}
 
 
 def qkv_columns(aw: AttnWorkload, r: int) -> torch.Tensor:

@@ -36,7 +36,8 @@ def Bfake(B):
 def test_header_declares_the_entry_points_and_status_string():
     assert set(_declared_functions()) == {
         "tp_column_linear", "tp_row_linear", "tp_mlp_shard_fwd", "tp_mlp_shard_bwd",
-        "tp_shard_reduce", "tp_shard_reduce_scatter", "tp_layernorm", "tp_status_string"}
+        "tp_linear_bwd", "tp_shard_reduce", "tp_shard_reduce_scatter", "tp_layernorm",
+        "tp_status_string"}
 
 
 def test_library_exports_every_declared_symbol(B):
@@ -116,6 +117,22 @@ def test_mlp_fwd_bwd_reject(Bfake):
     assert bwd(db1_i=MIS) == B.TP_ERR_ALIGN
     assert bwd(rank=8) == B.TP_ERR_RANK
     assert bwd(h=60) == B.TP_ERR_SHAPE
+
+
+def test_linear_bwd_rejects(Bfake):
+    B = Bfake
+    f = lambda **kw: B.tp_linear_bwd(**{**dict(
+        X=P, W=P, dY=P, dX=P2, dW=P2, db=None, tokens=32, in_features=768, out_features=256,
+        dtype=B.TP_BF16, stream=0, check=False), **kw})
+    assert f(X=None) == B.TP_ERR_NULL
+    assert f(dW=None) == B.TP_ERR_NULL
+    assert f(db=MIS) == B.TP_ERR_ALIGN
+    assert f(dY=MIS) == B.TP_ERR_ALIGN
+    assert f(in_features=770) == B.TP_ERR_SHAPE
+    assert f(out_features=0) == B.TP_ERR_SHAPE
+    assert f(tokens=-1) == B.TP_ERR_SHAPE
+    assert f(tokens=1 << 20, in_features=1 << 10) == B.TP_ERR_SHAPE   # dX over 2^31 bytes
+    assert f(dtype=7) == B.TP_ERR_DTYPE
 
 
 def test_shard_reduce_rejects(Bfake):

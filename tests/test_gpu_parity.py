@@ -211,6 +211,83 @@ def test_attention_gpt3_shard_sampled(B):
                  f"{aw.name} out-proj rows")
 
 
+LINEAR_BWD = [
+    # (T, in, out): the weight gradient's path on the device
+    (300, 264, 200),   # T % 32 != 0: the tile kernel's TN layout (both operands transposed in LDS)
+    (288, 512, 384),   # out <= in: dY^T, product stored transposed
+    (288, 384, 768),   # out > in: X^T
+    (256, 192, 192),   # below a tile in M: the general kernel
+    (64, 136, 520),
+    (33, 96, 64),
+]
+
+
+@pytest.mark.parametrize("shape", LINEAR_BWD, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_linear_bwd_matches_oracle(B, shape, dt):
+    T, k, n = shape
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    _log(f"case linear bwd {shape} {dt}")
+    X = synth.draw((T, k), 1.0, 3, synth.TAG_X, 0, tdt)
+    W = synth.draw((k, n), 0.02, 3, synth.TAG_W1, 0, tdt)
+    dY = synth.draw((T, n), 1.0, 3, synth.TAG_DZ, 0, tdt)
+    dX = torch.full((T, k), float("nan"), device="cuda")
+    dW = torch.full((k, n), float("nan"), device="cuda")
+    db = torch.full((n,), float("nan"), device="cuda")
+    B.tp_linear_bwd(dev(X), dev(W), dev(dY), dX, dW, db, T, k, n, tdt)
+    torch.cuda.synchronize()
+    g = oracle.linear_bwd(X, W, dY)
+    for name, got in (("dX", dX), ("dW", dW), ("db", db)):
+        assert_close(got, g[name], dt, f"linear bwd {shape} {dt} {name}")
+
+
+def test_linear_bwd_empty_tokens(B):
+    k, n = 64, 128
+    ph = torch.empty(8, dtype=torch.bfloat16, device="cuda")   # [0, *] arrays have no storage
+    phf = torch.empty(8, dtype=torch.float32, device="cuda")
+    W = torch.randn(k, n, device="cuda").bfloat16()
+    dW = torch.full((k, n), 7.0, device="cuda")
+    db = torch.full((n,), 7.0, device="cuda")
+    B.tp_linear_bwd(ph, W, ph, phf, dW, db, 0, k, n, B.TP_BF16)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(dW) == 0 and torch.count_nonzero(db) == 0
+
+
+def test_attention_gpt3_backward_sampled(B):
+    """Backward of rank 3's GPT-3-shaped attention projections (QKV on head
+    boundaries: out <= in, dY^T path; output projection: out > in, X^T path)
+    on sampled rows of dX and columns of dW / db.  Rows of dX depend only on
+    the same rows of dY, and columns of dW and db only on the same columns of
+    dY (and of W), so the oracle runs on those subsets."""
+    aw = configs.ATTN_GPT3
+    r = aw.ranks[0]
+    T, h, w = aw.T, aw.h, aw.w
+    _log(f"case {aw.name} backward rank {r}")
+    d = synth.make_attn_inputs(aw)
+    s = synth.attn_shard(aw, d, r)
+    gr = synth.make_attn_grads(aw)
+    dQ = gr["dQKV"][:, synth.qkv_columns(aw, r)].contiguous()
+    n = 3 * w
+    dX = torch.empty(T, h, device="cuda"); dW = torch.empty(h, n, device="cuda")
+    db = torch.empty(n, device="cuda")
+    B.tp_linear_bwd(dev(d["X"]), dev(s["Wqkv"]), dev(dQ), dX, dW, db, T, h, n, B.TP_BF16)
+    dO = torch.empty(T, w, device="cuda"); dWo = torch.empty(w, h, device="cuda")
+    B.tp_linear_bwd(dev(s["O"]), dev(s["Wo"]), dev(gr["dZ"]), dO, dWo, None, T, w, h, B.TP_BF16)
+    torch.cuda.synchronize()
+    rows = sample_indices(T, 4, seed=9)
+    cq, co = sample_indices(n, 5, seed=10), sample_indices(h, 5, seed=11)
+    _log(f"case {aw.name} backward rows {rows.tolist()} cols {cq.tolist()} {co.tolist()}")
+    g = oracle.linear_bwd(d["X"][rows], s["Wqkv"], dQ[rows], with_db=False)
+    assert_close(dX[rows], g["dX"], "bf16", "QKV dX rows")
+    g = oracle.linear_bwd(d["X"], s["Wqkv"][:, cq], dQ[:, cq])
+    assert_close(dW[:, cq], g["dW"], "bf16", "QKV dW cols")
+    assert_close(db[cq], g["db"], "bf16", "QKV db")
+    g = oracle.linear_bwd(s["O"][rows], s["Wo"], gr["dZ"][rows], with_db=False)
+    assert_close(dO[rows], g["dX"], "bf16", "out-proj dO rows")
+    g = oracle.linear_bwd(s["O"], s["Wo"][:, co], gr["dZ"][:, co], with_db=False)
+    assert_close(dWo[:, co], g["dW"], "bf16", "out-proj dW cols")
+
+
 def test_row_partials_in_bf16_then_summed_in_fp32(B):
     # Low-precision exchange (page "Tensor Parallelism原理与实践" §4.1 keeps fp32
     # for the reduction itself): each rank's row-parallel partial stored as
