@@ -25,19 +25,21 @@
 //   2. passes a barrier: slab k+1 is in LDS for everybody and nobody reads
 //      slab k's buffers any more;
 //   3. in four groups, each with a share of the DMA instructions, the MFMAs
-//      of a quarter of the A fragments and a share of the fragment reads:
-//      refills the
-//      freed buffers (5 slabs ahead, or half of the 64-k unit 2-3 slabs
-//      ahead), multiplies slab k (fragments read during slab k-1) and reads
-//      the fragments of slab k+1.
+//      of a quarter of the A fragments and (in the first three groups) a
+//      share of the fragment reads: refills the freed buffers (5 slabs ahead,
+//      or half of the 64-k unit 2-3 slabs ahead), multiplies slab k
+//      (fragments read during slab k-1) and reads the fragments of slab k+1.
 // Spreading the memory instructions over the MFMAs keeps the waves of a SIMD
 // from stalling together on a burst of loads while the matrix pipe idles.
 // Loads of elements outside the operands (ragged M/N tails, k past K) use a
 // per-lane offset of 2^31, beyond any operand, which the buffer descriptor
 // turns into zeros without touching memory.
 // Plain fp32 results are staged through the (then free) LDS ring so that the
-// stores to HBM cover whole row segments; other results are stored from the
-// registers, four consecutive columns per lane.
+// stores to HBM cover whole row segments (transposed on the way, for a
+// result stored as C^T); other results are stored from the registers, four
+// consecutive columns per lane.  The GeLU' epilogue can also sum its fp32
+// results per column in a fixed order (one row of partials per 256-row
+// block), the bias gradient's first step.
 //
 // LDS layouts (16-byte chunks permuted per row for conflict-free reads):
 //   K-major 64-k unit [256][64 k]: chunk c of row r at c ^ swz8(r);
