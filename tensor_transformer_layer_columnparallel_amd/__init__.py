@@ -9,18 +9,11 @@ generator can be used on a machine where the library has not been built.
 """
 from __future__ import annotations
 
-_ABI_NAMES = (
-    "tp_column_linear",
-    "tp_row_linear",
-    "tp_mlp_shard_fwd",
-    "tp_mlp_shard_bwd",
-    "tp_shard_reduce",
-    "tp_status_string",
-)
-
 
 def __getattr__(name):
-    if name in _ABI_NAMES or name in ("binding", "TPError", "load_library"):
+    # every entry point (tp_*), constant (TP_*) and helper of the binding
+    if name.startswith(("tp_", "TP_")) or name in ("binding", "TPError", "load_library",
+                                                    "ABI_FUNCTIONS"):
         import importlib
         binding = importlib.import_module(__name__ + ".binding")
         return binding if name == "binding" else getattr(binding, name)

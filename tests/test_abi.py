@@ -46,6 +46,14 @@ def test_library_exports_every_declared_symbol(B):
         assert hasattr(lib, name), name
 
 
+def test_package_exposes_every_entry_point(B):
+    import tensor_transformer_layer_columnparallel_amd as pkg
+    for name in _declared_functions():
+        assert name in B.ABI_FUNCTIONS, name
+        assert callable(getattr(pkg, name)), name
+    assert pkg.TP_REDUCE_CONCAT_TOKENS == 2 and pkg.TP_BF16 == 1
+
+
 def test_status_strings(B):
     for st in range(0, -9, -1):
         assert B.tp_status_string(st) and B.tp_status_string(st) != "unknown status"
