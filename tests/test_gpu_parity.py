@@ -501,6 +501,35 @@ def test_step_captured_in_a_hip_graph_replays_bit_identical(B):
             assert torch.equal(o, e), f"replay {rep}: {name} differs from the eager run"
 
 
+def test_two_ranks_concurrently_on_two_streams_match_serial(B):
+    # The library keeps no state between or during calls (its scratch is the
+    # caller's outputs), so two shards' forward + backward in flight at once
+    # on two streams must give the bytes of the serial runs.
+    w = configs.scaled(configs.GPT3_SHARD, "two_streams", T=288, h=544, ffn=2304, t=8,
+                       ranks=(0, 5))
+    _log(f"case {w.name}: serial, then concurrent on two streams")
+    d = to_device(synth.make_inputs(w))
+    serial = {}
+    for r in w.ranks:
+        Y, H, Z = gpu_shard_fwd(B, w, d, r)
+        serial[r] = (Y, H, Z, gpu_shard_bwd(B, w, d, r, Y, H))
+    torch.cuda.synchronize()
+    streams = {r: torch.cuda.Stream() for r in w.ranks}
+    conc = {}
+    for _ in range(2):
+        for r in w.ranks:
+            with torch.cuda.stream(streams[r]):
+                Y, H, Z = gpu_shard_fwd(B, w, d, r, stream=streams[r])
+                conc[r] = (Y, H, Z, gpu_shard_bwd(B, w, d, r, Y, H, stream=streams[r]))
+        torch.cuda.synchronize()
+        for r in w.ranks:
+            (Ys, Hs, Zs, gs), (Yc, Hc, Zc, gc) = serial[r], conc[r]
+            for name, a, b in (("Y", Ys, Yc), ("H", Hs, Hc), ("Z", Zs, Zc)):
+                assert torch.equal(a, b), f"rank {r}: {name} differs"
+            for k in ("dY", "dW2", "dW1", "dX", "db1"):
+                assert torch.equal(gs[k], gc[k]), f"rank {r}: {k} differs"
+
+
 def test_all_ones_and_identity(B):
     _log("case all-ones / identity")
     T, h, n = 64, 768, 256
