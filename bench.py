@@ -129,6 +129,54 @@ def copy_calibration(reps: int):
     log(f"copy calibration: {reps} copies of {COPY_ROWS * COPY_COLS * 4} bytes")
 
 
+def warm(fn, ms: float = 80.0):
+    """Calls fn back to back for about `ms` milliseconds of device time, so
+    that the measurement after it starts at the sustained engine clock."""
+    import torch
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(4):
+            fn()
+        torch.cuda.synchronize()
+
+
+def trace_summary(trace_dir: str, last: int):
+    """Markdown table of kernel durations (microseconds) from the
+    *kernel_trace.csv that rocprofv3 --kernel-trace writes under trace_dir:
+    calls, mean, min and max over all dispatches of each kernel, and calls and
+    mean inside the timed steps.  The timed steps are the window from the
+    start of the column GEMM's `last`-th dispatch from the end to 3 ms after
+    its final one (the rest of that step)."""
+    import csv
+    import glob
+    runs = {}
+    for path in glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True):
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                t0, t1 = int(row["Start_Timestamp"]), int(row["End_Timestamp"])
+                runs.setdefault(row["Kernel_Name"], []).append((t0, (t1 - t0) / 1e3))
+    if not runs:
+        raise SystemExit(f"no kernel trace under {trace_dir}")
+    col = [v for k, v in runs.items()
+           if any(all(x in k for x in key) for key in COLUMN_KERNEL_KEYS)]
+    if len(col) != 1:
+        raise SystemExit("the column GEMM kernel is not in the trace exactly once")
+    col = sorted(col[0])
+    w0, w1 = col[-last][0], col[-1][0] + 3_000_000
+    rows = []
+    for name, v in runs.items():
+        ds = [d for _, d in v]
+        tw = [d for t, d in v if w0 <= t <= w1]
+        rows.append((sum(ds), name, len(ds), sum(ds) / len(ds), min(ds), max(ds), len(tw),
+                     sum(tw) / len(tw) if tw else float("nan")))
+    rows.sort(reverse=True)
+    print(f"| kernel | calls | mean us | min us | max us | calls in the timed steps | mean us in the timed steps |")
+    print("|---|---|---|---|---|---|---|")
+    for _, name, c, mean, mn, mx, nt, tmean in rows:
+        short = name if len(name) <= 90 else name[:87] + "..."
+        print(f"| `{short}` | {c} | {mean:.1f} | {mn:.1f} | {mx:.1f} | {nt} | {tmean:.1f} |")
+
+
 def max_engine_clock_mhz():
     """The GPU agent's maximum engine clock as rocminfo reports it (None if
     rocminfo is unavailable)."""
@@ -158,9 +206,7 @@ def vendor_matmul_context(T, h, n, reps=10):
     X, W1, H, W2, dZ, dY = r(T, h), r(h, n), r(T, n), r(n, h), r(T, h), r(T, n)
     prods = [lambda: X @ W1, lambda: H @ W2, lambda: dZ @ W2.t(), lambda: H.t() @ dZ,
              lambda: X.t() @ dY, lambda: dY @ W1.t()]
-    for f in prods:
-        f()
-    torch.cuda.synchronize()
+    warm(lambda: [f() for f in prods])
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(reps):
@@ -209,8 +255,7 @@ def attention_shard(B, aw, stream, sptr, reps=10):
                                        stream=sptr)
     times = []
     for f in (qkv, proj, qkv_bwd, proj_bwd):
-        f()
-        torch.cuda.synchronize()
+        warm(f)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for _ in range(reps):
@@ -264,8 +309,7 @@ def sequence_parallel(B, stream, sptr, reps=10):
                        f"{Tr} tokens; layer norm of the shard (fp32 -> bf16); token "
                        f"AllGather of {t} bf16 shards", "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     for name, (f, nbytes) in ops.items():
-        f()
-        torch.cuda.synchronize()
+        warm(f)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for _ in range(reps):
@@ -309,8 +353,12 @@ def cpu_baseline(w, d_h, seconds: float):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    # The engine clock needs about 25 ms of sustained load to settle: the
+    # first launches run at a boost clock, the next ones dip well below the
+    # sustained clock while the power control catches up.  40 warm-up steps
+    # (about 70 ms) put the timed steps in the sustained state.
+    ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="wall-clock budget of the oracle baseline (0 disables it)")
     ap.add_argument("--no-reduce", action="store_true", help="skip the shard-sum measurement")
@@ -326,7 +374,13 @@ def main():
                     metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                     help="turn rocprofv3 --pmc CSV output into the stored traffic figure")
     ap.add_argument("--counter-commands", default="", help="commands recorded with the counters")
+    ap.add_argument("--trace-summary", nargs=2, metavar=("TRACE_DIR", "LAST"),
+                    help="per-kernel durations from a rocprofv3 --kernel-trace CSV: over all "
+                         "dispatches and over each kernel's LAST dispatches")
     args = ap.parse_args()
+    if args.trace_summary:
+        trace_summary(args.trace_summary[0], int(args.trace_summary[1]))
+        return
     if args.ingest_counters:
         ingest_counters(*args.ingest_counters, commands=args.counter_commands)
         return
@@ -464,8 +518,7 @@ def main():
             def call():
                 B.tp_shard_reduce(parts, Zs, wr.T, wr.h, wr.t, B.TP_REDUCE_SUM, parts.dtype,
                                   torch.float32, stream=sptr)
-            for _ in range(2):
-                call()
+            warm(call)
             reps = 10
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             torch.cuda.synchronize()
