@@ -140,13 +140,15 @@ def warm(fn, ms: float = 80.0):
         torch.cuda.synchronize()
 
 
-def trace_summary(trace_dir: str, last: int):
+def trace_summary(trace_dir: str, warmup: int, steps: int):
     """Markdown table of kernel durations (microseconds) from the
-    *kernel_trace.csv that rocprofv3 --kernel-trace writes under trace_dir:
-    calls, mean, min and max over all dispatches of each kernel, and calls and
-    mean inside the timed steps.  The timed steps are the window from the
-    start of the column GEMM's `last`-th dispatch from the end to 3 ms after
-    its final one (the rest of that step)."""
+    *kernel_trace.csv that rocprofv3 --kernel-trace writes under trace_dir
+    for a bench run with `warmup` warm-up and `steps` timed steps: calls,
+    mean, min and max over all dispatches of each kernel, and calls and mean
+    inside the timed steps.  The step loop runs first, one column GEMM per
+    step, so the timed steps are the window from the start of the column
+    GEMM's dispatch number `warmup` (from 0) to 3 ms after the start of
+    number `warmup + steps - 1` (the rest of that step)."""
     import csv
     import glob
     runs = {}
@@ -162,7 +164,9 @@ def trace_summary(trace_dir: str, last: int):
     if len(col) != 1:
         raise SystemExit("the column GEMM kernel is not in the trace exactly once")
     col = sorted(col[0])
-    w0, w1 = col[-last][0], col[-1][0] + 3_000_000
+    if len(col) < warmup + steps:
+        raise SystemExit("fewer column GEMM dispatches than warm-up + timed steps")
+    w0, w1 = col[warmup][0], col[warmup + steps - 1][0] + 3_000_000
     rows = []
     for name, v in runs.items():
         ds = [d for _, d in v]
@@ -322,6 +326,53 @@ def sequence_parallel(B, stream, sptr, reps=10):
     return out
 
 
+def full_layer(B, stream, sptr, reps=5):
+    """The full-layer emulation (h = 8192, ffn = 28672, t = 8, 4096 tokens,
+    no bias): every rank's shard forward, then the fp32 shard sum, once with
+    one tp_mlp_shard_fwd call per rank in rank order and once with all
+    shards batched into two launches (tp_mlp_layer_fwd).  Seeded random
+    inputs drawn on the device (same distributions as the parity cases)."""
+    import torch
+    from tensor_transformer_layer_columnparallel_amd import configs
+    w = configs.FULL_LAYER_8
+    T, h, n, t = w.T, w.h, w.n, w.t
+    bf, f32 = torch.bfloat16, torch.float32
+    g = torch.Generator(device="cuda").manual_seed(0)
+    X = torch.randn(T, h, device="cuda", generator=g).to(bf)
+    W1 = (torch.randn(t, h, n, device="cuda", generator=g) * w.std_w).to(bf)
+    W2 = (torch.randn(t, n, h, device="cuda", generator=g) * w.std_w).to(bf)
+    H = torch.empty(t, T, n, dtype=bf, device="cuda")
+    parts = torch.empty(t, T, h, dtype=f32, device="cuda")
+    Z = torch.empty(T, h, dtype=f32, device="cuda")
+
+    def seq():
+        for r in range(t):
+            B.tp_mlp_shard_fwd(X, W1[r], None, W2[r], H[r], None, parts[r], T, h, w.ffn, t, r,
+                               bf, stream=sptr)
+        B.tp_shard_reduce(parts, Z, T, h, t, B.TP_REDUCE_SUM, f32, f32, stream=sptr)
+
+    def batched():
+        B.tp_mlp_layer_fwd(X, W1, None, W2, H, None, parts, T, h, w.ffn, t, bf, stream=sptr)
+        B.tp_shard_reduce(parts, Z, T, h, t, B.TP_REDUCE_SUM, f32, f32, stream=sptr)
+
+    out = {"workload": f"full-layer emulation, h={h}, ffn={w.ffn}, t={t}, {T} tokens, no bias: "
+                       f"every shard's forward, then the fp32 shard sum",
+           "flops": w.fwd_flops()}
+    for name, f in (("sequential", seq), ("batched", batched)):
+        warm(f)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            f()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        out[name] = {"ms": round(ms, 4), "tflops": round(w.fwd_flops() / (ms * 1e-3) / 1e12, 2)}
+    out["sequential"]["what"] = "tp_mlp_shard_fwd per rank in rank order, then tp_shard_reduce"
+    out["batched"]["what"] = "tp_mlp_layer_fwd (all shards in two launches), then tp_shard_reduce"
+    return out
+
+
 def cpu_baseline(w, d_h, seconds: float):
     """Times the fp64 oracle on a bounded sample: chunks of 32 token rows of
     the same workload, each chunk a full forward + backward (6 products) of
@@ -366,6 +417,8 @@ def main():
                     help="skip the sequence-parallel stand-ins")
     ap.add_argument("--no-attention", action="store_true",
                     help="skip the attention-projection measurement")
+    ap.add_argument("--no-full-layer", action="store_true",
+                    help="skip the full-layer emulation (h = 8192, 8 shards + shard sum)")
     ap.add_argument("--no-vendor", action="store_true",
                     help="skip the vendor-BLAS context timing (torch.matmul)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="REPS",
@@ -374,12 +427,14 @@ def main():
                     metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                     help="turn rocprofv3 --pmc CSV output into the stored traffic figure")
     ap.add_argument("--counter-commands", default="", help="commands recorded with the counters")
-    ap.add_argument("--trace-summary", nargs=2, metavar=("TRACE_DIR", "LAST"),
-                    help="per-kernel durations from a rocprofv3 --kernel-trace CSV: over all "
-                         "dispatches and over each kernel's LAST dispatches")
+    ap.add_argument("--trace-summary", nargs=3, metavar=("TRACE_DIR", "WARMUP", "STEPS"),
+                    help="per-kernel durations from a rocprofv3 --kernel-trace CSV of a bench "
+                         "run with these warm-up and timed step counts: over all dispatches "
+                         "and inside the timed steps")
     args = ap.parse_args()
     if args.trace_summary:
-        trace_summary(args.trace_summary[0], int(args.trace_summary[1]))
+        trace_summary(args.trace_summary[0], int(args.trace_summary[1]),
+                      int(args.trace_summary[2]))
         return
     if args.ingest_counters:
         ingest_counters(*args.ingest_counters, commands=args.counter_commands)
@@ -503,6 +558,12 @@ def main():
         log("sequence parallel: " + ", ".join(f"{k} {sp[k]['ms']:.4f} ms {sp[k]['achieved']:.0f} GB/s"
                                               for k in ("reduce_scatter", "layernorm",
                                                         "concat_tokens")))
+
+    if not args.no_full_layer:
+        out["full_layer"] = full_layer(B, stream, sptr)
+        fl = out["full_layer"]
+        log(f"full layer: sequential {fl['sequential']['ms']:.3f} ms, batched "
+            f"{fl['batched']['ms']:.3f} ms ({fl['batched']['tflops']:.0f} TFLOP/s)")
 
     if not args.no_vendor:
         out["context_vendor_matmul"] = vendor_matmul_context(T, h, n)

@@ -131,6 +131,32 @@ TP_API int tp_mlp_shard_fwd(const void* X, const void* W1_i, const void* b1_i, c
                      int dtype, void* stream);
 
 /*
+ * Forward of every rank's MLP shard of one layer on this device, the t
+ * shards' products batched into two launches (all column products, then all
+ * row products) [P2 "核心工作机制"; P4 §2.1 (the layer output is the sum of
+ * the t partials)].  For r = 0 .. t-1 it computes exactly what
+ * tp_mlp_shard_fwd(rank = r) computes, bit for bit:
+ *   Y_r = X W1[r] + b1[r] ;  H[r] = g(Y_r) ;  Z[r] = H[r] W2[r]
+ * Buffers hold the shards stacked rank by rank (rank r's block at offset
+ * r * <block size>), the layout tp_shard_reduce takes:
+ *   X      [tokens, h]            shared by every rank
+ *   W1     [t][h][n]    b1 [t][n] or NULL     W2 [t][n][h]
+ *   H      [t][tokens][n]   (required; output and the row products' input)
+ *   Y_save [t][tokens][n] or NULL (pre-activations, for the backward)
+ *   Z      [t][tokens][h]   fp32 partial outputs; tp_shard_reduce with
+ *                           TP_REDUCE_SUM adds them into the layer output
+ * with n = ffn / t.  X, W1, b1, W2, H, Y_save have element type `dtype`.
+ * Errors as tp_mlp_shard_fwd (t < 1 -> TP_ERR_RANK); each rank's block
+ * must be smaller than 2^31 bytes.  Batching lets the tiles of all shards
+ * share the GPU: a shard whose output is not a whole number of tile waves
+ * (h = 8192, n = 3584: 304 tiles for 256 compute units) no longer leaves
+ * most of a second wave idle.
+ */
+TP_API int tp_mlp_layer_fwd(const void* X, const void* W1, const void* b1, const void* W2,
+                            void* H, void* Y_save, void* Z, int64_t tokens, int64_t h,
+                            int64_t ffn, int t, int dtype, void* stream);
+
+/*
  * Backward of one MLP shard from the full output gradient dZ (replicated on
  * every rank) and the forward's saved Y_i, H_i [P4 §3.1; P1]:
  *   dY_i  = (dZ W2_i^T) * g'(Y_i)      elementwise product

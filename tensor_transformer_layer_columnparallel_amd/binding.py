@@ -33,7 +33,7 @@ TP_ACT_NONE, TP_ACT_GELU_TANH = 0, 1
 TP_REDUCE_SUM, TP_REDUCE_CONCAT, TP_REDUCE_CONCAT_TOKENS = 0, 1, 2
 
 ABI_FUNCTIONS = ("tp_column_linear", "tp_row_linear", "tp_mlp_shard_fwd",
-                 "tp_mlp_shard_bwd", "tp_linear_bwd", "tp_shard_reduce",
+                 "tp_mlp_layer_fwd", "tp_mlp_shard_bwd", "tp_linear_bwd", "tp_shard_reduce",
                  "tp_shard_reduce_scatter", "tp_layernorm", "tp_status_string")
 
 
@@ -51,6 +51,7 @@ def load_library() -> ctypes.CDLL:
     lib.tp_column_linear.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, ci, ci, ci, ci, ci, vp]
     lib.tp_row_linear.argtypes = [vp, vp, vp, i64, i64, i64, ci, ci, ci, ci, vp]
     lib.tp_mlp_shard_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, ci, ci, ci, vp]
+    lib.tp_mlp_layer_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, ci, ci, vp]
     lib.tp_mlp_shard_bwd.argtypes = [vp] * 11 + [i64, i64, i64, ci, ci, ci, vp]
     lib.tp_linear_bwd.argtypes = [vp] * 6 + [i64, i64, i64, ci, vp]
     lib.tp_shard_reduce.argtypes = [vp, vp, i64, i64, ci, ci, ci, ci, vp]
@@ -160,6 +161,23 @@ def tp_mlp_shard_fwd(X, W1_i, b1_i, W2_i, H_i, Y_i_save, Z_i, tokens, h, ffn, t,
                                _ptr(Z_i, "Z_i", TP_F32, _prod(tokens, h)),
                                tokens, h, ffn, t, rank, dt, _stream(stream))
     return _ret("tp_mlp_shard_fwd", st, check)
+
+
+def tp_mlp_layer_fwd(X, W1, b1, W2, H, Y_save, Z, tokens, h, ffn, t, dtype, stream=None,
+                     check=True) -> int:
+    """Every rank's shard forward at once; W1 [t][h][n], b1 [t][n], W2 [t][n][h],
+    H and Y_save [t][tokens][n], Z [t][tokens][h] (fp32)."""
+    dt, n = _dt(dtype), _split(ffn, t)
+    tt = t if t > 0 else -1
+    st = _lib.tp_mlp_layer_fwd(_ptr(X, "X", dt, _prod(tokens, h)),
+                               _ptr(W1, "W1", dt, _prod(tt, h, n)),
+                               _ptr(b1, "b1", dt, _prod(tt, n)),
+                               _ptr(W2, "W2", dt, _prod(tt, n, h)),
+                               _ptr(H, "H", dt, _prod(tt, tokens, n)),
+                               _ptr(Y_save, "Y_save", dt, _prod(tt, tokens, n)),
+                               _ptr(Z, "Z", TP_F32, _prod(tt, tokens, h)),
+                               tokens, h, ffn, t, dt, _stream(stream))
+    return _ret("tp_mlp_layer_fwd", st, check)
 
 
 def tp_mlp_shard_bwd(X, W1_i, W2_i, Y_i, H_i, dZ, dY_i, dW2_i, dW1_i, dX_i, db1_i, tokens, h,

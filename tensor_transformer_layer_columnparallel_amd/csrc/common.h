@@ -54,6 +54,12 @@ struct GemmArgs {
     // DGelu, tile kernel only: column sums of C over each 256-row block of
     // tiles, fp32 [ceil(M / 256)][N], summed in a fixed order; may be null.
     float* colsum;
+    // `batch` independent products of this shape in one launch, product b
+    // reading A + b sA, B + b sB (and bias + b sBias) and writing C + b sC
+    // (and save + b sSave); strides in elements.  Store, Bias and BiasGelu
+    // epilogues only.
+    int64_t batch = 1;
+    int64_t sA = 0, sB = 0, sC = 0, sBias = 0, sSave = 0;
 };
 
 }  // namespace tpmlp

@@ -338,9 +338,22 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_ring_kernel(GemmArgs p, int t
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wave / kWavesN, wn = wave % kWavesN;
 
-    const int ntiles = tiles_m * tiles_n;
+    // Tiles of all products in one numbering, product-major; an XCD's run of
+    // consecutive tiles then lies in one product (one shard per XCD when
+    // eight shards are batched).
+    const int per_product = tiles_m * tiles_n;
+    const int ntiles = per_product * (int)p.batch;
     int tile = blockIdx.x;
     if (ntiles % kXcds == 0) tile = (tile % kXcds) * (ntiles / kXcds) + tile / kXcds;
+    if (p.batch > 1) {
+        const int64_t b = tile / per_product;
+        tile -= (int)b * per_product;
+        p.A = static_cast<const bf16*>(p.A) + b * p.sA;
+        p.B = static_cast<const bf16*>(p.B) + b * p.sB;
+        p.C = static_cast<OutT*>(p.C) + b * p.sC;
+        if (p.bias) p.bias = static_cast<const bf16*>(p.bias) + b * p.sBias;
+        if (p.save) p.save = static_cast<bf16*>(p.save) + b * p.sSave;
+    }
     int tm = tile % tiles_m, tn = tile / tiles_m;
     if (group_m > 0 && tiles_m % group_m == 0) {
         // Tiles in groups of group_m tile rows, column by column inside a
@@ -680,9 +693,13 @@ hipError_t launch(const GemmArgs& p, hipStream_t stream)
     // groups: the weight gradients (six waves) about 4% faster, the two-wave
     // NN row-layer product about 2%.  One-wave products and the two-wave NT
     // product keep the plain order, which measured as fast or faster for them.
-    const int group_m = tm * tn > 2 * kCUs || (!BK && tm * tn >= 2 * kCUs) ? 4 : 0;
-    hipLaunchKernelGGL((gemm_ring_kernel<NW, WM, AK, BK, E, O>), dim3((unsigned)(tm * tn)),
-                       dim3(64 * NW), 0, stream, p, tm, tn, group_m);
+    // Batched products give each XCD one product's tiles for its 32 CUs, so
+    // they take the 4-row groups as well.
+    const int group_m =
+        tm * tn > 2 * kCUs || (!BK && tm * tn >= 2 * kCUs) || p.batch > 1 ? 4 : 0;
+    hipLaunchKernelGGL((gemm_ring_kernel<NW, WM, AK, BK, E, O>),
+                       dim3((unsigned)(tm * tn * p.batch)), dim3(64 * NW), 0, stream, p, tm, tn,
+                       group_m);
     return hipGetLastError();
 }
 
@@ -696,11 +713,16 @@ bool gemm_ring_supported(const GemmArgs& p, Layout layout)
     // A K-major operand must not run past the end of a row inside a slab.
     if (layout != Layout::TN && p.K % kBK != 0) return false;
     const int64_t lim = (int64_t(1) << 31) - 1;
+    if (p.batch < 1 || (int64_t)((p.M + kBM - 1) / kBM) * ((p.N + kBN - 1) / kBN) * p.batch >
+                           (int64_t(1) << 30))
+        return false;
     return p.M * p.K * 2 <= lim && p.N * p.K * 2 <= lim;
 }
 
 hipError_t gemm_ring(const GemmArgs& p, Layout layout, Epi epi, Elt out, hipStream_t stream)
 {
+    if (p.batch > 1 && epi != Epi::Store && epi != Epi::Bias && epi != Epi::BiasGelu)
+        return hipErrorInvalidValue;
     switch (layout) {
     case Layout::NN:
         if (epi == Epi::BiasGelu) {

@@ -229,6 +229,24 @@ hipError_t launch(const GemmArgs& p, hipStream_t stream)
 hipError_t gemm_simple(const GemmArgs& p, Elt elt, Layout layout, Epi epi, Elt out,
                        hipStream_t stream)
 {
+    if (p.batch > 1) {
+        // Batched products: one launch per product.
+        if (epi != Epi::Store && epi != Epi::Bias && epi != Epi::BiasGelu)
+            return hipErrorInvalidValue;
+        const int64_t es = elt == Elt::F32 ? 4 : 2, os = out == Elt::F32 ? 4 : 2;
+        for (int64_t b = 0; b < p.batch; ++b) {
+            GemmArgs q = p;
+            q.batch = 1;
+            q.A = static_cast<const char*>(p.A) + b * p.sA * es;
+            q.B = static_cast<const char*>(p.B) + b * p.sB * es;
+            q.C = static_cast<char*>(p.C) + b * p.sC * os;
+            if (p.bias) q.bias = static_cast<const char*>(p.bias) + b * p.sBias * es;
+            if (p.save) q.save = static_cast<char*>(p.save) + b * p.sSave * es;
+            const hipError_t e = gemm_simple(q, elt, layout, epi, out, stream);
+            if (e != hipSuccess) return e;
+        }
+        return hipSuccess;
+    }
 #define TP_CASE(T, AK, BK_, E, O)                                                    \
     return launch<T, AK, BK_, E, O>(p, stream)
     if (elt == Elt::F32) {

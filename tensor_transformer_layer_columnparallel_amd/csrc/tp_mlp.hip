@@ -72,22 +72,34 @@ bool use_transposed_operands(int64_t tokens, int64_t h, int64_t n, Elt e)
     return gemm_ring_supported(a, Layout::NN) && gemm_ring_supported(b, Layout::NN);
 }
 
-// True when a product of this shape runs on the tile kernel.
-bool ring_path(int64_t M, int64_t N, int64_t K, Elt elt, Layout layout)
+// True when a product of this shape (`batch` of them in one launch) runs on
+// the tile kernel.
+bool ring_path(int64_t M, int64_t N, int64_t K, Elt elt, Layout layout, int64_t batch = 1)
 {
     GemmArgs p{};
     p.M = M; p.N = N; p.K = K;
+    p.batch = batch;
     return elt == Elt::BF16 && M > 0 && N > 0 && gemm_ring_supported(p, layout);
 }
+
+// `batch` products of one shape with operands at the given element strides
+// (A, B, C, bias, save), one launch on the tile kernel.
+struct Batch {
+    int64_t count = 1, sA = 0, sB = 0, sC = 0, sBias = 0, sSave = 0;
+};
 
 // colsum (DGelu on the tile kernel only): per-256-row-block column sums of C.
 hipError_t run_gemm(const void* A, const void* B, void* C, const void* bias, const void* aux,
                     void* save, int64_t M, int64_t N, int64_t K, Elt elt, Layout layout, Epi epi,
-                    Elt out, hipStream_t stream, float* colsum = nullptr)
+                    Elt out, hipStream_t stream, float* colsum = nullptr,
+                    const Batch& batch = Batch{})
 {
-    if (M == 0 || N == 0) return hipSuccess;
+    if (M == 0 || N == 0 || batch.count == 0) return hipSuccess;
     GemmArgs p{A, B, C, bias, aux, save, M, N, K, colsum};
-    if (ring_path(M, N, K, elt, layout)) return gemm_ring(p, layout, epi, out, stream);
+    p.batch = batch.count;
+    p.sA = batch.sA; p.sB = batch.sB; p.sC = batch.sC;
+    p.sBias = batch.sBias; p.sSave = batch.sSave;
+    if (ring_path(M, N, K, elt, layout, batch.count)) return gemm_ring(p, layout, epi, out, stream);
     return gemm_simple(p, elt, layout, epi, out, stream);
 }
 
@@ -175,6 +187,39 @@ int tp_mlp_shard_fwd(const void* X, const void* W1_i, const void* b1_i, const vo
     if (err != hipSuccess) return TP_ERR_HIP;
     return status_of(run_gemm(H_i, W2_i, Z_i, nullptr, nullptr, nullptr, tokens, h, n, e,
                               Layout::NN, Epi::Store, Elt::F32, s));
+}
+
+int tp_mlp_layer_fwd(const void* X, const void* W1, const void* b1, const void* W2, void* H,
+                     void* Y_save, void* Z, int64_t tokens, int64_t h, int64_t ffn, int t,
+                     int dtype, void* stream)
+{
+    if (!valid_dtype(dtype)) return TP_ERR_DTYPE;
+    int st = check_ptrs({X, W1, W2, H, Z}, {b1, Y_save});
+    if (st) return st;
+    int64_t n = 0;
+    if ((st = check_split(ffn, t, 0, &n))) return st;
+    if (tokens < 0 || !feature_dim_ok(h)) return TP_ERR_SHAPE;
+    const int es = elt_size(dtype);
+    if (!fits(tokens, h, es) || !fits(h, n, es) || !fits(tokens, n, es) || !fits(tokens, h, 4))
+        return TP_ERR_SHAPE;
+    const Elt e = to_elt(dtype);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    Batch col;
+    col.count = t;
+    col.sB = h * n;          // W1[r]
+    col.sC = tokens * n;     // H[r]
+    col.sBias = n;           // b1[r]
+    col.sSave = tokens * n;  // Y_save[r]
+    hipError_t err = run_gemm(X, W1, H, b1, nullptr, Y_save, tokens, n, h, e, Layout::NN,
+                              Epi::BiasGelu, e, s, nullptr, col);
+    if (err != hipSuccess) return TP_ERR_HIP;
+    Batch row;
+    row.count = t;
+    row.sA = tokens * n;     // H[r]
+    row.sB = n * h;          // W2[r]
+    row.sC = tokens * h;     // Z[r]
+    return status_of(run_gemm(H, W2, Z, nullptr, nullptr, nullptr, tokens, h, n, e, Layout::NN,
+                              Epi::Store, Elt::F32, s, nullptr, row));
 }
 
 int tp_mlp_shard_bwd(const void* X, const void* W1_i, const void* W2_i, const void* Y_i,

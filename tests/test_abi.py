@@ -35,7 +35,8 @@ def Bfake(B):
 
 def test_header_declares_the_entry_points_and_status_string():
     assert set(_declared_functions()) == {
-        "tp_column_linear", "tp_row_linear", "tp_mlp_shard_fwd", "tp_mlp_shard_bwd",
+        "tp_column_linear", "tp_row_linear", "tp_mlp_shard_fwd", "tp_mlp_layer_fwd",
+        "tp_mlp_shard_bwd",
         "tp_linear_bwd", "tp_shard_reduce", "tp_shard_reduce_scatter", "tp_layernorm",
         "tp_status_string"}
 
@@ -125,6 +126,30 @@ def test_mlp_fwd_bwd_reject(Bfake):
     assert bwd(db1_i=MIS) == B.TP_ERR_ALIGN
     assert bwd(rank=8) == B.TP_ERR_RANK
     assert bwd(h=60) == B.TP_ERR_SHAPE
+
+
+def test_mlp_layer_fwd_rejects(Bfake):
+    B = Bfake
+    f = lambda **kw: B.tp_mlp_layer_fwd(**{**dict(
+        X=P, W1=P, b1=None, W2=P, H=P2, Y_save=None, Z=P2, tokens=16, h=64, ffn=256, t=8,
+        dtype=B.TP_BF16, stream=0, check=False), **kw})
+    assert f(X=None) == B.TP_ERR_NULL
+    assert f(W2=None) == B.TP_ERR_NULL
+    assert f(H=None) == B.TP_ERR_NULL
+    assert f(Z=None) == B.TP_ERR_NULL
+    assert f(b1=MIS) == B.TP_ERR_ALIGN
+    assert f(Y_save=MIS) == B.TP_ERR_ALIGN
+    assert f(W1=MIS) == B.TP_ERR_ALIGN
+    assert f(t=0) == B.TP_ERR_RANK
+    assert f(t=-2) == B.TP_ERR_RANK
+    assert f(ffn=264, t=5) == B.TP_ERR_INDIVISIBLE
+    assert f(ffn=264, t=8) == B.TP_ERR_SHAPE               # shard width 33
+    assert f(ffn=260) == B.TP_ERR_SHAPE
+    assert f(h=60) == B.TP_ERR_SHAPE
+    assert f(tokens=-1) == B.TP_ERR_SHAPE
+    assert f(dtype=3) == B.TP_ERR_DTYPE
+    # one rank's block of 2^31 bytes or more
+    assert f(tokens=1 << 20, h=1 << 10, ffn=8 * 64) == B.TP_ERR_SHAPE
 
 
 def test_linear_bwd_rejects(Bfake):

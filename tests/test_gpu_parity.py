@@ -709,15 +709,90 @@ def test_full_layer_emulation_8_shards_sampled(B):
                            w.ffn, w.t, r, B.TP_BF16)
     Z = torch.empty(w.T, w.h, dtype=torch.float32, device="cuda")
     B.tp_shard_reduce(parts, Z, w.T, w.h, w.t, B.TP_REDUCE_SUM, B.TP_F32, B.TP_F32)
+    # The same layer with the 8 shards' products batched into two launches:
+    # every tile computes what the per-shard call computes, so the partials
+    # and their sum agree bit for bit.
+    _log(f"case {w.name}: all shards batched (tp_mlp_layer_fwd) + shard-sum")
+    W1s = torch.stack([d["W1"][r] for r in w.ranks])
+    W2s = torch.stack([d["W2"][r] for r in w.ranks])
+    Hs = torch.empty(w.t, w.T, w.n, dtype=torch.bfloat16, device="cuda")
+    parts_b = torch.empty_like(parts)
+    B.tp_mlp_layer_fwd(d["X"], W1s, None, W2s, Hs, None, parts_b, w.T, w.h, w.ffn, w.t,
+                       B.TP_BF16)
+    Zb = torch.empty_like(Z)
+    B.tp_shard_reduce(parts_b, Zb, w.T, w.h, w.t, B.TP_REDUCE_SUM, B.TP_F32, B.TP_F32)
     torch.cuda.synchronize()
+    assert torch.equal(parts_b, parts), "batched partials differ from the per-shard ones"
+    assert torch.equal(Zb, Z), "batched layer output differs from the per-shard one"
+    assert torch.equal(Hs[w.t - 1], H), "batched H of the last shard differs"
     Zc = Z.cpu()
-    del d, parts
+    del d, parts, parts_b, W1s, W2s, Hs
     torch.cuda.empty_cache()
     rows = sample_indices(w.T, 4, seed=4)
     _log(f"case {w.name}: unsharded oracle rows {rows.tolist()}")
     W1, b1, W2 = _unsharded(d_h, w.ranks)
     _, _, rZ = oracle.mlp_shard_fwd_rows(d_h["X"], W1, b1, W2, rows)
     assert_close(Zc[rows], rZ, "bf16", "full layer Z rows")
+
+
+LAYER_FWD = [  # (tokens, h, ffn, t, dtype, bias, save)
+    (300, 512, 8 * 224, 8, "bf16", True, True),    # tile kernel, ragged M and N tails
+    (512, 384, 4 * 384, 4, "bf16", False, True),   # tile kernel, whole tiles, no bias
+    (96, 256, 2 * 128, 2, "bf16", True, False),    # shard narrower than a tile: general kernel
+    (64, 128, 512, 4, "f32", True, True),          # fp32: general kernel, one launch per shard
+    (272, 256, 1 * 448, 1, "bf16", True, True),    # t = 1: the unsharded layer
+    (0, 256, 8 * 192, 8, "bf16", True, True),      # no tokens: nothing to do
+]
+
+
+@pytest.mark.parametrize("shape", LAYER_FWD, ids=lambda s: "x".join(map(str, s)))
+def test_layer_fwd_matches_each_shard_and_the_oracle(B, shape):
+    T, h, ffn, t, dt, bias, save = shape
+    _log(f"case layer fwd {shape}")
+    w = configs.Workload("layer_fwd", T=T, h=h, ffn=ffn, t=t, dtype=dt, ranks=tuple(range(t)),
+                         bias=bias)
+    n = w.n
+    d_h = synth.make_inputs(w, seed=21)
+    d = to_device(d_h)
+    tdt = torch.float32 if dt == "f32" else torch.bfloat16
+    W1s = torch.stack([d["W1"][r] for r in range(t)])
+    W2s = torch.stack([d["W2"][r] for r in range(t)])
+    b1s = torch.stack([d["b1"][r] for r in range(t)]) if bias else None
+    # stacked outputs followed by NaN sentinels inside the same allocation
+    Hf, Hs = _nan_padded(torch.zeros(t, T, n, dtype=tdt, device="cuda"))
+    Yf, Ys = _nan_padded(torch.zeros(t, T, n, dtype=tdt, device="cuda"))
+    Zf, Zs = _nan_padded(torch.zeros(t, T, h, dtype=torch.float32, device="cuda"))
+    if not T:
+        # Empty arrays have no storage; NaN-filled placeholders stand for the
+        # [0, *] arrays and must come back untouched.
+        ph = torch.full((64,), float("nan"), dtype=tdt, device="cuda")
+        phf = torch.full((64,), float("nan"), device="cuda")
+        assert B.tp_mlp_layer_fwd(ph, W1s, b1s, W2s, ph, ph, phf, T, h, ffn, t, tdt) == 0
+        torch.cuda.synchronize()
+        assert torch.isnan(ph).all() and torch.isnan(phf).all()
+        return
+    B.tp_mlp_layer_fwd(d["X"], W1s, b1s, W2s, Hs, Ys if save else None, Zs, T, h, ffn, t, tdt)
+    torch.cuda.synchronize()
+    assert torch.isnan(Hf[Hs.numel():]).all() and torch.isnan(Zf[Zs.numel():]).all()
+    assert torch.isnan(Yf[Ys.numel():]).all()
+    if not save:
+        assert torch.count_nonzero(Ys) == 0
+    for r in range(t):
+        Y, H, Z = gpu_shard_fwd(B, w, d, r)
+        torch.cuda.synchronize()
+        assert torch.equal(Hs[r], H), f"H[{r}] differs from the per-shard call"
+        assert torch.equal(Zs[r], Z), f"Z[{r}] differs from the per-shard call"
+        if save:
+            assert torch.equal(Ys[r], Y), f"Y[{r}] differs from the per-shard call"
+        rY, rH, rZ = oracle.mlp_shard_fwd(d_h["X"], d_h["W1"][r], d_h["b1"][r], d_h["W2"][r])
+        assert_close(Hs[r], rH, dt, f"layer fwd H[{r}]")
+        assert_close(Zs[r], rZ, dt, f"layer fwd Z[{r}]")
+    Zsum = torch.empty(T, h, dtype=torch.float32, device="cuda")
+    B.tp_shard_reduce(Zs, Zsum, T, h, t, B.TP_REDUCE_SUM, B.TP_F32, B.TP_F32)
+    torch.cuda.synchronize()
+    W1, b1, W2 = _unsharded(d_h, range(t))
+    _, _, rZ = oracle.mlp_shard_fwd(d_h["X"], W1, b1, W2)
+    assert_close(Zsum, rZ, dt, "layer fwd: sum of the partials vs the unsharded layer")
 
 
 def _nan_padded(x, pad=1 << 16):
