@@ -113,6 +113,48 @@ def ingest_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, comman
 
 COPY_ROWS, COPY_COLS = 8192, 8192
 
+MFMA_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES",
+                 "GRBM_GUI_ACTIVE", "GRBM_COUNT")
+
+
+def ingest_mfma(pmc_dir: str, simds: int = 1024, xcds: int = 8):
+    """Markdown table from one rocprofv3 --pmc run of MFMA_COUNTERS: per GEMM
+    kernel instance, the mean per dispatch of the bf16 MFMA work (the
+    counter counts multiply and add operations / 512), the MFMA unit's busy
+    fraction (busy cycles summed over the SIMDs / (GPU-active cycles of one
+    XCD x SIMDs)), the GPU-active cycles of one XCD and the engine clock they
+    imply over the dispatch's duration.  rocprofv3 reports each counter as
+    one value per dispatch, summed over its instances; GRBM_GUI_ACTIVE is
+    summed over the XCDs, hence divided by their count."""
+    import csv
+    import glob
+    disp = {}
+    for path in glob.glob(os.path.join(pmc_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                if "gemm" not in row["Kernel_Name"]:
+                    continue
+                d = disp.setdefault(row["Dispatch_Id"], {
+                    "name": row["Kernel_Name"],
+                    "ns": int(row["End_Timestamp"]) - int(row["Start_Timestamp"])})
+                c, v = row["Counter_Name"], float(row["Counter_Value"])
+                d[c] = d.get(c, 0.0) + v
+    if not disp:
+        raise SystemExit(f"no GEMM dispatches under {pmc_dir}")
+    per = {}
+    for d in disp.values():
+        per.setdefault(d["name"], []).append(d)
+    print("| kernel | dispatches | bf16 MFMA GFLOP per dispatch | MFMA busy | GPU-active cycles per XCD | clock GHz | duration us |")
+    print("|---|---|---|---|---|---|---|")
+    for name, ds in sorted(per.items(), key=lambda kv: -len(kv[1])):
+        mean = lambda k: sum(d.get(k, 0.0) for d in ds) / len(ds)
+        act, ns = mean("GRBM_GUI_ACTIVE") / xcds, mean("ns")
+        busy = mean("SQ_VALU_MFMA_BUSY_CYCLES") / (act * simds) if act else float("nan")
+        short = name if len(name) <= 90 else name[:87] + "..."
+        print(f"| `{short}` | {len(ds)} | {mean('SQ_INSTS_VALU_MFMA_MOPS_BF16') * 512 / 1e9:.1f} | "
+              f"{100 * busy:.1f}% | {act:.0f} | {act / ns:.2f} | {ns / 1e3:.1f} |")
+
+
 
 def copy_calibration(reps: int):
     """A plain device copy of known size (8192 x 8192 fp32 = 256 MiB read and
@@ -431,7 +473,13 @@ def main():
                     help="per-kernel durations from a rocprofv3 --kernel-trace CSV of a bench "
                          "run with these warm-up and timed step counts: over all dispatches "
                          "and inside the timed steps")
+    ap.add_argument("--ingest-mfma", metavar="PMC_DIR",
+                    help="MFMA work, busy fraction and clock per GEMM from a rocprofv3 --pmc run "
+                         "of " + " ".join(MFMA_COUNTERS))
     args = ap.parse_args()
+    if args.ingest_mfma:
+        ingest_mfma(args.ingest_mfma)
+        return
     if args.trace_summary:
         trace_summary(args.trace_summary[0], int(args.trace_summary[1]),
                       int(args.trace_summary[2]))
