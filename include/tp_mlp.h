@@ -44,6 +44,11 @@
  *     the shard width out_features / t, in_features / t) must be a positive
  *     multiple of 8.  Each operand must be smaller than 2^31 bytes.
  *   - Pointers must be 16-byte aligned.  Optional pointers may be NULL.
+ *   - No output may overlap an input or another output (the kernels read
+ *     inputs while other workgroups write outputs, and the backward stages
+ *     intermediate data in its outputs); the byte ranges the shape arguments
+ *     give are compared and an overlap returns TP_ERR_OVERLAP.  The one
+ *     exception is tp_layernorm with y == x exactly (in place).
  *   - Errors: arguments are validated before anything is enqueued; on any
  *     error nothing is launched and a negative tp_status is returned.  A
  *     failed launch returns TP_ERR_HIP (work enqueued earlier in the same
@@ -71,7 +76,8 @@ typedef enum {
     TP_ERR_DTYPE = -5,       /* unsupported element-type combination */
     TP_ERR_ALIGN = -6,       /* a pointer is not 16-byte aligned */
     TP_ERR_HIP = -7,         /* the HIP runtime rejected a launch */
-    TP_ERR_ARG = -8          /* an enum argument is out of range */
+    TP_ERR_ARG = -8,         /* an enum argument is out of range */
+    TP_ERR_OVERLAP = -9      /* an output overlaps an input or another output */
 } tp_status;
 
 typedef enum { TP_F32 = 0, TP_BF16 = 1 } tp_dtype;

@@ -27,7 +27,7 @@ LIB_PATH = os.path.join(_HERE, "libtpmlp.so")
 
 TP_OK = 0
 TP_ERR_NULL, TP_ERR_SHAPE, TP_ERR_INDIVISIBLE, TP_ERR_RANK = -1, -2, -3, -4
-TP_ERR_DTYPE, TP_ERR_ALIGN, TP_ERR_HIP, TP_ERR_ARG = -5, -6, -7, -8
+TP_ERR_DTYPE, TP_ERR_ALIGN, TP_ERR_HIP, TP_ERR_ARG, TP_ERR_OVERLAP = -5, -6, -7, -8, -9
 TP_F32, TP_BF16 = 0, 1
 TP_ACT_NONE, TP_ACT_GELU_TANH = 0, 1
 TP_REDUCE_SUM, TP_REDUCE_CONCAT, TP_REDUCE_CONCAT_TOKENS = 0, 1, 2

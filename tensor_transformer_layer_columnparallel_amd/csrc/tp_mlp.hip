@@ -54,6 +54,45 @@ int check_split(int64_t full, int t, int rank, int64_t* local)
 
 int status_of(hipError_t e) { return e == hipSuccess ? TP_OK : TP_ERR_HIP; }
 
+// A byte range [p, p + bytes) that an entry point reads or writes.
+struct Region {
+    const void* p;
+    int64_t bytes;
+};
+
+// a * b * c * es, saturating at INT64_MAX (shapes here are non-negative).
+int64_t nbytes(int64_t a, int64_t b, int64_t c, int64_t es)
+{
+    int64_t r = es;
+    for (int64_t d : {a, b, c}) {
+        if (d <= 0) return 0;
+        if (r > INT64_MAX / d) return INT64_MAX;
+        r *= d;
+    }
+    return r;
+}
+
+bool overlap(const Region& a, const Region& b)
+{
+    if (!a.p || !b.p || a.bytes <= 0 || b.bytes <= 0) return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+    const uintptr_t a1 = a0 + (uintptr_t)a.bytes < a0 ? UINTPTR_MAX : a0 + (uintptr_t)a.bytes;
+    const uintptr_t b1 = b0 + (uintptr_t)b.bytes < b0 ? UINTPTR_MAX : b0 + (uintptr_t)b.bytes;
+    return a0 < b1 && b0 < a1;
+}
+
+// TP_ERR_OVERLAP if an output overlaps an input or another output.
+int check_overlap(std::initializer_list<Region> outs, std::initializer_list<Region> ins)
+{
+    for (auto o = outs.begin(); o != outs.end(); ++o) {
+        for (const Region& i : ins)
+            if (overlap(*o, i)) return TP_ERR_OVERLAP;
+        for (auto o2 = o + 1; o2 != outs.end(); ++o2)
+            if (overlap(*o, *o2)) return TP_ERR_OVERLAP;
+    }
+    return TP_OK;
+}
+
 // The weight-gradient products x^T dy read both operands M/N-contiguous,
 // which the tile kernel can only do with transposing LDS reads of both.  With
 // bf16 operands, a token count that whole 32-deep slabs cover and room for
@@ -119,6 +158,7 @@ const char* tp_status_string(int status)
     case TP_ERR_ALIGN: return "a pointer is not 16-byte aligned";
     case TP_ERR_HIP: return "the HIP runtime rejected a launch";
     case TP_ERR_ARG: return "an enum argument is out of range";
+    case TP_ERR_OVERLAP: return "an output overlaps an input or another output";
     default: return "unknown status";
     }
 }
@@ -142,6 +182,11 @@ int tp_column_linear(const void* X, const void* W_i, const void* b_i, void* Y_i,
     // Without an activation the output is the pre-activation itself.
     const Epi epi = act == TP_ACT_GELU_TANH ? Epi::BiasGelu : Epi::Bias;
     if (epi == Epi::Bias && pre_save) return TP_ERR_ARG;
+    if ((st = check_overlap({{Y_i, nbytes(tokens, n, 1, elt_size(out_dtype))},
+                             {pre_save, nbytes(tokens, n, 1, es)}},
+                            {{X, nbytes(tokens, in_features, 1, es)},
+                             {W_i, nbytes(in_features, n, 1, es)}, {b_i, nbytes(n, 1, 1, es)}})))
+        return st;
     return status_of(run_gemm(X, W_i, Y_i, b_i, nullptr, pre_save, tokens, n, in_features,
                               to_elt(dtype), Layout::NN, epi, to_elt(out_dtype),
                               static_cast<hipStream_t>(stream)));
@@ -162,6 +207,10 @@ int tp_row_linear(const void* X_i, const void* W_i, void* Z_i, int64_t tokens,
     if (!fits(tokens, k, es) || !fits(k, out_features, es) ||
         !fits(tokens, out_features, elt_size(out_dtype)))
         return TP_ERR_SHAPE;
+    if ((st = check_overlap({{Z_i, nbytes(tokens, out_features, 1, elt_size(out_dtype))}},
+                            {{X_i, nbytes(tokens, k, 1, es)},
+                             {W_i, nbytes(k, out_features, 1, es)}})))
+        return st;
     return status_of(run_gemm(X_i, W_i, Z_i, nullptr, nullptr, nullptr, tokens, out_features, k,
                               to_elt(dtype), Layout::NN, Epi::Store, to_elt(out_dtype),
                               static_cast<hipStream_t>(stream)));
@@ -180,6 +229,11 @@ int tp_mlp_shard_fwd(const void* X, const void* W1_i, const void* b1_i, const vo
     const int es = elt_size(dtype);
     if (!fits(tokens, h, es) || !fits(h, n, es) || !fits(tokens, n, es) || !fits(tokens, h, 4))
         return TP_ERR_SHAPE;
+    if ((st = check_overlap({{H_i, nbytes(tokens, n, 1, es)}, {Y_i_save, nbytes(tokens, n, 1, es)},
+                             {Z_i, nbytes(tokens, h, 1, 4)}},
+                            {{X, nbytes(tokens, h, 1, es)}, {W1_i, nbytes(h, n, 1, es)},
+                             {b1_i, nbytes(n, 1, 1, es)}, {W2_i, nbytes(n, h, 1, es)}})))
+        return st;
     const Elt e = to_elt(dtype);
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t err = run_gemm(X, W1_i, H_i, b1_i, nullptr, Y_i_save, tokens, n, h, e, Layout::NN,
@@ -202,6 +256,11 @@ int tp_mlp_layer_fwd(const void* X, const void* W1, const void* b1, const void* 
     const int es = elt_size(dtype);
     if (!fits(tokens, h, es) || !fits(h, n, es) || !fits(tokens, n, es) || !fits(tokens, h, 4))
         return TP_ERR_SHAPE;
+    if ((st = check_overlap({{H, nbytes(t, tokens, n, es)}, {Y_save, nbytes(t, tokens, n, es)},
+                             {Z, nbytes(t, tokens, h, 4)}},
+                            {{X, nbytes(tokens, h, 1, es)}, {W1, nbytes(t, h, n, es)},
+                             {b1, nbytes(t, n, 1, es)}, {W2, nbytes(t, n, h, es)}})))
+        return st;
     const Elt e = to_elt(dtype);
     hipStream_t s = static_cast<hipStream_t>(stream);
     Batch col;
@@ -237,6 +296,13 @@ int tp_mlp_shard_bwd(const void* X, const void* W1_i, const void* W2_i, const vo
     if (!fits(tokens, h, es) || !fits(h, n, es) || !fits(tokens, n, es) || !fits(tokens, h, 4) ||
         !fits(h, n, 4))
         return TP_ERR_SHAPE;
+    if ((st = check_overlap({{dY_i, nbytes(tokens, n, 1, es)}, {dW2_i, nbytes(n, h, 1, 4)},
+                             {dW1_i, nbytes(h, n, 1, 4)}, {dX_i, nbytes(tokens, h, 1, 4)},
+                             {db1_i, nbytes(n, 1, 1, 4)}},
+                            {{X, nbytes(tokens, h, 1, es)}, {W1_i, nbytes(h, n, 1, es)},
+                             {W2_i, nbytes(n, h, 1, es)}, {Y_i, nbytes(tokens, n, 1, es)},
+                             {H_i, nbytes(tokens, n, 1, es)}, {dZ, nbytes(tokens, h, 1, es)}})))
+        return st;
     const Elt e = to_elt(dtype);
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t err;
@@ -314,6 +380,11 @@ int tp_linear_bwd(const void* X, const void* W, const void* dY, void* dX, void* 
     if (!fits(tokens, k, es) || !fits(k, n, es) || !fits(tokens, n, es) || !fits(tokens, k, 4) ||
         !fits(k, n, 4))
         return TP_ERR_SHAPE;
+    if ((st = check_overlap({{dX, nbytes(tokens, k, 1, 4)}, {dW, nbytes(k, n, 1, 4)},
+                             {db, nbytes(n, 1, 1, 4)}},
+                            {{X, nbytes(tokens, k, 1, es)}, {W, nbytes(k, n, 1, es)},
+                             {dY, nbytes(tokens, n, 1, es)}})))
+        return st;
     const Elt e = to_elt(dtype);
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t err;
@@ -358,6 +429,10 @@ int tp_shard_reduce(const void* parts, void* out, int64_t tokens, int64_t cols, 
     if (st) return st;
     if (t < 1) return TP_ERR_RANK;
     if (tokens < 0 || !feature_dim_ok(cols)) return TP_ERR_SHAPE;
+    const int64_t out_rows = op == TP_REDUCE_SUM ? 1 : t;   // CONCAT: t blocks of tokens x cols
+    if ((st = check_overlap({{out, nbytes(out_rows, tokens, cols, elt_size(out_dtype))}},
+                            {{parts, nbytes(t, tokens, cols, elt_size(in_dtype))}})))
+        return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int64_t count = tokens * cols;
     if (op == TP_REDUCE_SUM)
@@ -379,6 +454,9 @@ int tp_shard_reduce_scatter(const void* parts, void* out, int64_t tokens, int64_
     if (tokens < 0 || !feature_dim_ok(cols)) return TP_ERR_SHAPE;
     if (tokens % t != 0) return TP_ERR_INDIVISIBLE;
     const int64_t rows = tokens / t;
+    if ((st = check_overlap({{out, nbytes(rows, cols, 1, elt_size(out_dtype))}},
+                            {{parts, nbytes(t, tokens, cols, elt_size(in_dtype))}})))
+        return st;
     const char* base = static_cast<const char*>(parts) + rank * rows * cols * elt_size(in_dtype);
     return status_of(shard_sum(base, out, rows * cols, tokens * cols, t, to_elt(in_dtype),
                                to_elt(out_dtype), static_cast<hipStream_t>(stream)));
@@ -394,6 +472,12 @@ int tp_layernorm(const void* x, const void* gamma, const void* beta, void* y, in
     if (!(eps >= 0.0f) || eps == INFINITY) return TP_ERR_ARG;
     if (x == y && in_dtype != out_dtype) return TP_ERR_ARG;
     if (!fits(tokens, cols, 4)) return TP_ERR_SHAPE;
+    // y == x (in place) is allowed; any other overlap is not.
+    if ((st = check_overlap({{y, nbytes(tokens, cols, 1, elt_size(out_dtype))}},
+                            {{x == y ? nullptr : x, nbytes(tokens, cols, 1, elt_size(in_dtype))},
+                             {gamma, nbytes(cols, 1, 1, elt_size(out_dtype))},
+                             {beta, nbytes(cols, 1, 1, elt_size(out_dtype))}})))
+        return st;
     return status_of(layernorm(x, gamma, beta, y, tokens, cols, eps, to_elt(in_dtype),
                                to_elt(out_dtype), static_cast<hipStream_t>(stream)));
 }

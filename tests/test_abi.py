@@ -56,7 +56,7 @@ def test_package_exposes_every_entry_point(B):
 
 
 def test_status_strings(B):
-    for st in range(0, -9, -1):
+    for st in range(0, -10, -1):
         assert B.tp_status_string(st) and B.tp_status_string(st) != "unknown status"
     assert B.tp_status_string(12345) == "unknown status"
 
@@ -247,3 +247,75 @@ def test_binding_checks_tensor_arguments(Bfake):
     assert (ffn + 8) % 5 != 0
     assert B.tp_column_linear(P, P, None, P, None, T, h, ffn + 8, 5, 0, bf, bf,
                               B.TP_ACT_NONE, stream=0, check=False) == B.TP_ERR_INDIVISIBLE
+
+
+# Byte ranges for the overlap checks: Q + k is k bytes past Q (16-aligned).
+Q = 0x1000000
+
+
+def test_outputs_may_not_overlap_inputs_or_each_other(Bfake):
+    B = Bfake
+    OV = B.TP_ERR_OVERLAP
+    T, h, ffn, t = 32, 64, 256, 2
+    n = ffn // t
+    bf = B.TP_BF16
+    # disjoint regions: each argument 1 MiB apart
+    r = [Q + i * (1 << 20) for i in range(16)]
+    # column: Y_i over X; pre_save over Y_i; Y_i in the bias
+    col = lambda **kw: B.tp_column_linear(**{**dict(
+        X=r[0], W_i=r[1], b_i=r[2], Y_i=r[3], pre_save=r[4], tokens=T, in_features=h,
+        out_features=ffn, t=t, rank=0, dtype=bf, out_dtype=bf, act=B.TP_ACT_GELU_TANH, stream=0,
+        check=False), **kw})
+    assert col(Y_i=r[0] + T * h * 2 - 16) == OV          # last 16 bytes of X
+    assert col(pre_save=r[3] + 16) == OV
+    assert col(b_i=r[3] + 32) == OV
+    # row: Z_i over W_i
+    row = lambda **kw: B.tp_row_linear(**{**dict(
+        X_i=r[0], W_i=r[1], Z_i=r[2], tokens=T, in_features=ffn, out_features=h, t=t, rank=1,
+        dtype=bf, out_dtype=B.TP_F32, stream=0, check=False), **kw})
+    assert row(Z_i=r[1]) == OV
+    # shard forward: Z_i over H_i; H_i over W2_i
+    fwd = lambda **kw: B.tp_mlp_shard_fwd(**{**dict(
+        X=r[0], W1_i=r[1], b1_i=r[2], W2_i=r[3], H_i=r[4], Y_i_save=r[5], Z_i=r[6], tokens=T,
+        h=h, ffn=ffn, t=t, rank=0, dtype=bf, stream=0, check=False), **kw})
+    assert fwd(Z_i=r[4] + 16) == OV
+    assert fwd(H_i=r[3]) == OV
+    assert fwd(Y_i_save=r[0]) == OV
+    # layer forward: the stacked partials reach into the second rank's H
+    lay = lambda **kw: B.tp_mlp_layer_fwd(**{**dict(
+        X=r[0], W1=r[1], b1=r[2], W2=r[3], H=r[4], Y_save=r[5], Z=r[6], tokens=T, h=h, ffn=ffn,
+        t=t, dtype=bf, stream=0, check=False), **kw})
+    assert lay(Z=r[4] + T * n * 2) == OV                 # rank 1's block of H
+    assert lay(H=r[3] + n * h * 2) == OV                 # rank 1's block of W2
+    # shard backward: dX over dZ; dW1 over dW2; db1 over Y_i
+    bwd = lambda **kw: B.tp_mlp_shard_bwd(**{**dict(
+        X=r[0], W1_i=r[1], W2_i=r[2], Y_i=r[3], H_i=r[4], dZ=r[5], dY_i=r[6], dW2_i=r[7],
+        dW1_i=r[8], dX_i=r[9], db1_i=r[10], tokens=T, h=h, ffn=ffn, t=t, rank=0, dtype=bf,
+        stream=0, check=False), **kw})
+    assert bwd(dX_i=r[5]) == OV
+    assert bwd(dW1_i=r[7] + 64) == OV
+    assert bwd(db1_i=r[3]) == OV
+    assert bwd(dY_i=r[4]) == OV                          # dY_i in place of H_i
+    # linear backward: dW over X
+    lin = lambda **kw: B.tp_linear_bwd(**{**dict(
+        X=r[0], W=r[1], dY=r[2], dX=r[3], dW=r[4], db=r[5], tokens=T, in_features=h,
+        out_features=n, dtype=bf, stream=0, check=False), **kw})
+    assert lin(dW=r[0]) == OV
+    assert lin(db=r[3] + 16) == OV
+    # shard reduce: CONCAT's output is t blocks long
+    red = lambda **kw: B.tp_shard_reduce(**{**dict(
+        parts=r[0], out=r[1], tokens=T, cols=h, t=t, op=B.TP_REDUCE_SUM, in_dtype=B.TP_F32,
+        out_dtype=B.TP_F32, stream=0, check=False), **kw})
+    assert red(out=r[0] + t * T * h * 4 - 16) == OV
+    assert red(out=r[0] - T * h * 4 + 16) == OV          # SUM output ends inside parts
+    assert red(op=B.TP_REDUCE_CONCAT, out=r[0] - t * T * h * 4 + 16) == OV
+    rs = lambda **kw: B.tp_shard_reduce_scatter(**{**dict(
+        parts=r[0], out=r[1], tokens=T, cols=h, t=t, rank=1, in_dtype=B.TP_F32,
+        out_dtype=B.TP_F32, stream=0, check=False), **kw})
+    assert rs(out=r[0] + 256) == OV
+    # layer norm: a shifted output overlaps its input (exactly in place is allowed)
+    ln = lambda **kw: B.tp_layernorm(**{**dict(
+        x=r[0], gamma=r[1], beta=r[2], y=r[3], tokens=T, cols=h, eps=1e-5, in_dtype=B.TP_F32,
+        out_dtype=B.TP_F32, stream=0, check=False), **kw})
+    assert ln(y=r[0] + 16) == OV
+    assert ln(y=r[1]) == OV
