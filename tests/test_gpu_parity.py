@@ -401,6 +401,52 @@ def test_empty_tokens(B):
     assert torch.count_nonzero(db1) == 0
 
 
+def test_overlapping_outputs_are_rejected_before_any_launch(B):
+    """Real device buffers whose byte ranges overlap: the entry points return
+    TP_ERR_OVERLAP and leave the memory as it was."""
+    _log("case overlapping outputs")
+    T, h, ffn, t = 64, 128, 512, 4
+    n = ffn // t
+    bf, f32 = torch.bfloat16, torch.float32
+    g = torch.Generator(device="cuda").manual_seed(5)
+    X = torch.randn(T, h, device="cuda", generator=g).to(bf)
+    W1 = torch.randn(h, n, device="cuda", generator=g).to(bf)
+    W2 = torch.randn(n, h, device="cuda", generator=g).to(bf)
+    buf = torch.randn(T * n + T * h + 64, device="cuda", generator=g)   # fp32 words
+    snap = buf.clone()
+    H = buf.view(bf)[: T * n].view(T, n)          # bytes [0, 2 T n)
+    Z_in_H = buf[T * n // 4:][: T * h]            # starts at byte T n, inside H
+    Z_after_H = buf[T * n // 2:][: T * h]         # starts at byte 2 T n, just past H
+    # Z_i starting inside H_i
+    assert B.tp_mlp_shard_fwd(X, W1, None, W2, H, None, Z_in_H, T, h, ffn, t, 0, bf,
+                              check=False) == B.TP_ERR_OVERLAP
+    # the row layer writing its partial over its own input
+    assert B.tp_row_linear(H, W2, Z_in_H, T, ffn, h, t, 0, bf, f32,
+                           check=False) == B.TP_ERR_OVERLAP
+    # the shard sum writing into its own partials
+    parts = buf[: 2 * T * h].view(2, T, h)
+    assert B.tp_shard_reduce(parts, parts[1], T, h, 2, B.TP_REDUCE_SUM, f32, f32,
+                             check=False) == B.TP_ERR_OVERLAP
+    # the backward's dX_i starting inside dZ
+    bb = torch.randn(2 * T * h, device="cuda", generator=g)
+    bb_snap = bb.clone()
+    dZ = bb.view(bf)[: T * h].view(T, h)          # bytes [0, 2 T h)
+    dX_in_dZ = bb[T * h // 4:][: T * h].view(T, h)  # starts at byte T h
+    dY = torch.empty(T, n, dtype=bf, device="cuda")
+    dW2, dW1 = torch.empty(n, h, device="cuda"), torch.empty(h, n, device="cuda")
+    assert B.tp_mlp_shard_bwd(X, W1, W2, H, H, dZ, dY, dW2, dW1, dX_in_dZ, None, T, h, ffn, t,
+                              0, bf, check=False) == B.TP_ERR_OVERLAP
+    torch.cuda.synchronize()
+    assert torch.equal(buf, snap) and torch.equal(bb, bb_snap), "a rejected call wrote"
+    # adjacent but disjoint ranges are accepted (and computed correctly)
+    assert B.tp_mlp_shard_fwd(X, W1, None, W2, H, None, Z_after_H, T, h, ffn, t, 0, bf,
+                              check=False) == 0
+    torch.cuda.synchronize()
+    _, rH, rZ = oracle.mlp_shard_fwd(X.cpu(), W1.cpu(), None, W2.cpu())
+    assert_close(H, rH, "bf16", "adjacent H")
+    assert_close(Z_after_H.view(T, h), rZ, "bf16", "adjacent Z")
+
+
 # ----------------------------------------------------- invariants on device
 
 def test_column_shards_concat_bitexact_to_unsharded(B):
