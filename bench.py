@@ -330,30 +330,44 @@ def sequence_parallel(B, stream, sptr, reps=10):
     that shard (fp32 in, bf16 out), and the token AllGather of eight bf16
     shards."""
     import torch
-    T, h, t, r = 2048, 12288, 8, 0
+    T, h, t = 2048, 12288, 8
     Tr = T // t
+    bf, f32 = torch.bfloat16, torch.float32
+    # Each repetition works on data no earlier repetition touched, so that
+    # the 256 MB last-level cache does not serve it: the reduce-scatter walks
+    # the ranks (8 blocks of 100 MB), the layer norm and the concatenation
+    # rotate through copies of their buffers (600 and 800 MB).
     parts = torch.randn(t, T, h, device="cuda")
     rs = torch.empty(Tr, h, device="cuda")
-    gam = torch.ones(h, dtype=torch.bfloat16, device="cuda")
-    bet = torch.zeros(h, dtype=torch.bfloat16, device="cuda")
-    y = torch.empty(Tr, h, dtype=torch.bfloat16, device="cuda")
-    shards = torch.randn(t, Tr, h, device="cuda").bfloat16()
-    full = torch.empty(T, h, dtype=torch.bfloat16, device="cuda")
-    bf, f32 = torch.bfloat16, torch.float32
+    n_ln, n_cat = 32, 8
+    ln_in = [torch.randn(Tr, h, device="cuda") for _ in range(n_ln)]
+    ln_out = [torch.empty(Tr, h, dtype=bf, device="cuda") for _ in range(n_ln)]
+    gam = torch.ones(h, dtype=bf, device="cuda")
+    bet = torch.zeros(h, dtype=bf, device="cuda")
+    shards = [torch.randn(t, Tr, h, device="cuda").to(bf) for _ in range(n_cat)]
+    full = [torch.empty(T, h, dtype=bf, device="cuda") for _ in range(n_cat)]
+    k = [0]
+
+    def nxt(n):
+        k[0] += 1
+        return k[0] % n
+
     ops = {
-        "reduce_scatter": (lambda: B.tp_shard_reduce_scatter(parts, rs, T, h, t, r, f32, f32,
-                                                             stream=sptr),
+        "reduce_scatter": (lambda: B.tp_shard_reduce_scatter(parts, rs, T, h, t, nxt(t), f32,
+                                                             f32, stream=sptr),
                            (t * Tr * h + Tr * h) * 4),
-        "layernorm": (lambda: B.tp_layernorm(rs, gam, bet, y, Tr, h, 1e-5, f32, bf, stream=sptr),
+        "layernorm": (lambda: (lambda i: B.tp_layernorm(ln_in[i], gam, bet, ln_out[i], Tr, h,
+                                                        1e-5, f32, bf, stream=sptr))(nxt(n_ln)),
                       Tr * h * 4 + Tr * h * 2 + 2 * h * 2),
-        "concat_tokens": (lambda: B.tp_shard_reduce(shards, full, Tr, h, t,
-                                                    B.TP_REDUCE_CONCAT_TOKENS, bf, bf,
-                                                    stream=sptr),
+        "concat_tokens": (lambda: (lambda i: B.tp_shard_reduce(shards[i], full[i], Tr, h, t,
+                                                               B.TP_REDUCE_CONCAT_TOKENS, bf,
+                                                               bf, stream=sptr))(nxt(n_cat)),
                           2 * T * h * 2),
     }
     out = {"workload": f"t={t}, {T} tokens, h={h}: ReduceScatter of {t} fp32 partials to "
                        f"{Tr} tokens; layer norm of the shard (fp32 -> bf16); token "
-                       f"AllGather of {t} bf16 shards", "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+                       f"AllGather of {t} bf16 shards; every repetition on data not in the "
+                       f"last-level cache", "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     for name, (f, nbytes) in ops.items():
         warm(f)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
