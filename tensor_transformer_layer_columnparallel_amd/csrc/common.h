@@ -60,6 +60,10 @@ struct GemmArgs {
     // epilogues only.
     int64_t batch = 1;
     int64_t sA = 0, sB = 0, sC = 0, sBias = 0, sSave = 0;
+    // Row strides (elements) of A and B when they are not the packed ones
+    // (0: K for a K-contiguous operand, M or N for an M/N-contiguous one); a
+    // product over a K range of wider operands.  Tile kernel only.
+    int64_t lda = 0, ldb = 0;
 };
 
 }  // namespace tpmlp

@@ -170,6 +170,16 @@ __device__ __forceinline__ int mn_logical(int krow, int phys)
 
 constexpr uint32_t kInvalid = 0x80000000u;   // per-lane offset past any operand
 
+// Bytes from an operand's first element to the end of its last one: R rows
+// (M or N) by K, K-contiguous rows `ld` elements apart, or K rows of R
+// elements `ld` apart.
+__host__ __device__ __forceinline__ int64_t operand_bytes(bool kmajor, int64_t R, int64_t K,
+                                                         int64_t ld)
+{
+    if (R <= 0 || K <= 0) return 0;
+    return (kmajor ? (R - 1) * ld + K : (K - 1) * ld + R) * 2;
+}
+
 // DMA plan of a 32-k slab stream: R rows (M or N) x 32 k = R * 4 chunks =
 // R / 16 instructions of 64 chunks, kPer per wave (NW waves); instruction
 // idx = wave * kPer + j fills chunks [idx * 64, idx * 64 + 64).  Slots past
@@ -365,14 +375,16 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_ring_kernel(GemmArgs p, int t
     }
     const int64_t m0 = (int64_t)tm * kBM, n0 = (int64_t)tn * BN;
 
-    const i32x4 da = make_desc(p.A, (uint32_t)(p.M * p.K * 2));
-    const i32x4 db = make_desc(p.B, (uint32_t)(p.N * p.K * 2));
+    const int64_t lda = p.lda ? p.lda : (A_KMAJ ? p.K : p.M);
+    const int64_t ldb = p.ldb ? p.ldb : (B_KMAJ ? p.K : p.N);
+    const i32x4 da = make_desc(p.A, (uint32_t)operand_bytes(A_KMAJ, p.M, p.K, lda));
+    const i32x4 db = make_desc(p.B, (uint32_t)operand_bytes(B_KMAJ, p.N, p.K, ldb));
     PlanU pu;      // A K-major
     PlanA ps;      // A M-major
-    if constexpr (A_KMAJ) pu.init(wave, lane, m0, p.K, p.M, p.K);
-    else ps.init(wave, lane, m0, p.M, p.M, p.K);
+    if constexpr (A_KMAJ) pu.init(wave, lane, m0, lda, p.M, p.K);
+    else ps.init(wave, lane, m0, lda, p.M, p.K);
     PlanB pb;
-    pb.init(wave, lane, n0, B_KMAJ ? p.K : p.N, p.N, p.K);
+    pb.init(wave, lane, n0, ldb, p.N, p.K);
     const uint32_t a_base = lds_addr(sa), b_base = lds_addr(sb), junk_base = lds_addr(junk);
 
     const int wrow_a = wm * kWaveM, wrow_b = wn * kWaveN;
@@ -716,7 +728,11 @@ bool gemm_ring_supported(const GemmArgs& p, Layout layout)
     if (p.batch < 1 || (int64_t)((p.M + kBM - 1) / kBM) * ((p.N + kBN - 1) / kBN) * p.batch >
                            (int64_t(1) << 30))
         return false;
-    return p.M * p.K * 2 <= lim && p.N * p.K * 2 <= lim;
+    const bool ak = layout != Layout::TN, bk = layout == Layout::NT;
+    const int64_t lda = p.lda ? p.lda : (ak ? p.K : p.M);
+    const int64_t ldb = p.ldb ? p.ldb : (bk ? p.K : p.N);
+    if (lda < (ak ? p.K : p.M) || ldb < (bk ? p.K : p.N)) return false;
+    return operand_bytes(ak, p.M, p.K, lda) <= lim && operand_bytes(bk, p.N, p.K, ldb) <= lim;
 }
 
 hipError_t gemm_ring(const GemmArgs& p, Layout layout, Epi epi, Elt out, hipStream_t stream)

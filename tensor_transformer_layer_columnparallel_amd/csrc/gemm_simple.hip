@@ -229,6 +229,7 @@ hipError_t launch(const GemmArgs& p, hipStream_t stream)
 hipError_t gemm_simple(const GemmArgs& p, Elt elt, Layout layout, Epi epi, Elt out,
                        hipStream_t stream)
 {
+    if (p.lda || p.ldb) return hipErrorInvalidValue;   // packed operands only
     if (p.batch > 1) {
         // Batched products: one launch per product.
         if (epi != Epi::Store && epi != Epi::Bias && epi != Epi::BiasGelu)

@@ -113,11 +113,13 @@ bool use_transposed_operands(int64_t tokens, int64_t h, int64_t n, Elt e)
 
 // True when a product of this shape (`batch` of them in one launch) runs on
 // the tile kernel.
-bool ring_path(int64_t M, int64_t N, int64_t K, Elt elt, Layout layout, int64_t batch = 1)
+bool ring_path(int64_t M, int64_t N, int64_t K, Elt elt, Layout layout, int64_t batch = 1,
+               int64_t lda = 0, int64_t ldb = 0)
 {
     GemmArgs p{};
     p.M = M; p.N = N; p.K = K;
     p.batch = batch;
+    p.lda = lda; p.ldb = ldb;
     return elt == Elt::BF16 && M > 0 && N > 0 && gemm_ring_supported(p, layout);
 }
 
@@ -125,7 +127,25 @@ bool ring_path(int64_t M, int64_t N, int64_t K, Elt elt, Layout layout, int64_t 
 // (A, B, C, bias, save), one launch on the tile kernel.
 struct Batch {
     int64_t count = 1, sA = 0, sB = 0, sC = 0, sBias = 0, sSave = 0;
+    int64_t lda = 0, ldb = 0;   // row strides when not packed (tile kernel only)
 };
+
+// Split over K of the x W^T product dX[T][k] = dY[T][n] W[k][n]^T when its
+// output is too few 256 x 192 tiles to fill the GPU (the attention output
+// projection's dX: [2048, 1536], K = 12288, 64 tiles): s products over K
+// ranges of n / s, whose fp32 partials ([s][T][k]) must fit in `scratch_bytes`,
+// are summed in order afterwards.  Returns s (1: no split).
+int64_t dx_split(int64_t tokens, int64_t k, int64_t n, Elt e, int64_t scratch_bytes)
+{
+    if (e != Elt::BF16 || tokens == 0) return 1;
+    const int64_t tiles = ((tokens + 255) / 256) * ((k + 191) / 192);
+    int64_t s = 1;
+    while (s < 8 && tiles * s * 2 <= 256 && n % (32 * s * 2) == 0 &&
+           s * 2 * tokens * k * 4 <= scratch_bytes &&
+           ring_path(tokens, k, n / (s * 2), e, Layout::NT, s * 2, n, n))
+        s *= 2;
+    return s;
+}
 
 // colsum (DGelu on the tile kernel only): per-256-row-block column sums of C.
 hipError_t run_gemm(const void* A, const void* B, void* C, const void* bias, const void* aux,
@@ -138,7 +158,9 @@ hipError_t run_gemm(const void* A, const void* B, void* C, const void* bias, con
     p.batch = batch.count;
     p.sA = batch.sA; p.sB = batch.sB; p.sC = batch.sC;
     p.sBias = batch.sBias; p.sSave = batch.sSave;
-    if (ring_path(M, N, K, elt, layout, batch.count)) return gemm_ring(p, layout, epi, out, stream);
+    p.lda = batch.lda; p.ldb = batch.ldb;
+    if (ring_path(M, N, K, elt, layout, batch.count, batch.lda, batch.ldb))
+        return gemm_ring(p, layout, epi, out, stream);
     return gemm_simple(p, elt, layout, epi, out, stream);
 }
 
@@ -393,6 +415,27 @@ int tp_linear_bwd(const void* X, const void* W, const void* dY, void* dX, void* 
     if (db && (err = column_sum(dY, static_cast<float*>(db), tokens, n, e, dW, k * n * 4, s)) !=
                   hipSuccess)
         return TP_ERR_HIP;
+    // dX split over K: the partials go to dW's memory (written afterwards),
+    // are summed in order into dX, and dW is then computed with the
+    // transposed reads of both operands (no memory is left to stage a
+    // transposed copy).
+    const int64_t split = dx_split(tokens, k, n, e, k * n * 4);
+    if (split > 1) {
+        Batch b;
+        b.count = split;
+        b.sA = n / split;        // dY columns of K range j
+        b.sB = n / split;        // W columns of K range j
+        b.sC = tokens * k;       // partial j
+        b.lda = n;
+        b.ldb = n;
+        if ((err = run_gemm(dY, W, dW, nullptr, nullptr, nullptr, tokens, k, n / split, e,
+                            Layout::NT, Epi::Store, Elt::F32, s, nullptr, b)) != hipSuccess ||
+            (err = shard_sum(dW, dX, tokens * k, tokens * k, (int)split, Elt::F32, Elt::F32,
+                             s)) != hipSuccess)
+            return TP_ERR_HIP;
+        return status_of(run_gemm(X, dY, dW, nullptr, nullptr, nullptr, k, n, tokens, e,
+                                  Layout::TN, Epi::Store, Elt::F32, s));
+    }
     // dW = X^T dY.  Both operands are M/N-contiguous; with bf16 and whole
     // 32-deep slabs of tokens the smaller activation is transposed into dX's
     // memory (written last) first, so that the tile kernel reads a

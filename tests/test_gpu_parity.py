@@ -215,7 +215,9 @@ LINEAR_BWD = [
     # (T, in, out): the weight gradient's path on the device
     (300, 264, 200),   # T % 32 != 0: the tile kernel's TN layout (both operands transposed in LDS)
     (288, 512, 384),   # out <= in: dY^T, product stored transposed
-    (288, 384, 768),   # out > in: X^T
+    (288, 384, 768),   # out > in, dX in two products over K (partials in dW), dW via TN
+    (512, 192, 4096),  # dX too few tiles: eight products over K, summed in order
+    (300, 200, 2048),  # four products over K, ragged M and N tails
     (256, 192, 192),   # below a tile in M: the general kernel
     (64, 136, 520),
     (33, 96, 64),
@@ -239,6 +241,24 @@ def test_linear_bwd_matches_oracle(B, shape, dt):
     g = oracle.linear_bwd(X, W, dY)
     for name, got in (("dX", dX), ("dW", dW), ("db", db)):
         assert_close(got, g[name], dt, f"linear bwd {shape} {dt} {name}")
+
+
+def test_linear_bwd_split_over_k_is_deterministic(B):
+    # the dX products over K ranges and their ordered sum give the same bytes
+    # on every run
+    T, k, n = 512, 192, 4096
+    X = dev(synth.draw((T, k), 1.0, 4, synth.TAG_X, 0, torch.bfloat16))
+    W = dev(synth.draw((k, n), 0.02, 4, synth.TAG_W1, 0, torch.bfloat16))
+    dY = dev(synth.draw((T, n), 1.0, 4, synth.TAG_DZ, 0, torch.bfloat16))
+    outs = []
+    for _ in range(3):
+        dX, dW, db = (torch.empty(T, k, device="cuda"), torch.empty(k, n, device="cuda"),
+                      torch.empty(n, device="cuda"))
+        B.tp_linear_bwd(X, W, dY, dX, dW, db, T, k, n, torch.bfloat16)
+        outs.append((dX, dW, db))
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert all(torch.equal(a, b) for a, b in zip(o, outs[0]))
 
 
 def test_linear_bwd_empty_tokens(B):
