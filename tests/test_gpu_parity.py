@@ -861,6 +861,42 @@ def test_layer_fwd_matches_each_shard_and_the_oracle(B, shape):
     assert_close(Zsum, rZ, dt, "layer fwd: sum of the partials vs the unsharded layer")
 
 
+def test_layer_fwd_stacked_weights_beyond_2gib_sampled(B):
+    """Eight shards of 302 MB weights each: the stacked W1 and W2 are 2.4 GB, so
+    the later shards sit more than 2^31 bytes past the base pointer (64-bit
+    shard offsets); every shard's partial and their sum, on sampled rows,
+    against the oracle shard by shard."""
+    T, h, t = 256, 12288, 8
+    n = 12288
+    ffn = n * t
+    _log(f"case layer fwd, stacked weights of {2 * t * h * n / 2**30:.1f} GiB: drawing on the device")
+    g = torch.Generator(device="cuda").manual_seed(17)
+    bf = torch.bfloat16
+    X = torch.randn(T, h, device="cuda", generator=g).to(bf)
+    W1 = (torch.randn(t, h, n, device="cuda", generator=g) * 0.02).to(bf)
+    W2 = (torch.randn(t, n, h, device="cuda", generator=g) * 0.02).to(bf)
+    b1 = (torch.randn(t, n, device="cuda", generator=g) * 0.02).to(bf)
+    H = torch.empty(t, T, n, dtype=bf, device="cuda")
+    Z = torch.empty(t, T, h, dtype=torch.float32, device="cuda")
+    assert W1.numel() * 2 > 2**31 and W2.numel() * 2 > 2**31
+    B.tp_mlp_layer_fwd(X, W1, b1, W2, H, None, Z, T, h, ffn, t, bf)
+    Zs = torch.empty(T, h, dtype=torch.float32, device="cuda")
+    B.tp_shard_reduce(Z, Zs, T, h, t, B.TP_REDUCE_SUM, torch.float32, torch.float32)
+    torch.cuda.synchronize()
+    rows = sample_indices(T, 3, seed=17)
+    Xr = X[rows].cpu()
+    ref_sum = np.zeros((len(rows), h))
+    for r in range(t):
+        _log(f"case layer fwd beyond 2 GiB: oracle rows {rows.tolist()} of shard {r}")
+        _, rH, rZ = oracle.mlp_shard_fwd(Xr, W1[r].cpu(), b1[r].cpu(), W2[r].cpu())
+        assert_close(H[r][rows], rH, "bf16", f"stacked H[{r}] rows")
+        assert_close(Z[r][rows], rZ, "bf16", f"stacked Z[{r}] rows")
+        ref_sum += rZ
+    assert_close(Zs[rows], ref_sum, "bf16", "stacked layer sum rows")
+    del W1, W2, H, Z
+    torch.cuda.empty_cache()
+
+
 def _nan_padded(x, pad=1 << 16):
     """x on the device, followed inside the same allocation by `pad` NaNs."""
     flat = torch.full((x.numel() + pad,), float("nan"), dtype=x.dtype, device="cuda")
