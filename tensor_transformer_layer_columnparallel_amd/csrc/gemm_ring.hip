@@ -12,16 +12,20 @@
 //   - a K-contiguous A operand in units of 64 k: a unit row is one whole
 //     128-byte line (a 32-k slab would fetch half lines, and half-line DMA
 //     moves half the bytes per cycle); 3 units of 256 x 64 k (96 KiB);
-//   - an M-contiguous A operand and every B operand in 32-k slabs; 5 slabs
-//     each (80 KiB for A, 60 KiB for B).
+//   - a K-contiguous B operand (NT products) in units of 64 k as well, 2
+//     units of 192 x 64 k (48 KiB), each loaded whole at the odd step two
+//     slabs before its first slab is read;
+//   - an M-contiguous A operand and an N-contiguous B operand in 32-k slabs
+//     (whole lines already); 5 slabs each (80 KiB for A, 60 KiB for B).
 // The DMA is issued from inline assembly: the compiler's wait analysis cannot
 // tell the buffers apart and would wait for the DMA just issued before any
 // LDS read.  The waits are explicit instead.  Compute walks K in 32-k slabs;
 // at slab k every wave
 //   1. waits until its loads of slab k+1 have landed (the vector memory
 //      counter retires loads in issue order; every wave issues the same
-//      number of DMA instructions per slab, so the counts are static) and
-//      until its own LDS reads of slab k have returned;
+//      number of DMA instructions per slab, or per odd and per even slab,
+//      so the counts are static) and until its own LDS reads of slab k have
+//      returned;
 //   2. passes a barrier: slab k+1 is in LDS for everybody and nobody reads
 //      slab k's buffers any more;
 //   3. in four groups, each with a share of the DMA instructions, the MFMAs
@@ -249,18 +253,20 @@ struct SlabPlan {
     }
 };
 
-// DMA plan of a K-major 64-k unit stream (A, 256 rows): 256 rows x 128 bytes
-// = 32 instructions of 8 rows; wave w owns kPerUnit = 32 / NW of them,
-// issued in two parts of kPer (part p: w * kPerUnit + p * kPer + j) on
-// consecutive slabs.  Unit u
-// covers k in [64u, 64u + 64); chunks past K are invalidated per lane.
-template <int NW>
+// DMA plan of a K-major 64-k unit stream of ROWS rows (A: 256, or the B of
+// an NT product: 192) in a ring of BUFS units: ROWS rows x 128 bytes =
+// ROWS / 8 instructions of 8 rows; wave w owns kPerUnit = ROWS / 8 / NW of
+// them.  A issues them in two parts of kPer (part p: w * kPerUnit + p * kPer
+// + j) on consecutive slabs, B all at once.  Unit u covers k in [64u, 64u +
+// 64); chunks past K, and units before the first, are invalidated per lane.
+template <int NW, int ROWS = kBM, int BUFS = kUnitBufs>
 struct UnitPlan {
-    static constexpr int kBufBytes = kBM * 64 * 2;
-    static constexpr int kPerUnit = 32 / NW;      // instructions per wave and unit
-    static constexpr int kPer = kPerUnit / 2;     // per wave and slab (half a unit)
+    static_assert(ROWS % (8 * NW) == 0, "whole instructions per wave");
+    static constexpr int kBufBytes = ROWS * 64 * 2;
+    static constexpr int kPerUnit = ROWS / 8 / NW;    // instructions per wave and unit
+    static constexpr int kPer = kPerUnit / 2;         // per wave and slab (half a unit)
     uint32_t voff[kPerUnit];
-    int ulim[kPerUnit];   // units u < ulim hold this lane's chunk inside K
+    int ulim[kPerUnit];   // units 0 <= u < ulim hold this lane's chunk inside K
 
     __device__ __forceinline__ void init(int wave, int lane, int64_t r0, int64_t ld,
                                          int64_t extent, int64_t K)
@@ -275,16 +281,21 @@ struct UnitPlan {
             ulim[q] = ok ? (int)((K - chunk * 8 + 63) / 64) : 0;
         }
     }
+    __device__ __forceinline__ void issue_q(int q, int wave, i32x4 desc, uint32_t ring_base,
+                                            int unit) const
+    {
+        const uint32_t v =
+            unit >= 0 && unit < ulim[q] ? voff[q] + (uint32_t)unit * 128u : kInvalid;
+        const uint32_t buf = (uint32_t)(((unit % BUFS) + BUFS) % BUFS) * kBufBytes;
+        const uint32_t lds = __builtin_amdgcn_readfirstlane(
+            (int)(ring_base + buf + (uint32_t)(wave * kPerUnit + q) * 1024u));
+        dma16(desc, lds, v, 0u);
+    }
     // Instruction j of part `part` of unit `unit` into its ring buffer.
     __device__ __forceinline__ void issue(int part, int j, int wave, i32x4 desc,
                                           uint32_t ring_base, int unit) const
     {
-        const int q = kPer * part + j;
-        const uint32_t v = unit < ulim[q] ? voff[q] + (uint32_t)unit * 128u : kInvalid;
-        const uint32_t buf = (uint32_t)(unit % kUnitBufs) * kBufBytes;
-        const uint32_t lds = __builtin_amdgcn_readfirstlane(
-            (int)(ring_base + buf + (uint32_t)(wave * kPerUnit + q) * 1024u));
-        dma16(desc, lds, v, 0u);
+        issue_q(kPer * part + j, wave, desc, ring_base, unit);
     }
 };
 
@@ -334,11 +345,20 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_ring_kernel(GemmArgs p, int t
     using PlanU = UnitPlan<NW>;              // used when A is K-contiguous
     using PlanA = SlabPlan<false, kBM, NW>;  // used when A is M-contiguous
     using PlanB = SlabPlan<B_KMAJ, BN, NW>;
+    // NT: B K-contiguous too, loaded in whole-line 64-k units (a ring of two)
+    // like A, all of a unit's loads at the odd step two slabs before its first
+    // slab is read.
+#ifndef TPMLP_NT_B_UNITS
+#define TPMLP_NT_B_UNITS 1
+#endif
+    constexpr bool kBUnits = A_KMAJ && B_KMAJ && TPMLP_NT_B_UNITS;
+    using PlanBU = UnitPlan<NW, BN, 2>;
     constexpr int kABytes = A_KMAJ ? kUnitBufs * PlanU::kBufBytes : kSlabBufs * PlanA::kBufBytes;
-    constexpr int kBBytes = kSlabBufs * PlanB::kBufBytes;
+    constexpr int kBBytes = kBUnits ? 2 * PlanBU::kBufBytes : kSlabBufs * PlanB::kBufBytes;
     constexpr int kPerA = A_KMAJ ? PlanU::kPer : PlanA::kPer;   // DMA per wave and slab
-    constexpr int kPerB = PlanB::kPer;
-    constexpr int kDmaStep = kPerA + kPerB;
+    constexpr int kPerB = kBUnits ? PlanBU::kPerUnit : PlanB::kPer;
+    constexpr int kDmaStep = kPerA + kPerB;              // odd steps (all steps without B units)
+    constexpr int kDmaEven = kBUnits ? kPerA : kDmaStep;  // even steps
     __shared__ __attribute__((aligned(1024))) bf16 smem[(kABytes + kBBytes) / 2];
     bf16* const sa = smem;                  // A ring
     bf16* const sb = smem + kABytes / 2;    // B ring
@@ -384,7 +404,9 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_ring_kernel(GemmArgs p, int t
     if constexpr (A_KMAJ) pu.init(wave, lane, m0, lda, p.M, p.K);
     else ps.init(wave, lane, m0, lda, p.M, p.K);
     PlanB pb;
-    pb.init(wave, lane, n0, ldb, p.N, p.K);
+    PlanBU pbu;
+    if constexpr (kBUnits) pbu.init(wave, lane, n0, ldb, p.N, p.K);
+    else pb.init(wave, lane, n0, ldb, p.N, p.K);
     const uint32_t a_base = lds_addr(sa), b_base = lds_addr(sb), junk_base = lds_addr(junk);
 
     const int wrow_a = wm * kWaveM, wrow_b = wn * kWaveN;
@@ -400,10 +422,16 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_ring_kernel(GemmArgs p, int t
     // vs, read for the last time during step vs - 1); a K-major A refills
     // part (vs + 1) mod 2 of unit floor((vs + 1) / 2) + 2 (the buffer of the
     // unit holding slabs vs - 1 and vs, or vs - 2 and vs - 1).
+    // With B units, the B instructions (d >= kPerA) come only at odd steps vs
+    // and load unit (vs + 3) / 2 (unit -1, at the first prologue step, reads
+    // nothing), into the buffer of unit (vs - 1) / 2, whose last slab was read
+    // during step vs - 1.
     auto dma_op = [&](int d, int vs) {
         if (d < kPerA) {
             if constexpr (A_KMAJ) pu.issue((vs + 1) & 1, d, wave, da, a_base, ((vs + 1) >> 1) + kUnitBufs - 1);
             else ps.issue(d, da, a_base, junk_base, vs + kSlabBufs);
+        } else if constexpr (kBUnits) {
+            pbu.issue_q(d - kPerA, wave, db, b_base, (vs + 3) >> 1);
         } else {
             pb.issue(d - kPerA, db, b_base, junk_base, vs + kSlabBufs);
         }
@@ -427,9 +455,14 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_ring_kernel(GemmArgs p, int t
         }
 #pragma unroll
         for (int q = g; q < kFragN; q += kReadGroups) {
-            const bf16* bb = sb + (slab % kSlabBufs) * (PlanB::kBufBytes / 2);
-            if constexpr (B_KMAJ) fb[buf][q] = read_frag_k4(bb, wrow_b + q * 16, lane);
-            else fb[buf][q] = read_frag_mn<BN>(bb, wrow_b + q * 16, lane);
+            if constexpr (kBUnits) {
+                fb[buf][q] = read_frag_k8(sb + ((slab >> 1) & 1) * (PlanBU::kBufBytes / 2),
+                                          wrow_b + q * 16, slab & 1, lane);
+            } else {
+                const bf16* bb = sb + (slab % kSlabBufs) * (PlanB::kBufBytes / 2);
+                if constexpr (B_KMAJ) fb[buf][q] = read_frag_k4(bb, wrow_b + q * 16, lane);
+                else fb[buf][q] = read_frag_mn<BN>(bb, wrow_b + q * 16, lane);
+            }
         }
     };
     auto mfma_group = [&](int g, int buf) {
@@ -447,15 +480,27 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_ring_kernel(GemmArgs p, int t
     // step kt-4 or earlier, except the second half of a K-major A unit
     // starting at an even slab kt+1, issued at step kt-3: for odd kt only two
     // steps of loads may stay outstanding, otherwise three.
+    // With B units: B's unit for slab kt+1 was issued at step kt-2 (kt odd)
+    // or kt-3 (kt even), so only the loads of step kt-1 (an even step) or of
+    // steps kt-2 and kt-1 (one of each) may stay outstanding; that covers A's
+    // loads as well.
     auto slab_step = [&](auto odd, int kt, int cbuf, int nbuf) {
-        if constexpr (A_KMAJ && decltype(odd)::value) wait_vmcnt<kDmaStep * 2>();
-        else wait_vmcnt<kDmaStep * 3>();
+        constexpr bool kOdd = decltype(odd)::value;
+        if constexpr (kBUnits) {
+            if constexpr (kOdd) wait_vmcnt<kDmaEven>();
+            else wait_vmcnt<kDmaEven + kDmaStep>();
+        } else if constexpr (A_KMAJ && kOdd) {
+            wait_vmcnt<kDmaStep * 2>();
+        } else {
+            wait_vmcnt<kDmaStep * 3>();
+        }
         wait_lgkmcnt0();
         barrier();
+        constexpr int kSteps = kOdd ? kDmaStep : kDmaEven;
 #pragma unroll
         for (int g = 0; g < kGroups; ++g) {
 #pragma unroll
-            for (int d = g; d < kDmaStep; d += kGroups) dma_op(d, kt);
+            for (int d = g; d < kSteps; d += kGroups) dma_op(d, kt);
             mfma_group(g, cbuf);
             if (g < kReadGroups) read_group(g, kt + 1, nbuf);
             __builtin_amdgcn_sched_barrier(0);
@@ -467,11 +512,17 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_ring_kernel(GemmArgs p, int t
     const int nk = (int)((p.K + kBK - 1) / kBK);
     if (nk > 0) {
 #pragma unroll
-        for (int vs = -kLead; vs < 0; ++vs)
+        for (int vs = -kLead; vs < 0; ++vs) {
+            const int steps = (vs & 1) ? kDmaStep : kDmaEven;
 #pragma unroll
-            for (int d = 0; d < kDmaStep; ++d) dma_op(d, vs);
-        // Slab 0 came with the first two prologue steps.
-        wait_vmcnt<kDmaStep * (kLead - 2)>();
+            for (int d = 0; d < kDmaStep; ++d)
+                if (d < steps) dma_op(d, vs);
+        }
+        // Slab 0 came with the first two prologue steps (with B units: B's
+        // unit 0 with the third, so only steps -2 and -1 may be outstanding).
+        static_assert(kLead == 5, "prologue parity pattern");
+        if constexpr (kBUnits) wait_vmcnt<kDmaEven + kDmaStep>();
+        else wait_vmcnt<kDmaStep * (kLead - 2)>();
         barrier();
 #pragma unroll
         for (int g = 0; g < kReadGroups; ++g) read_group(g, 0, 0);
