@@ -14,7 +14,9 @@
 //     moves half the bytes per cycle); 3 units of 256 x 64 k (96 KiB);
 //   - a K-contiguous B operand (NT products) in units of 64 k as well, 2
 //     units of 192 x 64 k (48 KiB), each loaded whole at the odd step two
-//     slabs before its first slab is read;
+//     slabs before its first slab is read; A's units then go out whole at
+//     the even steps, so that the steps alternate between A's four loads
+//     and B's three;
 //   - an M-contiguous A operand and an N-contiguous B operand in 32-k slabs
 //     (whole lines already); 5 slabs each (80 KiB for A, 60 KiB for B).
 // The DMA is issued from inline assembly: the compiler's wait analysis cannot
@@ -352,13 +354,21 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_ring_kernel(GemmArgs p, int t
 #define TPMLP_NT_B_UNITS 1
 #endif
     constexpr bool kBUnits = A_KMAJ && B_KMAJ && TPMLP_NT_B_UNITS;
+#ifndef TPMLP_NT_A_WHOLE
+#define TPMLP_NT_A_WHOLE 1
+#endif
+    // With B units, A's unit may also go out whole, at the even steps, so
+    // that even steps carry A's loads and odd steps B's.
+    constexpr bool kAWhole = kBUnits && TPMLP_NT_A_WHOLE;
     using PlanBU = UnitPlan<NW, BN, 2>;
     constexpr int kABytes = A_KMAJ ? kUnitBufs * PlanU::kBufBytes : kSlabBufs * PlanA::kBufBytes;
     constexpr int kBBytes = kBUnits ? 2 * PlanBU::kBufBytes : kSlabBufs * PlanB::kBufBytes;
-    constexpr int kPerA = A_KMAJ ? PlanU::kPer : PlanA::kPer;   // DMA per wave and slab
+    // DMA per wave and step: kPerA of A then kPerB of B at odd steps (every
+    // step without B units), kDmaEven at even steps.
+    constexpr int kPerA = kAWhole ? 0 : (A_KMAJ ? PlanU::kPer : PlanA::kPer);
     constexpr int kPerB = kBUnits ? PlanBU::kPerUnit : PlanB::kPer;
-    constexpr int kDmaStep = kPerA + kPerB;              // odd steps (all steps without B units)
-    constexpr int kDmaEven = kBUnits ? kPerA : kDmaStep;  // even steps
+    constexpr int kDmaStep = kPerA + kPerB;
+    constexpr int kDmaEven = kAWhole ? PlanU::kPerUnit : (kBUnits ? kPerA : kDmaStep);
     __shared__ __attribute__((aligned(1024))) bf16 smem[(kABytes + kBBytes) / 2];
     bf16* const sa = smem;                  // A ring
     bf16* const sb = smem + kABytes / 2;    // B ring
@@ -427,6 +437,14 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_ring_kernel(GemmArgs p, int t
     // nothing), into the buffer of unit (vs - 1) / 2, whose last slab was read
     // during step vs - 1.
     auto dma_op = [&](int d, int vs) {
+        if constexpr (kAWhole) {
+            // even vs: A's unit (vs + 4) / 2, into the buffer of unit
+            // (vs - 2) / 2, whose last slab was read during step vs - 2;
+            // odd vs: B's unit (vs + 3) / 2 as below.
+            if ((vs & 1) == 0) pu.issue_q(d, wave, da, a_base, (vs + 4) >> 1);
+            else pbu.issue_q(d, wave, db, b_base, (vs + 3) >> 1);
+            return;
+        }
         if (d < kPerA) {
             if constexpr (A_KMAJ) pu.issue((vs + 1) & 1, d, wave, da, a_base, ((vs + 1) >> 1) + kUnitBufs - 1);
             else ps.issue(d, da, a_base, junk_base, vs + kSlabBufs);
@@ -514,8 +532,9 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_ring_kernel(GemmArgs p, int t
 #pragma unroll
         for (int vs = -kLead; vs < 0; ++vs) {
             const int steps = (vs & 1) ? kDmaStep : kDmaEven;
+            constexpr int kDmaMax = kDmaStep > kDmaEven ? kDmaStep : kDmaEven;
 #pragma unroll
-            for (int d = 0; d < kDmaStep; ++d)
+            for (int d = 0; d < kDmaMax; ++d)
                 if (d < steps) dma_op(d, vs);
         }
         // Slab 0 came with the first two prologue steps (with B units: B's
