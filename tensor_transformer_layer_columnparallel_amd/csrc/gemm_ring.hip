@@ -17,8 +17,12 @@
 //     slabs before its first slab is read; A's units then go out whole at
 //     the even steps, so that the steps alternate between A's four loads
 //     and B's three;
-//   - an M-contiguous A operand and an N-contiguous B operand in 32-k slabs
-//     (whole lines already); 5 slabs each (80 KiB for A, 60 KiB for B).
+//   - an N-contiguous B operand (NN products) in 32-k slabs (whole lines
+//     already), two at a time at the odd steps (three loads per wave, no
+//     filler) into a ring of 4 slabs (48 KiB), with A's units whole at the
+//     even steps as for NT;
+//   - an M-contiguous A operand (TN products) and its B in 32-k slabs, 5 each
+//     (80 KiB for A, 60 KiB for B).
 // The DMA is issued from inline assembly: the compiler's wait analysis cannot
 // tell the buffers apart and would wait for the DMA just issued before any
 // LDS read.  The waits are explicit instead.  Compute walks K in 32-k slabs;
@@ -301,6 +305,53 @@ struct UnitPlan {
     }
 };
 
+// DMA plan of an N-contiguous B operand (NN products) loaded two 32-k slabs
+// at a time: R columns x 64 k = 2 R / 16 instructions, kPer = 2 R / 16 / NW
+// per wave (no filler slots), each slab laid out as SlabPlan lays it out.
+// Pair v covers k-rows [64v, 64v + 64) and lives in slab buffers 2 (v mod 2)
+// and 2 (v mod 2) + 1 of a ring of four; k-rows past K, and pairs before the
+// first, are invalidated per lane.
+template <int NW, int R>
+struct PairPlan {
+    static constexpr int kSlabInstr = R / 16;
+    static_assert((2 * kSlabInstr) % NW == 0, "whole instructions per wave");
+    static constexpr int kPer = 2 * kSlabInstr / NW;
+    static constexpr int kSlabBytes = R * kBK * 2;
+    uint32_t voff[kPer];
+    uint32_t dst[kPer];   // byte offset inside the pair's two slab buffers
+    int krow[kPer];       // k-row inside the pair
+    uint32_t kstep2;      // bytes from one pair to the next
+    int64_t K;
+
+    __device__ __forceinline__ void init(int wave, int lane, int64_t r0, int64_t ld,
+                                         int64_t extent, int64_t K_)
+    {
+        K = K_;
+        kstep2 = (uint32_t)(2 * kBK * ld * 2);
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            const int idx = wave * kPer + j;
+            const int sl = idx / kSlabInstr, i = idx % kSlabInstr;
+            const int linear = i * 64 + lane;
+            const int kr = linear / (R / 8);
+            const int chunk = mn_logical<R>(kr, linear % (R / 8));
+            krow[j] = kr + kBK * sl;
+            voff[j] = r0 + chunk * 8 < extent
+                          ? (uint32_t)(((int64_t)krow[j] * ld + r0 + chunk * 8) * 2)
+                          : kInvalid;
+            dst[j] = (uint32_t)(sl * kSlabBytes + i * 1024);
+        }
+    }
+    __device__ __forceinline__ void issue(int j, i32x4 desc, uint32_t ring_base, int pair) const
+    {
+        const bool ok = voff[j] != kInvalid && pair >= 0 && (int64_t)pair * 2 * kBK + krow[j] < K;
+        const uint32_t v = ok ? voff[j] + (uint32_t)pair * kstep2 : kInvalid;
+        const uint32_t buf = (uint32_t)(pair & 1) * 2 * kSlabBytes;
+        const uint32_t lds = __builtin_amdgcn_readfirstlane((int)(ring_base + buf + dst[j]));
+        dma16(desc, lds, v, 0u);
+    }
+};
+
 // One fragment of a 32-k slab: 16 rows (M for A, N for B) starting at row0,
 // 8 bf16 per lane (lane l: row l % 16, k 8 (l / 16) .. 8 (l / 16) + 7).
 // K-major 32-k slab buffer.
@@ -359,14 +410,24 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_ring_kernel(GemmArgs p, int t
 #endif
     // With B units, A's unit may also go out whole, at the even steps, so
     // that even steps carry A's loads and odd steps B's.
-    constexpr bool kAWhole = kBUnits && TPMLP_NT_A_WHOLE;
+#ifndef TPMLP_NN_PAIRS
+#define TPMLP_NN_PAIRS 1
+#endif
+    // NN: B's slabs two at a time at the odd steps (three loads per wave, no
+    // filler) and A's unit whole at the even steps, the NT schedule with a
+    // ring of four B slabs.
+    constexpr bool kBPairs = A_KMAJ && !B_KMAJ && TPMLP_NN_PAIRS;
+    constexpr bool kAWhole = (kBUnits && TPMLP_NT_A_WHOLE) || kBPairs;
+    constexpr bool kAlt = kBUnits || kBPairs;   // B's loads only at odd steps
     using PlanBU = UnitPlan<NW, BN, 2>;
+    using PlanBP = PairPlan<NW, BN>;
+    constexpr int kBSlabBufs = kBPairs ? 4 : kSlabBufs;
     constexpr int kABytes = A_KMAJ ? kUnitBufs * PlanU::kBufBytes : kSlabBufs * PlanA::kBufBytes;
-    constexpr int kBBytes = kBUnits ? 2 * PlanBU::kBufBytes : kSlabBufs * PlanB::kBufBytes;
+    constexpr int kBBytes = kBUnits ? 2 * PlanBU::kBufBytes : kBSlabBufs * PlanB::kBufBytes;
     // DMA per wave and step: kPerA of A then kPerB of B at odd steps (every
-    // step without B units), kDmaEven at even steps.
+    // step without B units or pairs), kDmaEven at even steps.
     constexpr int kPerA = kAWhole ? 0 : (A_KMAJ ? PlanU::kPer : PlanA::kPer);
-    constexpr int kPerB = kBUnits ? PlanBU::kPerUnit : PlanB::kPer;
+    constexpr int kPerB = kBUnits ? PlanBU::kPerUnit : (kBPairs ? PlanBP::kPer : PlanB::kPer);
     constexpr int kDmaStep = kPerA + kPerB;
     constexpr int kDmaEven = kAWhole ? PlanU::kPerUnit : (kBUnits ? kPerA : kDmaStep);
     __shared__ __attribute__((aligned(1024))) bf16 smem[(kABytes + kBBytes) / 2];
@@ -415,7 +476,9 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_ring_kernel(GemmArgs p, int t
     else ps.init(wave, lane, m0, lda, p.M, p.K);
     PlanB pb;
     PlanBU pbu;
+    PlanBP pbp;
     if constexpr (kBUnits) pbu.init(wave, lane, n0, ldb, p.N, p.K);
+    else if constexpr (kBPairs) pbp.init(wave, lane, n0, ldb, p.N, p.K);
     else pb.init(wave, lane, n0, ldb, p.N, p.K);
     const uint32_t a_base = lds_addr(sa), b_base = lds_addr(sb), junk_base = lds_addr(junk);
 
@@ -442,7 +505,8 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_ring_kernel(GemmArgs p, int t
             // (vs - 2) / 2, whose last slab was read during step vs - 2;
             // odd vs: B's unit (vs + 3) / 2 as below.
             if ((vs & 1) == 0) pu.issue_q(d, wave, da, a_base, (vs + 4) >> 1);
-            else pbu.issue_q(d, wave, db, b_base, (vs + 3) >> 1);
+            else if constexpr (kBUnits) pbu.issue_q(d, wave, db, b_base, (vs + 3) >> 1);
+            else pbp.issue(d, db, b_base, (vs + 3) >> 1);
             return;
         }
         if (d < kPerA) {
@@ -477,7 +541,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_ring_kernel(GemmArgs p, int t
                 fb[buf][q] = read_frag_k8(sb + ((slab >> 1) & 1) * (PlanBU::kBufBytes / 2),
                                           wrow_b + q * 16, slab & 1, lane);
             } else {
-                const bf16* bb = sb + (slab % kSlabBufs) * (PlanB::kBufBytes / 2);
+                const bf16* bb = sb + (slab % kBSlabBufs) * (PlanB::kBufBytes / 2);
                 if constexpr (B_KMAJ) fb[buf][q] = read_frag_k4(bb, wrow_b + q * 16, lane);
                 else fb[buf][q] = read_frag_mn<BN>(bb, wrow_b + q * 16, lane);
             }
@@ -504,7 +568,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_ring_kernel(GemmArgs p, int t
     // loads as well.
     auto slab_step = [&](auto odd, int kt, int cbuf, int nbuf) {
         constexpr bool kOdd = decltype(odd)::value;
-        if constexpr (kBUnits) {
+        if constexpr (kAlt) {
             if constexpr (kOdd) wait_vmcnt<kDmaEven>();
             else wait_vmcnt<kDmaEven + kDmaStep>();
         } else if constexpr (A_KMAJ && kOdd) {
@@ -540,7 +604,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_ring_kernel(GemmArgs p, int t
         // Slab 0 came with the first two prologue steps (with B units: B's
         // unit 0 with the third, so only steps -2 and -1 may be outstanding).
         static_assert(kLead == 5, "prologue parity pattern");
-        if constexpr (kBUnits) wait_vmcnt<kDmaEven + kDmaStep>();
+        if constexpr (kAlt) wait_vmcnt<kDmaEven + kDmaStep>();
         else wait_vmcnt<kDmaStep * (kLead - 2)>();
         barrier();
 #pragma unroll
