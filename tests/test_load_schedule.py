@@ -1,0 +1,127 @@
+"""CPU replay of the tile kernel's load schedule (host logic, no GPU).
+
+For each layout the kernel uses (NN: B's 32-deep slabs in pairs; NT: both
+operands in 64-deep units; TN: 32-deep slabs), the replay issues every
+step's loads into their ring buffers in program order, applies the step's
+static wait (at most W loads of the wave still outstanding, every earlier
+one retired; all waves issue the same number of loads, so the barrier after
+the wait makes every wave's retired loads visible) and the barrier, and
+records which slab each fragment read sees.  It checks that
+
+  * every fragment read of slab s finds slab s in the buffer it reads, from
+    a load retired before the barrier that precedes the read;
+  * no load refills a buffer before the barrier that follows the last read
+    of what the buffer held;
+  * every step issues the per-parity load count the wait immediates assume.
+
+The schedule restates the kernel's indexing: at even steps vs A's 64-deep
+unit (vs + 4) / 2, four loads per wave, into ring buffer unit mod 3; at odd
+steps B's unit (NT, ring of 2) or slab pair (NN, slabs 2v and 2v + 1 in a
+ring of 4) v = (vs + 3) / 2, three loads per wave; waits of 4 (odd steps)
+and 7 (even steps, and the prologue).  TN: slab vs + 5 of both operands,
+four loads per wave, rings of 5, wait 12.  Fragments of slab s are read
+during step s - 1 (slab 0 after the prologue).
+"""
+import pytest
+
+LEAD = 5          # prologue steps
+A_UNITS = 3       # ring of 64-deep A units (NN, NT)
+SLAB_BUFS = 5     # rings of 32-deep slabs (TN)
+
+
+def step_loads(layout, vs):
+    """(loads per wave at step vs, [(buffer, slabs it will hold)]).  A buffer
+    a step fills is complete only once the step's last load of every wave
+    has retired: the waves split a unit's rows, and for an NN pair waves 0-3
+    fill the first slab and waves 4-7 the second, three loads each."""
+    if layout == "TN":
+        s = vs + SLAB_BUFS
+        return 4, [(("A", s % SLAB_BUFS), (s,)), (("B", s % SLAB_BUFS), (s,))]
+    if vs % 2 == 0:
+        u = (vs + 4) // 2
+        return 4, [(("A", u % A_UNITS), (2 * u, 2 * u + 1))]
+    v = (vs + 3) // 2
+    if layout == "NT":
+        return 3, [(("B", v % 2), (2 * v, 2 * v + 1))]
+    return 3, [(("B", (2 * v) % 4), (2 * v,)), (("B", (2 * v + 1) % 4), (2 * v + 1,))]
+
+
+def slab_reads(layout, s):
+    """[(buffer, slab)] the fragment reads of slab s use."""
+    if layout == "TN":
+        return [(("A", s % SLAB_BUFS), s), (("B", s % SLAB_BUFS), s)]
+    b = ("B", (s // 2) % 2) if layout == "NT" else ("B", s % 4)
+    return [(("A", (s // 2) % A_UNITS), s), (b, s)]
+
+
+def default_wait(layout, kt):
+    if layout == "TN":
+        return 12
+    return 4 if kt % 2 else 7
+
+
+def replay(layout, nk, wait_of=None, prologue_wait=None):
+    wait_of = wait_of or (lambda kt: default_wait(layout, kt))
+    prologue_wait = (12 if layout == "TN" else 7) if prologue_wait is None else prologue_wait
+    issued = 0
+    retired = 0
+    content = {}        # buffer -> (slabs, index of the load that wrote it last)
+    last_read = {}      # buffer -> step during which it was last read
+    counts = {}
+
+    def issue(vs):
+        nonlocal issued
+        n, fills = step_loads(layout, vs)
+        counts.setdefault(vs % 2, set()).add(n)
+        for buf, slabs in fills:
+            assert last_read.get(buf, -10**9) < vs, f"{layout}: step {vs} refills {buf} early"
+            content[buf] = (slabs, issued + n - 1)
+        issued += n
+
+    def read(s, step, visible):
+        for buf, slab in slab_reads(layout, s):
+            slabs, idx = content[buf]
+            assert slab in slabs, f"{layout}: slab {s} not in {buf} (holds {slabs})"
+            assert idx < visible, f"{layout}: slab {s} read before its load retired"
+            last_read[buf] = step
+
+    for vs in range(-LEAD, 0):
+        issue(vs)
+    retired = max(retired, issued - prologue_wait)
+    read(0, -1, retired)
+    for kt in range(nk):
+        retired = max(retired, issued - wait_of(kt))
+        visible = retired                      # the barrier
+        issue(kt)
+        read(kt + 1, kt, visible)
+    return counts
+
+
+@pytest.mark.parametrize("layout", ["NN", "NT", "TN"])
+@pytest.mark.parametrize("nk", [1, 2, 3, 4, 5, 8, 13, 64, 384])
+def test_load_schedule_reads_only_retired_slabs(layout, nk):
+    counts = replay(layout, nk)
+    if layout == "TN":
+        assert counts == {0: {4}, 1: {4}}
+    else:
+        assert counts == {0: {4}, 1: {3}}     # the per-parity counts the waits assume
+
+
+@pytest.mark.parametrize("layout", ["NN", "NT"])
+def test_replay_rejects_one_more_outstanding_load(layout):
+    # Not vacuous, and the waits are tight: one more outstanding load at the
+    # odd steps (the last load of B's unit or pair for the next slab, issued
+    # two steps back, is then not retired) or after the prologue reads
+    # unretired data.  The
+    # even steps' wait never binds: the odd step before it has already
+    # retired everything the even step reads.
+    with pytest.raises(AssertionError, match="before its load retired"):
+        replay(layout, 16, wait_of=lambda kt: 5 if kt % 2 else 7)
+    with pytest.raises(AssertionError, match="before its load retired"):
+        replay(layout, 16, prologue_wait=8)
+    replay(layout, 16, wait_of=lambda kt: 4 if kt % 2 else 10)
+
+
+def test_replay_rejects_one_more_outstanding_load_tn():
+    with pytest.raises(AssertionError, match="before its load retired"):
+        replay("TN", 16, wait_of=lambda kt: 13)
