@@ -75,14 +75,17 @@ constexpr int kBN = 192;
 constexpr int kSlabBufs = 5;                // ring of 32-k slabs (A M-major, B)
 constexpr int kUnitBufs = 3;                // ring of 64-k units (A K-major)
 constexpr int kLead = 5;                    // DMA steps issued before the first slab
-constexpr int kGroups = 4;                  // interleave groups per slab
-// Only the first three groups carry fragment reads, so the last group's
+// Interleave groups per slab, and how many of them carry fragment reads.
+// Only the first three of four groups carry reads, so the last group's
 // MFMAs cover the latency of the last reads before the next barrier (2-3%
 // faster on the NN products than reads in all four groups; reads in two
 // groups or all up front were slower).  Within a group the reads follow the
 // MFMAs (about 1% faster on the row-layer product and the backward than
-// before them, the same on the column product).
-constexpr int kReadGroups = 3;
+// before them, the same on the column product).  The bias + GeLU product
+// (the column layer) measured 0.8% faster with two groups, reads in the
+// first; the other products 1-2% slower with that.
+template <Epi E> constexpr int kGroupsOf = E == Epi::BiasGelu ? 2 : 4;
+template <Epi E> constexpr int kReadGroupsOf = E == Epi::BiasGelu ? 1 : 3;
 constexpr int kXcds = 8;
 constexpr int kCUs = 256;
 
@@ -518,6 +521,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_ring_kernel(GemmArgs p, int t
             pb.issue(d - kPerA, db, b_base, junk_base, vs + kSlabBufs);
         }
     };
+    constexpr int kGroups = kGroupsOf<EPI>, kReadGroups = kReadGroupsOf<EPI>;
     // The work of one slab is cut into kGroups groups, each holding (in this
     // order) the DMA instructions d with d % kGroups == g, the MFMAs of the A
     // fragments a with a % kGroups == g and (for g < kReadGroups) the
