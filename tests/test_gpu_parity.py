@@ -506,6 +506,38 @@ def test_deterministic_rerun(B):
         assert torch.equal(a, b)
 
 
+def test_gpt3_shard_step_is_bitwise_reproducible(B):
+    """The GPT-3-shaped shard's forward and backward (every product layout,
+    384-slab pipelines) three times back to back: every output identical to
+    the bit."""
+    w = configs.GPT3_SHARD
+    T, h, n = w.T, w.h, w.n
+    _log("case full-size step reproducibility")
+    bf = torch.bfloat16
+    g = torch.Generator(device="cuda").manual_seed(23)
+    X = torch.randn(T, h, device="cuda", generator=g).to(bf)
+    W1 = (torch.randn(h, n, device="cuda", generator=g) * 0.02).to(bf)
+    b1 = (torch.randn(n, device="cuda", generator=g) * 0.02).to(bf)
+    W2 = (torch.randn(n, h, device="cuda", generator=g) * 0.02).to(bf)
+    dZ = torch.randn(T, h, device="cuda", generator=g).to(bf)
+    runs = []
+    for _ in range(3):
+        o = {"H": torch.empty(T, n, dtype=bf, device="cuda"),
+             "Y": torch.empty(T, n, dtype=bf, device="cuda"),
+             "Z": torch.empty(T, h, device="cuda"), "dY": torch.empty(T, n, dtype=bf, device="cuda"),
+             "dW2": torch.empty(n, h, device="cuda"), "dW1": torch.empty(h, n, device="cuda"),
+             "dX": torch.empty(T, h, device="cuda"), "db1": torch.empty(n, device="cuda")}
+        B.tp_mlp_shard_fwd(X, W1, b1, W2, o["H"], o["Y"], o["Z"], T, h, w.ffn, w.t, 0, bf)
+        B.tp_mlp_shard_bwd(X, W1, W2, o["Y"], o["H"], dZ, o["dY"], o["dW2"], o["dW1"], o["dX"],
+                           o["db1"], T, h, w.ffn, w.t, 0, bf)
+        runs.append(o)
+    torch.cuda.synchronize()
+    for o in runs[1:]:
+        for k in o:
+            assert torch.equal(o[k], runs[0][k]), f"{k} differs between runs"
+    assert torch.isfinite(runs[0]["dW1"]).all() and torch.count_nonzero(runs[0]["dX"]) > 0
+
+
 def test_side_stream_matches_default_stream(B):
     # Calls only enqueue on the stream they are given: a forward + backward on
     # a separate stream gives the same bytes as on the default stream.
