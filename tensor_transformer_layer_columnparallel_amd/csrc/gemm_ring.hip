@@ -34,10 +34,11 @@
 //      returned;
 //   2. passes a barrier: slab k+1 is in LDS for everybody and nobody reads
 //      slab k's buffers any more;
-//   3. in four groups, each with a share of the DMA instructions, the MFMAs
-//      of a quarter of the A fragments and (in the first three groups) a
-//      share of the fragment reads: refills the freed buffers (5 slabs ahead,
-//      or half of the 64-k unit 2-3 slabs ahead), multiplies slab k
+//   3. in four groups (two for the bias + GeLU product), each with a share
+//      of the DMA instructions, the MFMAs of a share of the A fragments and
+//      (in all groups but the last) a share of the fragment reads: refills
+//      freed buffers (5 slabs ahead on the TN slab rings; 2-3 slabs ahead
+//      for the units and slab pairs of NN and NT), multiplies slab k
 //      (fragments read during slab k-1) and reads the fragments of slab k+1.
 // Spreading the memory instructions over the MFMAs keeps the waves of a SIMD
 // from stalling together on a burst of loads while the matrix pipe idles.
@@ -52,7 +53,7 @@
 // block), the bias gradient's first step.
 //
 // LDS layouts (16-byte chunks permuted per row for conflict-free reads):
-//   K-major 64-k unit [256][64 k]: chunk c of row r at c ^ swz8(r);
+//   K-major 64-k unit [rows][64 k]: chunk c of row r at c ^ swz8(r);
 //   K-major 32-k slab [rows][32 k]: chunk c of row r at c ^ swz4(r);
 //                 both read with ds_read_b128;
 //   MN-major slab [32 k][R cols]: chunk pairs rotated by k-row (R = 256, an A
