@@ -8,38 +8,29 @@
 // 8 XCDs) map to neighbouring tiles on the same XCD and share its L2.
 //
 // Operands are copied L2 -> LDS by buffer_load_dwordx4 ... lds (DMA, no VGPR
-// staging) into rings of buffers:
-//   - a K-contiguous A operand in units of 64 k: a unit row is one whole
-//     128-byte line (a 32-k slab would fetch half lines, and half-line DMA
-//     moves half the bytes per cycle); 3 units of 256 x 64 k (96 KiB);
-//   - a K-contiguous B operand (NT products) in units of 64 k as well, 2
-//     units of 192 x 64 k (48 KiB), each loaded whole at the odd step two
-//     slabs before its first slab is read; A's units then go out whole at
-//     the even steps, so that the steps alternate between A's four loads
-//     and B's three;
-//   - an N-contiguous B operand (NN products) in 32-k slabs (whole lines
-//     already), two at a time at the odd steps (three loads per wave, no
-//     filler) into a ring of 4 slabs (48 KiB), with A's units whole at the
-//     even steps as for NT;
-//   - an M-contiguous A operand (TN products) and its B in 32-k slabs, 5 each
-//     (80 KiB for A, 60 KiB for B).
+// staging) in 64-k blocks: a K-contiguous operand in units of 64 k (a unit
+// row is one whole 128-byte line; a 32-k slab would fetch half lines, and
+// half-line DMA moves half the bytes per cycle), an M/N-contiguous one in
+// pairs of 32-k slabs (each slab row already whole lines).  A's units or
+// pairs fill a ring of three (96 KiB), B's a ring of two (48 KiB).  The
+// steps alternate: all of one A unit or pair at each even step (four loads
+// per wave), all of one B unit or pair at each odd step (three), each two or
+// three slabs before its first slab is read.
 // The DMA is issued from inline assembly: the compiler's wait analysis cannot
 // tell the buffers apart and would wait for the DMA just issued before any
 // LDS read.  The waits are explicit instead.  Compute walks K in 32-k slabs;
 // at slab k every wave
 //   1. waits until its loads of slab k+1 have landed (the vector memory
 //      counter retires loads in issue order; every wave issues the same
-//      number of DMA instructions per slab, or per odd and per even slab,
-//      so the counts are static) and until its own LDS reads of slab k have
-//      returned;
+//      number of DMA instructions per odd and per even slab, so the counts
+//      are static) and until its own LDS reads of slab k have returned;
 //   2. passes a barrier: slab k+1 is in LDS for everybody and nobody reads
 //      slab k's buffers any more;
 //   3. in four groups (two for the bias + GeLU product), each with a share
 //      of the DMA instructions, the MFMAs of a share of the A fragments and
-//      (in all groups but the last) a share of the fragment reads: refills
-//      freed buffers (5 slabs ahead on the TN slab rings; 2-3 slabs ahead
-//      for the units and slab pairs of NN and NT), multiplies slab k
-//      (fragments read during slab k-1) and reads the fragments of slab k+1.
+//      (in all groups but the last) a share of the fragment reads: refills a
+//      freed buffer, multiplies slab k (fragments read during slab k-1) and
+//      reads the fragments of slab k+1.
 // Spreading the memory instructions over the MFMAs keeps the waves of a SIMD
 // from stalling together on a burst of loads while the matrix pipe idles.
 // Loads of elements outside the operands (ragged M/N tails, k past K) use a
@@ -53,9 +44,8 @@
 // block), the bias gradient's first step.
 //
 // LDS layouts (16-byte chunks permuted per row for conflict-free reads):
-//   K-major 64-k unit [rows][64 k]: chunk c of row r at c ^ swz8(r);
-//   K-major 32-k slab [rows][32 k]: chunk c of row r at c ^ swz4(r);
-//                 both read with ds_read_b128;
+//   K-major 64-k unit [rows][64 k]: chunk c of row r at c ^ swz8(r), read
+//                 with ds_read_b128;
 //   MN-major slab [32 k][R cols]: chunk pairs rotated by k-row (R = 256, an A
 //                 operand) or XORed in blocks of four (R = 192, a B operand);
 //                 read with ds_read_b64_tr_b16 (lane i of a 16-lane group
@@ -73,8 +63,8 @@ namespace {
 constexpr int kBM = 256;
 constexpr int kBK = 32;
 constexpr int kBN = 192;
-constexpr int kSlabBufs = 5;                // ring of 32-k slabs (A M-major, B)
-constexpr int kUnitBufs = 3;                // ring of 64-k units (A K-major)
+constexpr int kABufs = 3;                   // A's ring: 64-k units or 32-k slab pairs
+constexpr int kBBufs = 2;                   // B's ring (a power of two)
 constexpr int kLead = 5;                    // DMA steps issued before the first slab
 // Interleave groups per slab, and how many of them carry fragment reads.
 // Only the first three of four groups carry reads, so the last group's
@@ -134,19 +124,10 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p)
     return (uint32_t)reinterpret_cast<uintptr_t>((TP_LDS const void*)p);
 }
 
-// Chunk permutations of K-major buffers (XORs of row bits) for the fragment
-// reads (lane l: row l % 16, chunk l / 16, 16 bytes).
-// swz4 (32-k slabs, 64-byte rows) was chosen by measuring ds_read_b128 with
-// all 256 two-bit XOR forms on the device: only how row bits 2 and 3 enter
-// matters.  With d1 and d2 the chunk XORs of rows 4 and 8 (relative to row
-// 0), reads run at full rate (about 190 B/clk/CU) when d1 != d2 and neither
-// is 1, at 2/3 of it for most other forms (d1 = 1, d2 = 2 ran at 118
-// B/clk/CU and showed as LDS bank-conflict cycles in the NT products), and
-// at 1/3 for d1 = d2 = 1.  This one has d1 = 0, d2 = 2 and measured fastest.
-__device__ __forceinline__ int swz4(int row)
-{
-    return (row & 1) | ((((row >> 1) ^ (row >> 3)) & 1) << 1);
-}
+// Chunk permutation of K-major units (an XOR of row bits) for the fragment
+// reads (lane l: row l % 16, chunk l / 16 (+ 4 for the unit's second slab),
+// 16 bytes), chosen with a bank model; it runs at the full ds_read_b128 rate
+// in a device probe and shows no bank-conflict cycles in the counters.
 __device__ __forceinline__ int swz8(int row)
 {
     return ((row >> 1) & 3) | (((row ^ (row >> 3)) & 1) << 2);
@@ -194,87 +175,17 @@ __host__ __device__ __forceinline__ int64_t operand_bytes(bool kmajor, int64_t R
     return (kmajor ? (R - 1) * ld + K : (K - 1) * ld + R) * 2;
 }
 
-// DMA plan of a 32-k slab stream: R rows (M or N) x 32 k = R * 4 chunks =
-// R / 16 instructions of 64 chunks, kPer per wave (NW waves); instruction
-// idx = wave * kPer + j fills chunks [idx * 64, idx * 64 + 64).  Slots past
-// R / 16 (R = 192 with 8 waves) are dummies that read nothing into a junk
-// LDS area.  K-major rows advance 64
-// bytes per slab (K is a multiple of 32); M/N-major slabs advance 32 rows of
-// the operand, and k-rows past K are invalidated.
-template <bool KMAJ, int R, int NW>
-struct SlabPlan {
-    static constexpr int kInstr = R / 16;
-    static constexpr int kPer = (kInstr + NW - 1) / NW;   // per wave and slab
-    static constexpr int kJunkBytes = (NW * kPer - kInstr + kPer - 1) / kPer * 1024;
-    static constexpr int kBufBytes = R * kBK * 2;
-    uint32_t voff[kPer];
-    uint32_t dst[kPer];   // byte offset inside a buffer (or the junk area)
-    int krow[kPer];
-    bool real[kPer];
-    uint32_t kstep;
-    int nk;
-    int64_t K;
-
-    __device__ __forceinline__ void init(int wave, int lane, int64_t r0, int64_t ld,
-                                         int64_t extent, int64_t K_)
-    {
-        K = K_;
-        nk = (int)((K_ + kBK - 1) / kBK);
-        kstep = KMAJ ? (uint32_t)(kBK * 2) : (uint32_t)(kBK * ld * 2);
-#pragma unroll
-        for (int j = 0; j < kPer; ++j) {
-            const int idx = wave * kPer + j;
-            real[j] = idx < kInstr;
-            const int linear = idx * 64 + lane;
-            krow[j] = 0;
-            if (!real[j]) {
-                voff[j] = kInvalid;
-            } else if (KMAJ) {
-                const int row = linear >> 2;
-                const int chunk = (linear & 3) ^ swz4(row);
-                voff[j] = r0 + row < extent ? (uint32_t)(((r0 + row) * ld + chunk * 8) * 2)
-                                            : kInvalid;
-            } else {
-                krow[j] = linear / (R / 8);
-                const int chunk = mn_logical<R>(krow[j], linear % (R / 8));
-                voff[j] = r0 + chunk * 8 < extent
-                              ? (uint32_t)((krow[j] * ld + r0 + chunk * 8) * 2)
-                              : kInvalid;
-            }
-            dst[j] = real[j] ? (uint32_t)idx * 1024u
-                             : (uint32_t)(idx - kInstr) / kPer * 1024u;
-        }
-    }
-    // Instruction j of slab `slab` into its ring buffer.
-    __device__ __forceinline__ void issue(int j, i32x4 desc, uint32_t ring_base,
-                                          uint32_t junk_base, int slab) const
-    {
-        uint32_t v;
-        if (KMAJ) {
-            v = slab < nk ? voff[j] + (uint32_t)slab * kstep : kInvalid;
-        } else {
-            const bool ok = voff[j] != kInvalid && (int64_t)slab * kBK + krow[j] < K;
-            v = ok ? voff[j] + (uint32_t)slab * kstep : kInvalid;
-        }
-        const uint32_t buf = (uint32_t)(slab % kSlabBufs) * kBufBytes;
-        const uint32_t lds = __builtin_amdgcn_readfirstlane(
-            (int)((real[j] ? ring_base + buf : junk_base) + dst[j]));
-        dma16(desc, lds, v, 0u);
-    }
-};
-
 // DMA plan of a K-major 64-k unit stream of ROWS rows (A: 256, or the B of
 // an NT product: 192) in a ring of BUFS units: ROWS rows x 128 bytes =
 // ROWS / 8 instructions of 8 rows; wave w owns kPerUnit = ROWS / 8 / NW of
-// them.  A issues them in two parts of kPer (part p: w * kPerUnit + p * kPer
-// + j) on consecutive slabs, B all at once.  Unit u covers k in [64u, 64u +
-// 64); chunks past K, and units before the first, are invalidated per lane.
-template <int NW, int ROWS = kBM, int BUFS = kUnitBufs>
+// them (instructions w * kPerUnit + q), all issued at one step.  Unit u
+// covers k in [64u, 64u + 64); chunks past K, and units before the first,
+// are invalidated per lane.
+template <int NW, int ROWS, int BUFS>
 struct UnitPlan {
     static_assert(ROWS % (8 * NW) == 0, "whole instructions per wave");
     static constexpr int kBufBytes = ROWS * 64 * 2;
     static constexpr int kPerUnit = ROWS / 8 / NW;    // instructions per wave and unit
-    static constexpr int kPer = kPerUnit / 2;         // per wave and slab (half a unit)
     uint32_t voff[kPerUnit];
     int ulim[kPerUnit];   // units 0 <= u < ulim hold this lane's chunk inside K
 
@@ -301,21 +212,16 @@ struct UnitPlan {
             (int)(ring_base + buf + (uint32_t)(wave * kPerUnit + q) * 1024u));
         dma16(desc, lds, v, 0u);
     }
-    // Instruction j of part `part` of unit `unit` into its ring buffer.
-    __device__ __forceinline__ void issue(int part, int j, int wave, i32x4 desc,
-                                          uint32_t ring_base, int unit) const
-    {
-        issue_q(kPer * part + j, wave, desc, ring_base, unit);
-    }
 };
 
-// DMA plan of an N-contiguous B operand (NN products) loaded two 32-k slabs
-// at a time: R columns x 64 k = 2 R / 16 instructions, kPer = 2 R / 16 / NW
-// per wave (no filler slots), each slab laid out as SlabPlan lays it out.
-// Pair v covers k-rows [64v, 64v + 64) and lives in slab buffers 2 (v mod 2)
-// and 2 (v mod 2) + 1 of a ring of four; k-rows past K, and pairs before the
-// first, are invalidated per lane.
-template <int NW, int R>
+// DMA plan of an M/N-contiguous operand loaded two 32-k slabs at a time (B
+// of the NN products, A and B of the TN products): R columns x 64 k = 2 R /
+// 16 instructions, kPer = 2 R / 16 / NW per wave (no filler slots), each
+// slab laid out as SlabPlan lays it out.  Pair v covers k-rows [64v, 64v +
+// 64) and lives in slab buffers 2 (v mod BUFS) and 2 (v mod BUFS) + 1 of a
+// ring of 2 BUFS slabs; k-rows past K, and pairs before the first, are
+// invalidated per lane.
+template <int NW, int R, int BUFS>
 struct PairPlan {
     static constexpr int kSlabInstr = R / 16;
     static_assert((2 * kSlabInstr) % NW == 0, "whole instructions per wave");
@@ -350,7 +256,7 @@ struct PairPlan {
     {
         const bool ok = voff[j] != kInvalid && pair >= 0 && (int64_t)pair * 2 * kBK + krow[j] < K;
         const uint32_t v = ok ? voff[j] + (uint32_t)pair * kstep2 : kInvalid;
-        const uint32_t buf = (uint32_t)(pair & 1) * 2 * kSlabBytes;
+        const uint32_t buf = (uint32_t)(((pair % BUFS) + BUFS) % BUFS) * 2 * kSlabBytes;
         const uint32_t lds = __builtin_amdgcn_readfirstlane((int)(ring_base + buf + dst[j]));
         dma16(desc, lds, v, 0u);
     }
@@ -358,12 +264,6 @@ struct PairPlan {
 
 // One fragment of a 32-k slab: 16 rows (M for A, N for B) starting at row0,
 // 8 bf16 per lane (lane l: row l % 16, k 8 (l / 16) .. 8 (l / 16) + 7).
-// K-major 32-k slab buffer.
-__device__ __forceinline__ bf16x8 read_frag_k4(const bf16* buf, int row0, int lane)
-{
-    const int i = lane & 15, g = lane >> 4;
-    return *reinterpret_cast<const bf16x8*>(buf + (row0 + i) * kBK + (g ^ swz4(i)) * 8);
-}
 // K-major 64-k unit buffer, slab half `half`.
 __device__ __forceinline__ bf16x8 read_frag_k8(const bf16* buf, int row0, int half, int lane)
 {
@@ -399,45 +299,25 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_ring_kernel(GemmArgs p, int t
     constexpr int kWavesM = WM, kWavesN = NW / WM;
     constexpr int kWaveM = kBM / kWavesM, kWaveN = BN / kWavesN;
     constexpr int kFragM = kWaveM / 16, kFragN = kWaveN / 16;
-    using PlanU = UnitPlan<NW>;              // used when A is K-contiguous
-    using PlanA = SlabPlan<false, kBM, NW>;  // used when A is M-contiguous
-    using PlanB = SlabPlan<B_KMAJ, BN, NW>;
-    // NT: B K-contiguous too, loaded in whole-line 64-k units (a ring of two)
-    // like A, all of a unit's loads at the odd step two slabs before its first
-    // slab is read.
-#ifndef TPMLP_NT_B_UNITS
-#define TPMLP_NT_B_UNITS 1
-#endif
-    constexpr bool kBUnits = A_KMAJ && B_KMAJ && TPMLP_NT_B_UNITS;
-#ifndef TPMLP_NT_A_WHOLE
-#define TPMLP_NT_A_WHOLE 1
-#endif
-    // With B units, A's unit may also go out whole, at the even steps, so
-    // that even steps carry A's loads and odd steps B's.
-#ifndef TPMLP_NN_PAIRS
-#define TPMLP_NN_PAIRS 1
-#endif
-    // NN: B's slabs two at a time at the odd steps (three loads per wave, no
-    // filler) and A's unit whole at the even steps, the NT schedule with a
-    // ring of four B slabs.
-    constexpr bool kBPairs = A_KMAJ && !B_KMAJ && TPMLP_NN_PAIRS;
-    constexpr bool kAWhole = (kBUnits && TPMLP_NT_A_WHOLE) || kBPairs;
-    constexpr bool kAlt = kBUnits || kBPairs;   // B's loads only at odd steps
-    using PlanBU = UnitPlan<NW, BN, 2>;
-    using PlanBP = PairPlan<NW, BN>;
-    constexpr int kBSlabBufs = kBPairs ? 4 : kSlabBufs;
-    constexpr int kABytes = A_KMAJ ? kUnitBufs * PlanU::kBufBytes : kSlabBufs * PlanA::kBufBytes;
-    constexpr int kBBytes = kBUnits ? 2 * PlanBU::kBufBytes : kBSlabBufs * PlanB::kBufBytes;
-    // DMA per wave and step: kPerA of A then kPerB of B at odd steps (every
-    // step without B units or pairs), kDmaEven at even steps.
-    constexpr int kPerA = kAWhole ? 0 : (A_KMAJ ? PlanU::kPer : PlanA::kPer);
-    constexpr int kPerB = kBUnits ? PlanBU::kPerUnit : (kBPairs ? PlanBP::kPer : PlanB::kPer);
-    constexpr int kDmaStep = kPerA + kPerB;
-    constexpr int kDmaEven = kAWhole ? PlanU::kPerUnit : (kBUnits ? kPerA : kDmaStep);
+    // A: 64-k units (K-contiguous) or pairs of 32-k slabs (M-contiguous) in
+    // a ring of three, all of one unit or pair at each even step; B likewise
+    // (units for NT, slab pairs for NN and TN) in a ring of two at the odd
+    // steps.  The steps alternate between A's loads and B's.
+    using PlanAU = UnitPlan<NW, kBM, kABufs>;
+    using PlanAP = PairPlan<NW, kBM, kABufs>;
+    using PlanBU = UnitPlan<NW, BN, kBBufs>;
+    using PlanBP = PairPlan<NW, BN, kBBufs>;
+    constexpr int kABytes = kABufs * kBM * 64 * 2;   // 96 KiB
+    constexpr int kBBytes = kBBufs * BN * 64 * 2;    // 48 KiB
+    static_assert(PlanAU::kBufBytes == 2 * PlanAP::kSlabBytes &&
+                      PlanBU::kBufBytes == 2 * PlanBP::kSlabBytes,
+                  "a unit and a slab pair take the same bytes");
+    // DMA instructions per wave at even steps (A) and at odd steps (B).
+    constexpr int kDmaEven = A_KMAJ ? PlanAU::kPerUnit : PlanAP::kPer;
+    constexpr int kDmaOdd = B_KMAJ ? PlanBU::kPerUnit : PlanBP::kPer;
     __shared__ __attribute__((aligned(1024))) bf16 smem[(kABytes + kBBytes) / 2];
     bf16* const sa = smem;                  // A ring
     bf16* const sb = smem + kABytes / 2;    // B ring
-    __shared__ __attribute__((aligned(1024))) bf16 junk[(PlanB::kJunkBytes > 0 ? PlanB::kJunkBytes : 1024) / 2];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -474,17 +354,15 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_ring_kernel(GemmArgs p, int t
     const int64_t ldb = p.ldb ? p.ldb : (B_KMAJ ? p.K : p.N);
     const i32x4 da = make_desc(p.A, (uint32_t)operand_bytes(A_KMAJ, p.M, p.K, lda));
     const i32x4 db = make_desc(p.B, (uint32_t)operand_bytes(B_KMAJ, p.N, p.K, ldb));
-    PlanU pu;      // A K-major
-    PlanA ps;      // A M-major
-    if constexpr (A_KMAJ) pu.init(wave, lane, m0, lda, p.M, p.K);
-    else ps.init(wave, lane, m0, lda, p.M, p.K);
-    PlanB pb;
+    PlanAU pau;
+    PlanAP pap;
+    if constexpr (A_KMAJ) pau.init(wave, lane, m0, lda, p.M, p.K);
+    else pap.init(wave, lane, m0, lda, p.M, p.K);
     PlanBU pbu;
     PlanBP pbp;
-    if constexpr (kBUnits) pbu.init(wave, lane, n0, ldb, p.N, p.K);
-    else if constexpr (kBPairs) pbp.init(wave, lane, n0, ldb, p.N, p.K);
-    else pb.init(wave, lane, n0, ldb, p.N, p.K);
-    const uint32_t a_base = lds_addr(sa), b_base = lds_addr(sb), junk_base = lds_addr(junk);
+    if constexpr (B_KMAJ) pbu.init(wave, lane, n0, ldb, p.N, p.K);
+    else pbp.init(wave, lane, n0, ldb, p.N, p.K);
+    const uint32_t a_base = lds_addr(sa), b_base = lds_addr(sb);
 
     const int wrow_a = wm * kWaveM, wrow_b = wn * kWaveN;
     f32x4 acc[kFragM][kFragN];
@@ -494,32 +372,20 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_ring_kernel(GemmArgs p, int t
         for (int b = 0; b < kFragN; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
     bf16x8 fa[2][kFragM], fb[2][kFragN];
 
-    // DMA instruction d (A below kPerA, then B) of step vs (negative in the
-    // prologue).  B and an M-major A refill slab vs + 5 (the buffer of slab
-    // vs, read for the last time during step vs - 1); a K-major A refills
-    // part (vs + 1) mod 2 of unit floor((vs + 1) / 2) + 2 (the buffer of the
-    // unit holding slabs vs - 1 and vs, or vs - 2 and vs - 1).
-    // With B units, the B instructions (d >= kPerA) come only at odd steps vs
-    // and load unit (vs + 3) / 2 (unit -1, at the first prologue step, reads
-    // nothing), into the buffer of unit (vs - 1) / 2, whose last slab was read
-    // during step vs - 1.
+    // DMA instruction d of step vs (negative in the prologue).  Even vs: A's
+    // unit or pair (vs + 4) / 2, into the buffer of (vs - 2) / 2, whose last
+    // slab (vs - 1) was read during step vs - 2.  Odd vs: B's unit or pair
+    // (vs + 3) / 2, into the buffer of (vs - 1) / 2, whose last slab (vs)
+    // was read during step vs - 1.  Each lands two or three slabs before its
+    // first slab is read; B's unit or pair -1, at the first prologue step,
+    // reads nothing and keeps the prologue in the same pattern.
     auto dma_op = [&](int d, int vs) {
-        if constexpr (kAWhole) {
-            // even vs: A's unit (vs + 4) / 2, into the buffer of unit
-            // (vs - 2) / 2, whose last slab was read during step vs - 2;
-            // odd vs: B's unit (vs + 3) / 2 as below.
-            if ((vs & 1) == 0) pu.issue_q(d, wave, da, a_base, (vs + 4) >> 1);
-            else if constexpr (kBUnits) pbu.issue_q(d, wave, db, b_base, (vs + 3) >> 1);
-            else pbp.issue(d, db, b_base, (vs + 3) >> 1);
-            return;
-        }
-        if (d < kPerA) {
-            if constexpr (A_KMAJ) pu.issue((vs + 1) & 1, d, wave, da, a_base, ((vs + 1) >> 1) + kUnitBufs - 1);
-            else ps.issue(d, da, a_base, junk_base, vs + kSlabBufs);
-        } else if constexpr (kBUnits) {
-            pbu.issue_q(d - kPerA, wave, db, b_base, (vs + 3) >> 1);
+        if ((vs & 1) == 0) {
+            if constexpr (A_KMAJ) pau.issue_q(d, wave, da, a_base, (vs + 4) >> 1);
+            else pap.issue(d, da, a_base, (vs + 4) >> 1);
         } else {
-            pb.issue(d - kPerA, db, b_base, junk_base, vs + kSlabBufs);
+            if constexpr (B_KMAJ) pbu.issue_q(d, wave, db, b_base, (vs + 3) >> 1);
+            else pbp.issue(d, db, b_base, (vs + 3) >> 1);
         }
     };
     constexpr int kGroups = kGroupsOf<EPI>, kReadGroups = kReadGroupsOf<EPI>;
@@ -534,22 +400,20 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_ring_kernel(GemmArgs p, int t
 #pragma unroll
         for (int a = g; a < kFragM; a += kReadGroups) {
             if constexpr (A_KMAJ)
-                fa[buf][a] = read_frag_k8(sa + ((slab >> 1) % kUnitBufs) * (PlanU::kBufBytes / 2),
+                fa[buf][a] = read_frag_k8(sa + ((slab >> 1) % kABufs) * (kBM * 64),
                                           wrow_a + a * 16, slab & 1, lane);
             else
-                fa[buf][a] = read_frag_mn<kBM>(sa + (slab % kSlabBufs) * (PlanA::kBufBytes / 2),
+                fa[buf][a] = read_frag_mn<kBM>(sa + (slab % (2 * kABufs)) * (kBM * kBK),
                                                wrow_a + a * 16, lane);
         }
 #pragma unroll
         for (int q = g; q < kFragN; q += kReadGroups) {
-            if constexpr (kBUnits) {
-                fb[buf][q] = read_frag_k8(sb + ((slab >> 1) & 1) * (PlanBU::kBufBytes / 2),
+            if constexpr (B_KMAJ)
+                fb[buf][q] = read_frag_k8(sb + ((slab >> 1) & (kBBufs - 1)) * (BN * 64),
                                           wrow_b + q * 16, slab & 1, lane);
-            } else {
-                const bf16* bb = sb + (slab % kBSlabBufs) * (PlanB::kBufBytes / 2);
-                if constexpr (B_KMAJ) fb[buf][q] = read_frag_k4(bb, wrow_b + q * 16, lane);
-                else fb[buf][q] = read_frag_mn<BN>(bb, wrow_b + q * 16, lane);
-            }
+            else
+                fb[buf][q] = read_frag_mn<BN>(sb + (slab % (2 * kBBufs)) * (BN * kBK),
+                                              wrow_b + q * 16, lane);
         }
     };
     auto mfma_group = [&](int g, int buf) {
@@ -563,27 +427,17 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_ring_kernel(GemmArgs p, int t
     // Slab kt: wait for slab kt+1 (own loads, then everybody's via the
     // barrier, which also retires every wave's reads of slab kt), then refill
     // while multiplying slab kt (fragments read during the previous slab) and
-    // reading the fragments of slab kt+1.  Slab kt+1's loads were issued at
-    // step kt-4 or earlier, except the second half of a K-major A unit
-    // starting at an even slab kt+1, issued at step kt-3: for odd kt only two
-    // steps of loads may stay outstanding, otherwise three.
-    // With B units: B's unit for slab kt+1 was issued at step kt-2 (kt odd)
-    // or kt-3 (kt even), so only the loads of step kt-1 (an even step) or of
-    // steps kt-2 and kt-1 (one of each) may stay outstanding; that covers A's
-    // loads as well.
+    // reading the fragments of slab kt+1.  B's loads for slab kt+1 were
+    // issued at step kt-2 (kt odd) or kt-3 (kt even), A's at step kt-3 or
+    // kt-2, so only the loads of step kt-1 (an even step, kt odd) or of
+    // steps kt-2 and kt-1 (one of each, kt even) may stay outstanding.
     auto slab_step = [&](auto odd, int kt, int cbuf, int nbuf) {
         constexpr bool kOdd = decltype(odd)::value;
-        if constexpr (kAlt) {
-            if constexpr (kOdd) wait_vmcnt<kDmaEven>();
-            else wait_vmcnt<kDmaEven + kDmaStep>();
-        } else if constexpr (A_KMAJ && kOdd) {
-            wait_vmcnt<kDmaStep * 2>();
-        } else {
-            wait_vmcnt<kDmaStep * 3>();
-        }
+        if constexpr (kOdd) wait_vmcnt<kDmaEven>();
+        else wait_vmcnt<kDmaEven + kDmaOdd>();
         wait_lgkmcnt0();
         barrier();
-        constexpr int kSteps = kOdd ? kDmaStep : kDmaEven;
+        constexpr int kSteps = kOdd ? kDmaOdd : kDmaEven;
 #pragma unroll
         for (int g = 0; g < kGroups; ++g) {
 #pragma unroll
@@ -598,19 +452,18 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_ring_kernel(GemmArgs p, int t
 
     const int nk = (int)((p.K + kBK - 1) / kBK);
     if (nk > 0) {
+        static_assert(kLead == 5, "prologue parity pattern");
 #pragma unroll
         for (int vs = -kLead; vs < 0; ++vs) {
-            const int steps = (vs & 1) ? kDmaStep : kDmaEven;
-            constexpr int kDmaMax = kDmaStep > kDmaEven ? kDmaStep : kDmaEven;
+            constexpr int kDmaMax = kDmaOdd > kDmaEven ? kDmaOdd : kDmaEven;
+            const int steps = (vs & 1) ? kDmaOdd : kDmaEven;
 #pragma unroll
             for (int d = 0; d < kDmaMax; ++d)
                 if (d < steps) dma_op(d, vs);
         }
-        // Slab 0 came with the first two prologue steps (with B units: B's
-        // unit 0 with the third, so only steps -2 and -1 may be outstanding).
-        static_assert(kLead == 5, "prologue parity pattern");
-        if constexpr (kAlt) wait_vmcnt<kDmaEven + kDmaStep>();
-        else wait_vmcnt<kDmaStep * (kLead - 2)>();
+        // Slab 0 came with steps -4 (A) and -3 (B): only steps -2 and -1 may
+        // be outstanding.
+        wait_vmcnt<kDmaEven + kDmaOdd>();
         barrier();
 #pragma unroll
         for (int g = 0; g < kReadGroups; ++g) read_group(g, 0, 0);
@@ -810,25 +663,6 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_ring_kernel(GemmArgs p, int t
     }
 }
 
-#ifndef TPMLP_RING_NW_NN
-#define TPMLP_RING_NW_NN 8
-#endif
-#ifndef TPMLP_RING_WM_NN
-#define TPMLP_RING_WM_NN 2
-#endif
-#ifndef TPMLP_RING_NW_NT
-#define TPMLP_RING_NW_NT 8
-#endif
-#ifndef TPMLP_RING_WM_NT
-#define TPMLP_RING_WM_NT 2
-#endif
-#ifndef TPMLP_RING_NW_TN
-#define TPMLP_RING_NW_TN 8
-#endif
-#ifndef TPMLP_RING_WM_TN
-#define TPMLP_RING_WM_TN 4
-#endif
-
 // NW waves per workgroup, WM of them along M (and NW / WM along N).  Four
 // waves (one per SIMD, 256 x 48 or 128 x 96 outputs each) read less LDS per
 // flop but measured about 35% slower than eight: with one wave per SIMD
@@ -836,8 +670,8 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_ring_kernel(GemmArgs p, int t
 template <bool AK, bool BK, Epi E, typename O>
 hipError_t launch(const GemmArgs& p, hipStream_t stream)
 {
-    constexpr int NW = AK ? (BK ? TPMLP_RING_NW_NT : TPMLP_RING_NW_NN) : TPMLP_RING_NW_TN;
-    constexpr int WM = AK ? (BK ? TPMLP_RING_WM_NT : TPMLP_RING_WM_NN) : TPMLP_RING_WM_TN;
+    constexpr int NW = 8;
+    constexpr int WM = AK ? 2 : 4;   // TN: 4 x 2 waves (its A fragments in four groups)
     const int tm = (int)((p.M + kBM - 1) / kBM);
     const int tn = (int)((p.N + kBN - 1) / kBN);
     // Products with several waves of tiles walk an XCD's tiles in 4-row

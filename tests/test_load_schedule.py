@@ -1,9 +1,9 @@
 """CPU replay of the tile kernel's load schedule (host logic, no GPU).
 
 For each layout the kernel uses (NN: B's 32-deep slabs in pairs; NT: both
-operands in 64-deep units; TN: 32-deep slabs), the replay issues every
-step's loads into their ring buffers in program order, applies the step's
-static wait (at most W loads of the wave still outstanding, every earlier
+operands in 64-deep units; TN: both operands' slabs in pairs), the replay
+issues every step's loads into their ring buffers in program order, applies
+the step's static wait (at most W loads of the wave still outstanding, every earlier
 one retired; all waves issue the same number of loads, so the barrier after
 the wait makes every wave's retired loads visible) and the barrier, and
 records which slab each fragment read sees.  It checks that
@@ -18,51 +18,51 @@ The schedule restates the kernel's indexing: at even steps vs A's 64-deep
 unit (vs + 4) / 2, four loads per wave, into ring buffer unit mod 3; at odd
 steps B's unit (NT, ring of 2) or slab pair (NN, slabs 2v and 2v + 1 in a
 ring of 4) v = (vs + 3) / 2, three loads per wave; waits of 4 (odd steps)
-and 7 (even steps, and the prologue).  TN: slab vs + 5 of both operands,
-four loads per wave, rings of 5, wait 12.  Fragments of slab s are read
-during step s - 1 (slab 0 after the prologue).
+and 7 (even steps, and the prologue).  TN: at even steps A's slab pair
+(slabs 2u and 2u + 1, u = (vs + 4) / 2, in a ring of 6 slabs), four loads
+per wave, at odd steps B's pair as for NN, the same waits.  Fragments of
+slab s are read during step s - 1 (slab 0 after the prologue).
 """
 import pytest
 
 LEAD = 5          # prologue steps
 A_UNITS = 3       # ring of 64-deep A units (NN, NT)
-SLAB_BUFS = 5     # rings of 32-deep slabs (TN)
+A_SLABS = 6       # ring of 32-deep A slabs (TN)
+B_SLABS = 4       # ring of 32-deep B slabs (NN, TN)
 
 
 def step_loads(layout, vs):
     """(loads per wave at step vs, [(buffer, slabs it will hold)]).  A buffer
     a step fills is complete only once the step's last load of every wave
     has retired: the waves split a unit's rows, and for an NN pair waves 0-3
-    fill the first slab and waves 4-7 the second, three loads each."""
-    if layout == "TN":
-        s = vs + SLAB_BUFS
-        return 4, [(("A", s % SLAB_BUFS), (s,)), (("B", s % SLAB_BUFS), (s,))]
+    fill the first slab and waves 4-7 the second, three loads each (TN's A
+    pair: four each)."""
     if vs % 2 == 0:
         u = (vs + 4) // 2
+        if layout == "TN":
+            return 4, [(("A", (2 * u) % A_SLABS), (2 * u,)),
+                       (("A", (2 * u + 1) % A_SLABS), (2 * u + 1,))]
         return 4, [(("A", u % A_UNITS), (2 * u, 2 * u + 1))]
     v = (vs + 3) // 2
     if layout == "NT":
         return 3, [(("B", v % 2), (2 * v, 2 * v + 1))]
-    return 3, [(("B", (2 * v) % 4), (2 * v,)), (("B", (2 * v + 1) % 4), (2 * v + 1,))]
+    return 3, [(("B", (2 * v) % B_SLABS), (2 * v,)), (("B", (2 * v + 1) % B_SLABS), (2 * v + 1,))]
 
 
 def slab_reads(layout, s):
     """[(buffer, slab)] the fragment reads of slab s use."""
-    if layout == "TN":
-        return [(("A", s % SLAB_BUFS), s), (("B", s % SLAB_BUFS), s)]
-    b = ("B", (s // 2) % 2) if layout == "NT" else ("B", s % 4)
-    return [(("A", (s // 2) % A_UNITS), s), (b, s)]
+    a = ("A", s % A_SLABS) if layout == "TN" else ("A", (s // 2) % A_UNITS)
+    b = ("B", (s // 2) % 2) if layout == "NT" else ("B", s % B_SLABS)
+    return [(a, s), (b, s)]
 
 
 def default_wait(layout, kt):
-    if layout == "TN":
-        return 12
     return 4 if kt % 2 else 7
 
 
 def replay(layout, nk, wait_of=None, prologue_wait=None):
     wait_of = wait_of or (lambda kt: default_wait(layout, kt))
-    prologue_wait = (12 if layout == "TN" else 7) if prologue_wait is None else prologue_wait
+    prologue_wait = 7 if prologue_wait is None else prologue_wait
     issued = 0
     retired = 0
     content = {}        # buffer -> (slabs, index of the load that wrote it last)
@@ -101,13 +101,10 @@ def replay(layout, nk, wait_of=None, prologue_wait=None):
 @pytest.mark.parametrize("nk", [1, 2, 3, 4, 5, 8, 13, 64, 384])
 def test_load_schedule_reads_only_retired_slabs(layout, nk):
     counts = replay(layout, nk)
-    if layout == "TN":
-        assert counts == {0: {4}, 1: {4}}
-    else:
-        assert counts == {0: {4}, 1: {3}}     # the per-parity counts the waits assume
+    assert counts == {0: {4}, 1: {3}}     # the per-parity counts the waits assume
 
 
-@pytest.mark.parametrize("layout", ["NN", "NT"])
+@pytest.mark.parametrize("layout", ["NN", "NT", "TN"])
 def test_replay_rejects_one_more_outstanding_load(layout):
     # Not vacuous, and the waits are tight: one more outstanding load at the
     # odd steps (the last load of B's unit or pair for the next slab, issued
@@ -121,7 +118,3 @@ def test_replay_rejects_one_more_outstanding_load(layout):
         replay(layout, 16, prologue_wait=8)
     replay(layout, 16, wait_of=lambda kt: 4 if kt % 2 else 10)
 
-
-def test_replay_rejects_one_more_outstanding_load_tn():
-    with pytest.raises(AssertionError, match="before its load retired"):
-        replay("TN", 16, wait_of=lambda kt: 13)
