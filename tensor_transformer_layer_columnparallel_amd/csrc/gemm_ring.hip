@@ -77,6 +77,13 @@ constexpr int kLead = 5;                    // DMA steps issued before the first
 // first; the other products 1-2% slower with that.
 template <Epi E> constexpr int kGroupsOf = E == Epi::BiasGelu ? 2 : 4;
 template <Epi E> constexpr int kReadGroupsOf = E == Epi::BiasGelu ? 1 : 3;
+// The fragment reads of the next slab issue at raised wave priority
+// (s_setprio 1), so that a wave whose reads are due gets them out ahead of
+// its SIMD partner's MFMAs: 3-4% faster on the row-layer product and about
+// 1% on the backward; the bias + GeLU product measured about 1% slower and
+// keeps the default priority.  Raising the MFMAs' or the DMA's priority
+// instead measured no gain or slower.
+template <Epi E> constexpr bool kUrgentReadsOf = E != Epi::BiasGelu;
 constexpr int kXcds = 8;
 constexpr int kCUs = 256;
 
@@ -443,7 +450,11 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_ring_kernel(GemmArgs p, int t
 #pragma unroll
             for (int d = g; d < kSteps; d += kGroups) dma_op(d, kt);
             mfma_group(g, cbuf);
-            if (g < kReadGroups) read_group(g, kt + 1, nbuf);
+            if (g < kReadGroups) {
+                if constexpr (kUrgentReadsOf<EPI>) __builtin_amdgcn_s_setprio(1);
+                read_group(g, kt + 1, nbuf);
+                if constexpr (kUrgentReadsOf<EPI>) __builtin_amdgcn_s_setprio(0);
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
     };
