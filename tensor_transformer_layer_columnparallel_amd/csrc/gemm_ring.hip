@@ -26,11 +26,11 @@
 //      are static) and until its own LDS reads of slab k have returned;
 //   2. passes a barrier: slab k+1 is in LDS for everybody and nobody reads
 //      slab k's buffers any more;
-//   3. in four groups (two for the bias + GeLU product), each with a share
-//      of the DMA instructions, the MFMAs of a share of the A fragments and
-//      (in all groups but the last) a share of the fragment reads: refills a
-//      freed buffer, multiplies slab k (fragments read during slab k-1) and
-//      reads the fragments of slab k+1.
+//   3. in four groups, each with a share of the DMA instructions, the MFMAs
+//      of a share of the A fragments and (in all groups but the last) a
+//      share of the fragment reads, the reads at raised wave priority:
+//      refills a freed buffer, multiplies slab k (fragments read during slab
+//      k-1) and reads the fragments of slab k+1.
 // Spreading the memory instructions over the MFMAs keeps the waves of a SIMD
 // from stalling together on a burst of loads while the matrix pipe idles.
 // Loads of elements outside the operands (ragged M/N tails, k past K) use a
@@ -72,18 +72,15 @@ constexpr int kLead = 5;                    // DMA steps issued before the first
 // faster on the NN products than reads in all four groups; reads in two
 // groups or all up front were slower).  Within a group the reads follow the
 // MFMAs (about 1% faster on the row-layer product and the backward than
-// before them, the same on the column product).  The bias + GeLU product
-// (the column layer) measured 0.8% faster with two groups, reads in the
-// first; the other products 1-2% slower with that.
-template <Epi E> constexpr int kGroupsOf = E == Epi::BiasGelu ? 2 : 4;
-template <Epi E> constexpr int kReadGroupsOf = E == Epi::BiasGelu ? 1 : 3;
+// before them, the same on the column product).
+constexpr int kGroups = 4;
+constexpr int kReadGroups = 3;
 // The fragment reads of the next slab issue at raised wave priority
 // (s_setprio 1), so that a wave whose reads are due gets them out ahead of
-// its SIMD partner's MFMAs: 3-4% faster on the row-layer product and about
-// 1% on the backward; the bias + GeLU product measured about 1% slower and
-// keeps the default priority.  Raising the MFMAs' or the DMA's priority
-// instead measured no gain or slower.
-template <Epi E> constexpr bool kUrgentReadsOf = E != Epi::BiasGelu;
+// its SIMD partner's MFMAs: 3-4% faster on the row-layer product, 3% on the
+// bias + GeLU product (which at the default priority ran best with two
+// groups, reads in the first) and 1-1.5% on the backward.  Raising the
+// MFMAs' or the DMA's priority instead measured no gain or slower.
 constexpr int kXcds = 8;
 constexpr int kCUs = 256;
 
@@ -395,7 +392,6 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_ring_kernel(GemmArgs p, int t
             else pbp.issue(d, db, b_base, (vs + 3) >> 1);
         }
     };
-    constexpr int kGroups = kGroupsOf<EPI>, kReadGroups = kReadGroupsOf<EPI>;
     // The work of one slab is cut into kGroups groups, each holding (in this
     // order) the DMA instructions d with d % kGroups == g, the MFMAs of the A
     // fragments a with a % kGroups == g and (for g < kReadGroups) the
@@ -451,9 +447,9 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_ring_kernel(GemmArgs p, int t
             for (int d = g; d < kSteps; d += kGroups) dma_op(d, kt);
             mfma_group(g, cbuf);
             if (g < kReadGroups) {
-                if constexpr (kUrgentReadsOf<EPI>) __builtin_amdgcn_s_setprio(1);
+                __builtin_amdgcn_s_setprio(1);
                 read_group(g, kt + 1, nbuf);
-                if constexpr (kUrgentReadsOf<EPI>) __builtin_amdgcn_s_setprio(0);
+                __builtin_amdgcn_s_setprio(0);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
