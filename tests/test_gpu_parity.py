@@ -261,6 +261,35 @@ def test_linear_bwd_split_over_k_is_deterministic(B):
         assert all(torch.equal(a, b) for a, b in zip(o, outs[0]))
 
 
+@pytest.mark.parametrize("shape", [(2047, 4096, 3072), (1000, 1536, 12288)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_linear_bwd_ragged_tokens_large_sampled(B, shape):
+    """Token counts that are not whole 32-deep slabs put the weight gradient
+    on the TN products (both operands read transposed, slab pairs with a
+    ragged last pair): 2047 tokens over 16 x 16 tiles, and 1000 tokens after
+    dX split into eight products over K.  Sampled rows of dX and columns of
+    dW and db against the oracle."""
+    T, k, n = shape
+    _log(f"case linear bwd ragged tokens {shape}")
+    X = synth.draw((T, k), 1.0, 6, synth.TAG_X, 0, torch.bfloat16)
+    W = synth.draw((k, n), 0.02, 6, synth.TAG_W1, 0, torch.bfloat16)
+    dY = synth.draw((T, n), 1.0, 6, synth.TAG_DZ, 0, torch.bfloat16)
+    dX = torch.full((T, k), float("nan"), device="cuda")
+    dW = torch.full((k, n), float("nan"), device="cuda")
+    db = torch.full((n,), float("nan"), device="cuda")
+    B.tp_linear_bwd(dev(X), dev(W), dev(dY), dX, dW, db, T, k, n, B.TP_BF16)
+    torch.cuda.synchronize()
+    assert not torch.isnan(dW).any() and not torch.isnan(dX).any()
+    rows = sample_indices(T, 4, seed=21)
+    cols = sample_indices(n, 6, seed=22)
+    _log(f"case linear bwd ragged tokens {shape} rows {rows.tolist()} cols {cols.tolist()}")
+    g = oracle.linear_bwd(X[rows], W, dY[rows], with_db=False)
+    assert_close(dX[rows], g["dX"], "bf16", f"{shape} dX rows")
+    g = oracle.linear_bwd(X, W[:, cols], dY[:, cols])
+    assert_close(dW[:, cols], g["dW"], "bf16", f"{shape} dW cols")
+    assert_close(db[cols], g["db"], "bf16", f"{shape} db cols")
+
+
 def test_linear_bwd_empty_tokens(B):
     k, n = 64, 128
     ph = torch.empty(8, dtype=torch.bfloat16, device="cuda")   # [0, *] arrays have no storage
