@@ -118,3 +118,27 @@ def test_replay_rejects_one_more_outstanding_load(layout):
         replay(layout, 16, prologue_wait=8)
     replay(layout, 16, wait_of=lambda kt: 4 if kt % 2 else 10)
 
+
+
+def test_replay_constants_match_the_kernel_source():
+    # The replay restates the kernel's ring sizes, lead and per-wave load
+    # counts; read them from the source so that the two cannot drift apart.
+    import os
+    import re
+    src = open(os.path.join(os.path.dirname(__file__), "..",
+                            "tensor_transformer_layer_columnparallel_amd", "csrc",
+                            "gemm_ring.hip")).read()
+
+    def const(name):
+        m = re.search(r"constexpr int %s = (\d+);" % name, src)
+        assert m, name
+        return int(m.group(1))
+
+    a_bufs, b_bufs, lead = const("kABufs"), const("kBBufs"), const("kLead")
+    bm, bn, bk, nw = const("kBM"), const("kBN"), const("kBK"), const("NW")
+    assert (a_bufs, 2 * a_bufs, 2 * b_bufs, lead) == (A_UNITS, A_SLABS, B_SLABS, LEAD)
+    # loads per wave: a 64-deep unit of R rows is R / 8 loads of 8 rows, a
+    # slab pair 2 R / 16 loads of 64 16-byte chunks; both R * 64 * 2 bytes
+    assert bk == 32
+    assert bm // 8 // nw == 2 * bm // 16 // nw == 4     # even steps (A)
+    assert bn // 8 // nw == 2 * bn // 16 // nw == 3     # odd steps (B)
