@@ -40,9 +40,9 @@
 // stores to HBM cover whole row segments (transposed on the way, for a
 // result stored as C^T), written with non-temporal stores (the backward 2%
 // faster; they measured slower for the stores below); other results are
-// stored from the registers, four consecutive columns per lane.  The GeLU' epilogue can also sum its fp32
-// results per column in a fixed order (one row of partials per 256-row
-// block), the bias gradient's first step.
+// stored from the registers, four consecutive columns per lane.  The GeLU'
+// epilogue can also sum its fp32 results per column in a fixed order (one
+// row of partials per 256-row block), the bias gradient's first step.
 //
 // LDS layouts (16-byte chunks permuted per row for conflict-free reads):
 //   K-major 64-k unit [rows][64 k]: chunk c of row r at c ^ swz8(r), read
@@ -220,13 +220,14 @@ struct UnitPlan {
     }
 };
 
-// DMA plan of an M/N-contiguous operand loaded two 32-k slabs at a time (B
-// of the NN products, A and B of the TN products): R columns x 64 k = 2 R /
-// 16 instructions, kPer = 2 R / 16 / NW per wave (no filler slots), each
-// slab laid out as SlabPlan lays it out.  Pair v covers k-rows [64v, 64v +
-// 64) and lives in slab buffers 2 (v mod BUFS) and 2 (v mod BUFS) + 1 of a
-// ring of 2 BUFS slabs; k-rows past K, and pairs before the first, are
-// invalidated per lane.
+// DMA plan of an M/N-contiguous operand loaded two 32-k slabs at a time (B of
+// the NN products, A and B of the TN products): R columns x 64 k = 2 R / 16
+// instructions, kPer = 2 R / 16 / NW per wave (no filler slots).  A slab is
+// [32 k][R] with its 16-byte chunks permuted per k-row (mn_phys); its
+// instruction i fills chunks [64 i, 64 i + 64).  Pair v covers k-rows
+// [64v, 64v + 64) and lives in slab buffers 2 (v mod BUFS) and
+// 2 (v mod BUFS) + 1 of a ring of 2 BUFS slabs; k-rows past K, and pairs
+// before the first, are invalidated per lane.
 template <int NW, int R, int BUFS>
 struct PairPlan {
     static constexpr int kSlabInstr = R / 16;
@@ -433,9 +434,10 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_ring_kernel(GemmArgs p, int t
     // barrier, which also retires every wave's reads of slab kt), then refill
     // while multiplying slab kt (fragments read during the previous slab) and
     // reading the fragments of slab kt+1.  B's loads for slab kt+1 were
-    // issued at step kt-2 (kt odd) or kt-3 (kt even), A's at step kt-3 or
-    // kt-2, so only the loads of step kt-1 (an even step, kt odd) or of
-    // steps kt-2 and kt-1 (one of each, kt even) may stay outstanding.
+    // issued at step kt-2 (kt odd) or kt-3 (kt even), A's at step kt-3 (kt
+    // odd) or kt-4 (kt even), so only the loads of step kt-1 (an even step,
+    // kt odd) or of steps kt-2 and kt-1 (one of each, kt even) may stay
+    // outstanding.
     auto slab_step = [&](auto odd, int kt, int cbuf, int nbuf) {
         constexpr bool kOdd = decltype(odd)::value;
         if constexpr (kOdd) wait_vmcnt<kDmaEven>();
