@@ -156,6 +156,47 @@ def ingest_mfma(pmc_dir: str, simds: int = 1024, xcds: int = 8):
 
 
 
+def ingest_pmc(pmc_dir: str, xcds: int = 8, cus: int = 256):
+    """Markdown table from one rocprofv3 --pmc run: per GEMM kernel instance
+    (and the activation transpose), the mean per dispatch of every counter
+    collected (rocprofv3 sums a counter over its hardware instances), and
+    each one divided by the GPU-active cycles of all CUs (GRBM_GUI_ACTIVE,
+    summed over the XCDs, / XCDs x CUs) when that counter was collected: for
+    a counter of cycles per CU or per SQ that is the fraction of the
+    kernel's active time it covers."""
+    import csv
+    import glob
+    disp = {}
+    for path in glob.glob(os.path.join(pmc_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                k = row["Kernel_Name"]
+                if "gemm" not in k and "transpose" not in k:
+                    continue
+                d = disp.setdefault(row["Dispatch_Id"], {
+                    "name": k, "ns": int(row["End_Timestamp"]) - int(row["Start_Timestamp"])})
+                c, v = row["Counter_Name"], float(row["Counter_Value"])
+                d[c] = d.get(c, 0.0) + v
+    if not disp:
+        raise SystemExit(f"no GEMM dispatches under {pmc_dir}")
+    per = {}
+    for d in disp.values():
+        per.setdefault(d["name"], []).append(d)
+    names = sorted({c for d in disp.values() for c in d if c not in ("name", "ns")})
+    print("| kernel | dispatches | duration us | " + " | ".join(names) + " |")
+    print("|---|---|---|" + "---|" * len(names))
+    for name, ds in sorted(per.items(), key=lambda kv: -len(kv[1])):
+        mean = lambda k: sum(d.get(k, 0.0) for d in ds) / len(ds)
+        act = mean("GRBM_GUI_ACTIVE") / xcds
+        cells = []
+        for c in names:
+            v = mean(c)
+            frac = f" ({v / (act * cus):.3f})" if act and c != "GRBM_GUI_ACTIVE" else ""
+            cells.append(f"{v:.4g}{frac}")
+        short = name if len(name) <= 90 else name[:87] + "..."
+        print(f"| `{short}` | {len(ds)} | {mean('ns') / 1e3:.1f} | " + " | ".join(cells) + " |")
+
+
 def copy_calibration(reps: int):
     """A plain device copy of known size (8192 x 8192 fp32 = 256 MiB read and
     written), issued through the library's concatenation with t = 1."""
@@ -171,15 +212,18 @@ def copy_calibration(reps: int):
     log(f"copy calibration: {reps} copies of {COPY_ROWS * COPY_COLS * 4} bytes")
 
 
-def warm(fn, ms: float = 80.0):
+def warm(fn, ms: float = 80.0) -> int:
     """Calls fn back to back for about `ms` milliseconds of device time, so
-    that the measurement after it starts at the sustained engine clock."""
+    that the measurement after it starts at the sustained engine clock.
+    Returns the number of calls."""
     import torch
-    t0 = time.perf_counter()
+    t0, calls = time.perf_counter(), 0
     while (time.perf_counter() - t0) * 1e3 < ms:
         for _ in range(4):
             fn()
+        calls += 4
         torch.cuda.synchronize()
+    return calls
 
 
 def trace_summary(trace_dir: str, warmup: int, steps: int):
@@ -429,6 +473,88 @@ def full_layer(B, stream, sptr, reps=5):
     return out
 
 
+def small_configs(B, stream, reps=50):
+    """The two small workloads, each timed after 80 ms of warm-up calls with
+    HIP events on the launch stream, both as `reps` eager calls and as the
+    same calls captured once in a HIP graph and replayed (the graph removes
+    the host's launch gaps, which dominate at these sizes):
+      tiny fp32 MLP, t = 2: both shards' forward (tp_mlp_shard_fwd) and the
+        fp32 shard sum (tp_shard_reduce) of the two partials;
+      column-parallel linear 768 -> 3072, t = 4, rank 0, bf16: one
+        tp_column_linear call, X [4096, 768] x W_0 [768, 768], bf16 output."""
+    import torch
+    from tensor_transformer_layer_columnparallel_amd import configs, synth
+    f32, bf = torch.float32, torch.bfloat16
+    dev = "cuda"
+
+    w1 = configs.TINY_F32
+    d = synth.make_inputs(w1)
+    X = d["X"].to(dev)
+    W1 = [d["W1"][r].to(dev) for r in w1.ranks]
+    b1 = [d["b1"][r].to(dev) for r in w1.ranks]
+    W2 = [d["W2"][r].to(dev) for r in w1.ranks]
+    H = [torch.empty(w1.T, w1.n, device=dev) for _ in w1.ranks]
+    parts = torch.empty(w1.t, w1.T, w1.h, device=dev)
+    Z = torch.empty(w1.T, w1.h, device=dev)
+
+    def c1(st):
+        for r in w1.ranks:
+            B.tp_mlp_shard_fwd(X, W1[r], b1[r], W2[r], H[r], None, parts[r], w1.T, w1.h, w1.ffn,
+                               w1.t, r, f32, stream=st.cuda_stream)
+        B.tp_shard_reduce(parts, Z, w1.T, w1.h, w1.t, B.TP_REDUCE_SUM, f32, f32,
+                          stream=st.cuda_stream)
+
+    w2 = configs.COLUMN_768
+    d2 = synth.make_inputs(w2)
+    X2, Wc, bc = d2["X"].to(dev), d2["W1"][0].to(dev), d2["b1"][0].to(dev)
+    Y2 = torch.empty(w2.T, w2.n, dtype=bf, device=dev)
+
+    def c2(st):
+        B.tp_column_linear(X2, Wc, bc, Y2, None, w2.T, w2.h, w2.ffn, w2.t, 0, bf, bf,
+                           B.TP_ACT_NONE, stream=st.cuda_stream)
+
+    def timed(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        warm(lambda: fn(stream))
+        e0.record(stream)
+        for _ in range(reps):
+            fn(stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        eager_us = e0.elapsed_time(e1) / reps * 1e3
+        # The same calls captured in a HIP graph on a side stream, replayed on
+        # the launch stream.
+        g, cap = torch.cuda.CUDAGraph(), torch.cuda.Stream()
+        cap.wait_stream(stream)
+        with torch.cuda.graph(g, stream=cap):
+            for _ in range(reps):
+                fn(cap)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            warm(g.replay)
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return eager_us, e0.elapsed_time(e1) / reps * 1e3
+
+    out = {}
+    for name, f, flops, what in (
+            ("tiny_mlp_f32_t2", c1, w1.fwd_flops(),
+             f"tiny fp32 MLP, t={w1.t}, both shards: X[{w1.T},{w1.h}], W1_r[{w1.h},{w1.n}], "
+             f"W2_r[{w1.n},{w1.h}]; two tp_mlp_shard_fwd + tp_shard_reduce SUM (5 kernels)"),
+            ("column_linear_768", c2, w2.fwd_flops(),
+             f"column-parallel linear 768->3072, t={w2.t}, rank 0: X[{w2.T},{w2.h}] x "
+             f"W_0[{w2.h},{w2.n}], bf16 out, no activation; one tp_column_linear")):
+        eager_us, graph_us = timed(f)
+        tf = flops / (graph_us * 1e-6) / 1e12
+        out[name] = {"workload": what, "flops": flops, "eager_us": round(eager_us, 2),
+                     "graph_us": round(graph_us, 2), "tflops_graph": round(tf, 3),
+                     "pct_peak_graph": round(100 * tf / PEAK_BF16_TFLOPS, 2)}
+    out["reps"] = reps
+    return out
+
+
 def cpu_baseline(w, d_h, seconds: float):
     """Times the fp64 oracle on a bounded sample: chunks of 32 token rows of
     the same workload, each chunk a full forward + backward (6 products) of
@@ -466,11 +592,16 @@ def main():
     # sustained clock while the power control catches up.  40 warm-up steps
     # (about 70 ms) put the timed steps in the sustained state.
     ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--warmup-ms", type=float, default=100.0,
+                    help="after the warm-up steps, keep calling the step for at least this "
+                         "long (device time), whatever --warmup is")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="wall-clock budget of the oracle baseline (0 disables it)")
     ap.add_argument("--no-reduce", action="store_true", help="skip the shard-sum measurement")
     ap.add_argument("--no-sp", action="store_true",
                     help="skip the sequence-parallel stand-ins")
+    ap.add_argument("--no-small", action="store_true",
+                    help="skip the tiny fp32 MLP and the 768 -> 3072 column layer")
     ap.add_argument("--no-attention", action="store_true",
                     help="skip the attention-projection measurement")
     ap.add_argument("--no-full-layer", action="store_true",
@@ -487,12 +618,18 @@ def main():
                     help="per-kernel durations from a rocprofv3 --kernel-trace CSV of a bench "
                          "run with these warm-up and timed step counts: over all dispatches "
                          "and inside the timed steps")
+    ap.add_argument("--ingest-pmc", metavar="PMC_DIR",
+                    help="every counter of a rocprofv3 --pmc run per GEMM kernel, and its "
+                         "ratio to the CUs' GPU-active cycles")
     ap.add_argument("--ingest-mfma", metavar="PMC_DIR",
                     help="MFMA work, busy fraction and clock per GEMM from a rocprofv3 --pmc run "
                          "of " + " ".join(MFMA_COUNTERS))
     args = ap.parse_args()
     if args.ingest_mfma:
         ingest_mfma(args.ingest_mfma)
+        return
+    if args.ingest_pmc:
+        ingest_pmc(args.ingest_pmc)
         return
     if args.trace_summary:
         trace_summary(args.trace_summary[0], int(args.trace_summary[1]),
@@ -554,10 +691,16 @@ def main():
         if ev is not None:
             ev[3].record(stream)
 
-    log(f"warmup {args.warmup} steps")
+    log(f"warmup {args.warmup} steps, then at least {args.warmup_ms:.0f} ms of steps")
+    wall0 = time.perf_counter()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    warmup_steps = args.warmup
+    if args.warmup_ms > 0:
+        warmup_steps += warm(step, args.warmup_ms)
+    warmup_ms = (time.perf_counter() - wall0) * 1e3
+    log(f"warm-up: {warmup_steps} steps in {warmup_ms:.0f} ms")
 
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -592,7 +735,9 @@ def main():
                           f"{gemm / 1e9:.1f} GFLOP per launch"}
 
     out = {"metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
-           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+           "steps": args.steps, "warmup": args.warmup, "warmup_steps_run": warmup_steps,
+           "warmup_ms": round(warmup_ms, 1),
+           "ms_per_step": round(ms_step, 4),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
            "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights)",
            "config": {"workload": "gpt3-shaped MLP shard fwd+bwd, rank 0 of t=8",
@@ -607,6 +752,13 @@ def main():
            "device": {"name": props.name, "cus": props.multi_processor_count,
                       "max_engine_clock_mhz": clock_mhz}}
     del H, Y, Z, dY, dW2, dW1, dX, db1
+
+    if not args.no_small:
+        out["small_configs"] = small_configs(B, stream)
+        sc = out["small_configs"]
+        log("small configs: " + ", ".join(f"{k} {v['eager_us']:.1f} us eager, "
+                                         f"{v['graph_us']:.1f} us graph"
+                                         for k, v in sc.items() if isinstance(v, dict)))
 
     if not args.no_attention:
         out["attention_shard"] = attention_shard(B, configs.ATTN_GPT3, stream, sptr)

@@ -1,7 +1,10 @@
 """GPU parity: every entry point of libtpmlp against the fp64 oracle on the
-same seeded inputs.  Reduced sizes are compared element by element (several
-tiles plus ragged tails); full workload sizes are compared on sampled rows
-and columns the oracle computes directly."""
+same seeded inputs, element by element: reduced sizes (several tiles plus
+ragged tails) and the full workload sizes (the GPT-3 shard's forward and
+backward, the full-layer emulation's summed output, the GPT-3 attention
+shard).  Only the cases at the boundary's largest accepted operands, and two
+large ragged-token backward shapes, are compared on sampled rows and columns
+the oracle computes directly."""
 import sys
 
 import numpy as np
@@ -9,8 +12,8 @@ import pytest
 import torch
 
 import oracle
-from parity_utils import (assert_close, dev, gpu_shard_bwd, gpu_shard_fwd, sample_indices,
-                          to_device, to_np64)
+from parity_utils import (assert_close, dev, gpu_shard_bwd, gpu_shard_fwd, max_ratio,
+                          sample_indices, to_device, to_np64)
 from tensor_transformer_layer_columnparallel_amd import configs, synth
 
 pytestmark = pytest.mark.gpu
@@ -24,6 +27,14 @@ def B():
 
 def _log(msg):
     print(msg, file=sys.stderr, flush=True)
+
+
+def _whole(got, ref, dtype, what):
+    """Compares a whole output tensor with the oracle's and logs the two
+    error measures the tolerance is stated in."""
+    rf = assert_close(got, ref, dtype, what)
+    _log(f"parity {what}: rel_fro {rf:.3e} max_ratio {max_ratio(got, ref):.3e} "
+         f"({to_np64(ref).size} elements)")
 
 
 def _unsharded(inputs, ranks):
@@ -191,9 +202,10 @@ def test_attention_output_projection_small(B):
     assert_close(Z, oracle.row_linear(d["O"], d["Wo"]), "bf16", f"{aw.name} O W_o")
 
 
-def test_attention_gpt3_shard_sampled(B):
+def test_attention_gpt3_shard_whole_tensors(B):
     """GPT-3-shaped attention shard (96 heads, t = 8, rank 3) at full size,
-    in the bench's launch configuration, on sampled rows."""
+    in the bench's launch configuration, on every element of the QKV output
+    and of the output projection's fp32 partial."""
     aw = configs.ATTN_GPT3
     r = aw.ranks[0]
     _log(f"case {aw.name} rank {r}")
@@ -204,11 +216,8 @@ def test_attention_gpt3_shard_sampled(B):
     assert B.tp_row_linear(dev(s["O"]), dev(s["Wo"]), Z, aw.T, aw.h, aw.h, aw.t, r, B.TP_BF16,
                            B.TP_F32) == 0
     torch.cuda.synchronize()
-    rows = sample_indices(aw.T, 4, seed=7)
-    assert_close(Y[rows], oracle.column_linear(d["X"][rows], s["Wqkv"], s["bqkv"]), "bf16",
-                 f"{aw.name} QKV rows")
-    assert_close(Z[rows], oracle.row_linear(s["O"][rows], s["Wo"]), "bf16",
-                 f"{aw.name} out-proj rows")
+    _whole(Y, oracle.column_linear(d["X"], s["Wqkv"], s["bqkv"]), "bf16", f"{aw.name} QKV")
+    _whole(Z, oracle.row_linear(s["O"], s["Wo"]), "bf16", f"{aw.name} out-proj")
 
 
 LINEAR_BWD = [
@@ -302,12 +311,11 @@ def test_linear_bwd_empty_tokens(B):
     assert torch.count_nonzero(dW) == 0 and torch.count_nonzero(db) == 0
 
 
-def test_attention_gpt3_backward_sampled(B):
+def test_attention_gpt3_backward_whole_tensors(B):
     """Backward of rank 3's GPT-3-shaped attention projections (QKV on head
-    boundaries: out <= in, dY^T path; output projection: out > in, X^T path)
-    on sampled rows of dX and columns of dW / db.  Rows of dX depend only on
-    the same rows of dY, and columns of dW and db only on the same columns of
-    dY (and of W), so the oracle runs on those subsets."""
+    boundaries: out <= in, dY^T path; output projection: out > in, dX over
+    four K ranges and dW on the TN product) on every element of dX, dW and
+    db."""
     aw = configs.ATTN_GPT3
     r = aw.ranks[0]
     T, h, w = aw.T, aw.h, aw.w
@@ -323,18 +331,13 @@ def test_attention_gpt3_backward_sampled(B):
     dO = torch.empty(T, w, device="cuda"); dWo = torch.empty(w, h, device="cuda")
     B.tp_linear_bwd(dev(s["O"]), dev(s["Wo"]), dev(gr["dZ"]), dO, dWo, None, T, w, h, B.TP_BF16)
     torch.cuda.synchronize()
-    rows = sample_indices(T, 4, seed=9)
-    cq, co = sample_indices(n, 5, seed=10), sample_indices(h, 5, seed=11)
-    _log(f"case {aw.name} backward rows {rows.tolist()} cols {cq.tolist()} {co.tolist()}")
-    g = oracle.linear_bwd(d["X"][rows], s["Wqkv"], dQ[rows], with_db=False)
-    assert_close(dX[rows], g["dX"], "bf16", "QKV dX rows")
-    g = oracle.linear_bwd(d["X"], s["Wqkv"][:, cq], dQ[:, cq])
-    assert_close(dW[:, cq], g["dW"], "bf16", "QKV dW cols")
-    assert_close(db[cq], g["db"], "bf16", "QKV db")
-    g = oracle.linear_bwd(s["O"][rows], s["Wo"], gr["dZ"][rows], with_db=False)
-    assert_close(dO[rows], g["dX"], "bf16", "out-proj dO rows")
-    g = oracle.linear_bwd(s["O"], s["Wo"][:, co], gr["dZ"][:, co], with_db=False)
-    assert_close(dWo[:, co], g["dW"], "bf16", "out-proj dW cols")
+    g = oracle.linear_bwd(d["X"], s["Wqkv"], dQ)
+    _whole(dX, g["dX"], "bf16", "QKV dX")
+    _whole(dW, g["dW"], "bf16", "QKV dW")
+    _whole(db, g["db"], "bf16", "QKV db")
+    g = oracle.linear_bwd(s["O"], s["Wo"], gr["dZ"], with_db=False)
+    _whole(dO, g["dX"], "bf16", "out-proj dO")
+    _whole(dWo, g["dW"], "bf16", "out-proj dW")
 
 
 def test_row_partials_in_bf16_then_summed_in_fp32(B):
@@ -721,32 +724,65 @@ def gpt3_run(B):
     return w, d_h, out
 
 
-def test_gpt3_shard_forward_sampled(gpt3_run):
+def test_gpt3_shard_forward_whole_tensors(gpt3_run):
+    # The GPT-3 shard's forward (configuration 3) against the oracle on every
+    # element of Y_i, H_i and Z_i.
     w, d_h, out = gpt3_run
-    rows = sample_indices(w.T, 6, seed=1)
-    _log(f"case {w.name} fwd rows {rows.tolist()}")
-    rY, rH, rZ = oracle.mlp_shard_fwd_rows(d_h["X"], d_h["W1"][0], d_h["b1"][0], d_h["W2"][0],
-                                           rows)
-    assert_close(out["Y"][rows], rY, "bf16", "gpt3 Y rows")
-    assert_close(out["H"][rows], rH, "bf16", "gpt3 H rows")
-    assert_close(out["Z"][rows], rZ, "bf16", "gpt3 Z rows")
+    _log(f"case {w.name}: oracle forward (whole tensors)")
+    rY, rH, rZ = oracle.mlp_shard_fwd(d_h["X"], d_h["W1"][0], d_h["b1"][0], d_h["W2"][0])
+    _whole(out["Y"], rY, "bf16", "gpt3 Y")
+    _whole(out["H"], rH, "bf16", "gpt3 H")
+    _whole(out["Z"], rZ, "bf16", "gpt3 Z")
 
 
-def test_gpt3_shard_backward_sampled(gpt3_run):
+def test_gpt3_shard_backward_whole_tensors(gpt3_run):
+    # The GPT-3 shard's backward (configuration 4) against the oracle on every
+    # element of dY_i, dW2_i, dW1_i, dX_i and db1_i.  The weight gradients
+    # (1536 tiles each) take the grouped tile walk.
     w, d_h, out = gpt3_run
-    rows = sample_indices(w.T, 4, seed=2)
-    cols = sample_indices(w.n, 6, seed=3)
-    _log(f"case {w.name} bwd rows {rows.tolist()} cols {cols.tolist()}")
-    gr = oracle.mlp_shard_bwd_rows(d_h["X"], d_h["W1"][0], d_h["b1"][0], d_h["W2"][0],
-                                   d_h["dZ"], rows)
-    assert_close(out["dY"][rows], gr["dY"], "bf16", "gpt3 dY rows")
-    assert_close(out["dX"][rows], gr["dX"], "bf16", "gpt3 dX rows")
-    gc = oracle.mlp_shard_bwd_cols(d_h["X"], d_h["W1"][0], d_h["b1"][0], d_h["W2"][0],
-                                   d_h["dZ"], cols)
-    assert_close(out["dY"][:, cols], gc["dY"], "bf16", "gpt3 dY cols")
-    assert_close(out["dW1"][:, cols], gc["dW1"], "bf16", "gpt3 dW1 cols")
-    assert_close(out["dW2"][cols, :], gc["dW2"], "bf16", "gpt3 dW2 rows")
-    assert_close(out["db1"][cols], gc["db1"], "bf16", "gpt3 db1")
+    _log(f"case {w.name}: oracle backward (whole tensors)")
+    g = oracle.mlp_shard_bwd(d_h["X"], d_h["W1"][0], d_h["b1"][0], d_h["W2"][0], d_h["dZ"])
+    for k in ("dY", "dW2", "dW1", "dX", "db1"):
+        _whole(out[k], g[k], "bf16", f"gpt3 {k}")
+
+
+@pytest.mark.parametrize("T,k,n", [(1000, 96, 24920), (1024, 24920, 992)],
+                         ids=["column_row_1000x96x24920", "linear_bwd_1024x24920x992"])
+def test_grouped_tile_walk_elementwise(B, T, k, n):
+    # Products of more than two waves of 256 x 192 tiles walk each XCD's
+    # tiles in groups of four tile rows.  Here 4 x 130 = 520 tiles (a multiple
+    # of the 8 XCDs, so the XCD remap applies as well), with ragged M and N
+    # tails, compared element by element:
+    #   (1000, 96, 24920): the column layer (bias + GeLU, Y saved) and the row
+    #     layer's plain fp32 product, both NN;
+    #   (1024, 24920, 992): a linear shard's backward, whose dX is an NT
+    #     product and whose dW is dY^T X stored transposed (NN, M = 992).
+    bf = torch.bfloat16
+    g = torch.Generator().manual_seed(T + k + n)
+    r = lambda *sh, std=1.0: (torch.randn(*sh, generator=g) * std).to(bf)
+    if k == 96:
+        X, W, b = r(T, k), r(k, n, std=0.02), r(n, std=0.02)
+        H = torch.empty(T, n, dtype=bf, device="cuda")
+        Y = torch.empty(T, n, dtype=bf, device="cuda")
+        Z = torch.empty(T, n, dtype=torch.float32, device="cuda")
+        Xd, Wd, bd = dev(X), dev(W), dev(b)
+        B.tp_column_linear(Xd, Wd, bd, H, Y, T, k, n, 1, 0, bf, bf, B.TP_ACT_GELU_TANH)
+        B.tp_row_linear(Xd, Wd, Z, T, k, n, 1, 0, bf, torch.float32)
+        torch.cuda.synchronize()
+        _whole(Y, oracle.column_linear(X, W, b), "bf16", "grouped walk: column Y")
+        _whole(H, oracle.column_linear(X, W, b, gelu=True), "bf16", "grouped walk: column H")
+        _whole(Z, oracle.row_linear(X, W), "bf16", "grouped walk: row Z")
+    else:
+        X, W, dY = r(T, k), r(k, n, std=0.02), r(T, n)
+        dX = torch.empty(T, k, dtype=torch.float32, device="cuda")
+        dW = torch.empty(k, n, dtype=torch.float32, device="cuda")
+        db = torch.empty(n, dtype=torch.float32, device="cuda")
+        B.tp_linear_bwd(dev(X), dev(W), dev(dY), dX, dW, db, T, k, n, bf)
+        torch.cuda.synchronize()
+        ref = oracle.linear_bwd(X, W, dY)
+        _whole(dX, ref["dX"], "bf16", "grouped walk: dX")
+        _whole(dW, ref["dW"], "bf16", "grouped walk: dW")
+        _whole(db, ref["db"], "bf16", "grouped walk: db")
 
 
 MAX_OPERAND_BYTES = 2**31 - 1   # the boundary rejects any larger operand
@@ -823,7 +859,7 @@ def test_largest_accepted_fp32_outputs_fwd_bwd_sampled(B):
     assert_close(out["db1"][cols], gc["db1"], "bf16", "largest fp32: db1")
 
 
-def test_full_layer_emulation_8_shards_sampled(B):
+def test_full_layer_emulation_8_shards_whole_output(B):
     w = configs.FULL_LAYER_8
     _log(f"case {w.name}: generating inputs")
     d_h = synth.make_inputs(w)
@@ -855,11 +891,13 @@ def test_full_layer_emulation_8_shards_sampled(B):
     Zc = Z.cpu()
     del d, parts, parts_b, W1s, W2s, Hs
     torch.cuda.empty_cache()
-    rows = sample_indices(w.T, 4, seed=4)
-    _log(f"case {w.name}: unsharded oracle rows {rows.tolist()}")
+    # The summed layer output (configuration 5) against the unsharded oracle,
+    # X [4096, 8192] through W1 [8192, 28672] and W2 [28672, 8192], on every
+    # element.
+    _log(f"case {w.name}: unsharded oracle (whole output)")
     W1, b1, W2 = _unsharded(d_h, w.ranks)
-    _, _, rZ = oracle.mlp_shard_fwd_rows(d_h["X"], W1, b1, W2, rows)
-    assert_close(Zc[rows], rZ, "bf16", "full layer Z rows")
+    _, _, rZ = oracle.mlp_shard_fwd(d_h["X"], W1, b1, W2)
+    _whole(Zc, rZ, "bf16", "full layer Z")
 
 
 LAYER_FWD = [  # (tokens, h, ffn, t, dtype, bias, save)
@@ -1068,10 +1106,10 @@ def test_layernorm_matches_oracle(B, in_dt, out_dt, T, cols):
     assert torch.equal(y.cpu(), y2.cpu())          # fixed reduction order
 
 
-def test_sequence_parallel_chain_gpt3_sampled(B):
+def test_sequence_parallel_chain_gpt3_whole(B):
     """Row-layer partials of t = 8 ranks at the GPT-3 shape -> ReduceScatter
     to rank 3's 256 tokens (fp32) -> layer norm -> bf16 -> token AllGather
-    stand-in, against the oracle on sampled rows."""
+    stand-in, against the oracle on every element of the shard."""
     T, h, t, r = 2048, 12288, 8, 3
     _log("case sequence-parallel chain gpt3")
     g = torch.Generator().manual_seed(51)
@@ -1088,9 +1126,9 @@ def test_sequence_parallel_chain_gpt3_sampled(B):
     full = torch.empty(T, h, dtype=torch.bfloat16, device="cuda")
     B.tp_shard_reduce(shards, full, T // t, h, t, B.TP_REDUCE_CONCAT_TOKENS, B.TP_BF16, B.TP_BF16)
     torch.cuda.synchronize()
-    rows = sample_indices(T // t, 5, seed=9)
-    # rank r's sampled rows of the sum: rows r*T/t + rows of every partial
-    ref_rs = oracle.shard_sum(parts_h[:, r * (T // t) + torch.as_tensor(rows), :])
-    ref = oracle.layernorm(ref_rs, gam_h, bet_h, 1e-5)
-    assert_close(y[rows], ref, "bf16", "sp chain rows")
+    ref_rs = oracle.reduce_scatter(parts_h, r)
+    # the fp32 sum: within the summation bound of t - 1 additions
+    bound = (t - 1) * 2.0 ** -24 * oracle.reduce_scatter(parts_h.abs(), r) + 1e-30
+    assert np.all(np.abs(to_np64(rs) - ref_rs) <= bound)
+    _whole(y, oracle.layernorm(ref_rs, gam_h, bet_h, 1e-5), "bf16", "sp chain layer norm")
     assert torch.equal(full[r * (T // t):(r + 1) * (T // t)].cpu(), y.cpu())
