@@ -85,6 +85,8 @@ constexpr int kReadGroups = 3;
 // MFMAs' or the DMA's priority instead measured no gain or slower.
 constexpr int kXcds = 8;
 constexpr int kCUs = 256;
+constexpr int kABytes = kABufs * kBM * 64 * 2;   // A's ring: 96 KiB
+constexpr int kBBytes = kBBufs * kBN * 64 * 2;   // B's ring: 48 KiB
 
 // Raw buffer descriptor (gfx9 family): base, stride 0, byte extent, word 3.
 __device__ __forceinline__ i32x4 make_desc(const void* base, uint32_t bytes)
@@ -296,200 +298,22 @@ __device__ __forceinline__ bf16x8 read_frag_mn(const bf16* buf, int row0, int la
                   half[1][0], half[1][1], half[1][2], half[1][3]};
 }
 
-static_assert(kBM == kGemmRingTileRows, "row blocks of GemmArgs::colsum");
-
-template <int NW, int WM, bool A_KMAJ, bool B_KMAJ, Epi EPI, typename OutT>
-__global__ __launch_bounds__(64 * NW, 1) void gemm_ring_kernel(GemmArgs p, int tiles_m,
-                                                               int tiles_n, int group_m)
+// Writes a finished tile: lane holds row (lane % 16) and columns
+// 4 * (lane / 16) + 0..3 of every 16 x 16 fragment of its wave's block
+// (wave row wm, first rows/columns wrow_a/wrow_b of the tile).  Plain fp32
+// results are staged through the LDS ring, which must no longer be read or
+// written by any wave's loads.
+template <int NW, int WM, Epi EPI, typename OutT>
+__device__ __forceinline__ void store_tile(const GemmArgs& p,
+                                           f32x4 (&acc)[kBM / WM / 16][kBN / (NW / WM) / 16],
+                                           bf16* smem, int64_t m0, int64_t n0, int tm, int wm,
+                                           int wrow_a, int wrow_b, int lane)
 {
     constexpr int BN = kBN;
     constexpr int kWavesM = WM, kWavesN = NW / WM;
-    constexpr int kWaveM = kBM / kWavesM, kWaveN = BN / kWavesN;
-    constexpr int kFragM = kWaveM / 16, kFragN = kWaveN / 16;
-    // A: 64-k units (K-contiguous) or pairs of 32-k slabs (M-contiguous) in
-    // a ring of three, all of one unit or pair at each even step; B likewise
-    // (units for NT, slab pairs for NN and TN) in a ring of two at the odd
-    // steps.  The steps alternate between A's loads and B's.
-    using PlanAU = UnitPlan<NW, kBM, kABufs>;
-    using PlanAP = PairPlan<NW, kBM, kABufs>;
-    using PlanBU = UnitPlan<NW, BN, kBBufs>;
-    using PlanBP = PairPlan<NW, BN, kBBufs>;
-    constexpr int kABytes = kABufs * kBM * 64 * 2;   // 96 KiB
-    constexpr int kBBytes = kBBufs * BN * 64 * 2;    // 48 KiB
-    static_assert(PlanAU::kBufBytes == 2 * PlanAP::kSlabBytes &&
-                      PlanBU::kBufBytes == 2 * PlanBP::kSlabBytes,
-                  "a unit and a slab pair take the same bytes");
-    // DMA instructions per wave at even steps (A) and at odd steps (B).
-    constexpr int kDmaEven = A_KMAJ ? PlanAU::kPerUnit : PlanAP::kPer;
-    constexpr int kDmaOdd = B_KMAJ ? PlanBU::kPerUnit : PlanBP::kPer;
-    __shared__ __attribute__((aligned(1024))) bf16 smem[(kABytes + kBBytes) / 2];
-    bf16* const sa = smem;                  // A ring
-    bf16* const sb = smem + kABytes / 2;    // B ring
+    constexpr int kWaveN = BN / kWavesN;
+    constexpr int kFragM = kBM / kWavesM / 16, kFragN = kWaveN / 16;
 
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int wm = wave / kWavesN, wn = wave % kWavesN;
-
-    // Tiles of all products in one numbering, product-major; an XCD's run of
-    // consecutive tiles then lies in one product (one shard per XCD when
-    // eight shards are batched).
-    const int per_product = tiles_m * tiles_n;
-    const int ntiles = per_product * (int)p.batch;
-    int tile = blockIdx.x;
-    if (ntiles % kXcds == 0) tile = (tile % kXcds) * (ntiles / kXcds) + tile / kXcds;
-    if (p.batch > 1) {
-        const int64_t b = tile / per_product;
-        tile -= (int)b * per_product;
-        p.A = static_cast<const bf16*>(p.A) + b * p.sA;
-        p.B = static_cast<const bf16*>(p.B) + b * p.sB;
-        p.C = static_cast<OutT*>(p.C) + b * p.sC;
-        if (p.bias) p.bias = static_cast<const bf16*>(p.bias) + b * p.sBias;
-        if (p.save) p.save = static_cast<bf16*>(p.save) + b * p.sSave;
-    }
-    int tm = tile % tiles_m, tn = tile / tiles_m;
-    if (group_m > 0 && tiles_m % group_m == 0) {
-        // Tiles in groups of group_m tile rows, column by column inside a
-        // group, so that an XCD's run of tiles covers a group_m-row block.
-        const int per_group = group_m * tiles_n;
-        const int grp = tile / per_group, r = tile % per_group;
-        tm = grp * group_m + r % group_m;
-        tn = r / group_m;
-    }
-    const int64_t m0 = (int64_t)tm * kBM, n0 = (int64_t)tn * BN;
-
-    const int64_t lda = p.lda ? p.lda : (A_KMAJ ? p.K : p.M);
-    const int64_t ldb = p.ldb ? p.ldb : (B_KMAJ ? p.K : p.N);
-    const i32x4 da = make_desc(p.A, (uint32_t)operand_bytes(A_KMAJ, p.M, p.K, lda));
-    const i32x4 db = make_desc(p.B, (uint32_t)operand_bytes(B_KMAJ, p.N, p.K, ldb));
-    PlanAU pau;
-    PlanAP pap;
-    if constexpr (A_KMAJ) pau.init(wave, lane, m0, lda, p.M, p.K);
-    else pap.init(wave, lane, m0, lda, p.M, p.K);
-    PlanBU pbu;
-    PlanBP pbp;
-    if constexpr (B_KMAJ) pbu.init(wave, lane, n0, ldb, p.N, p.K);
-    else pbp.init(wave, lane, n0, ldb, p.N, p.K);
-    const uint32_t a_base = lds_addr(sa), b_base = lds_addr(sb);
-
-    const int wrow_a = wm * kWaveM, wrow_b = wn * kWaveN;
-    f32x4 acc[kFragM][kFragN];
-#pragma unroll
-    for (int a = 0; a < kFragM; ++a)
-#pragma unroll
-        for (int b = 0; b < kFragN; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-    bf16x8 fa[2][kFragM], fb[2][kFragN];
-
-    // DMA instruction d of step vs (negative in the prologue).  Even vs: A's
-    // unit or pair (vs + 4) / 2, into the buffer of (vs - 2) / 2, whose last
-    // slab (vs - 1) was read during step vs - 2.  Odd vs: B's unit or pair
-    // (vs + 3) / 2, into the buffer of (vs - 1) / 2, whose last slab (vs)
-    // was read during step vs - 1.  Each lands two or three slabs before its
-    // first slab is read; B's unit or pair -1, at the first prologue step,
-    // reads nothing and keeps the prologue in the same pattern.
-    auto dma_op = [&](int d, int vs) {
-        if ((vs & 1) == 0) {
-            if constexpr (A_KMAJ) pau.issue_q(d, wave, da, a_base, (vs + 4) >> 1);
-            else pap.issue(d, da, a_base, (vs + 4) >> 1);
-        } else {
-            if constexpr (B_KMAJ) pbu.issue_q(d, wave, db, b_base, (vs + 3) >> 1);
-            else pbp.issue(d, db, b_base, (vs + 3) >> 1);
-        }
-    };
-    // The work of one slab is cut into kGroups groups, each holding (in this
-    // order) the MFMAs of the A fragments a with a % kGroups == g, (for g <
-    // kReadGroups) the fragment reads of the next slab with index %
-    // kReadGroups == g and the DMA instructions d with d % kGroups == g, so
-    // that the waves never stall on a burst of memory instructions while the
-    // matrix pipe idles.
-    static_assert(kFragM % kGroups == 0, "whole A fragments per group");
-    auto read_group = [&](int g, int slab, int buf) {
-#pragma unroll
-        for (int a = g; a < kFragM; a += kReadGroups) {
-            if constexpr (A_KMAJ)
-                fa[buf][a] = read_frag_k8(sa + ((slab >> 1) % kABufs) * (kBM * 64),
-                                          wrow_a + a * 16, slab & 1, lane);
-            else
-                fa[buf][a] = read_frag_mn<kBM>(sa + (slab % (2 * kABufs)) * (kBM * kBK),
-                                               wrow_a + a * 16, lane);
-        }
-#pragma unroll
-        for (int q = g; q < kFragN; q += kReadGroups) {
-            if constexpr (B_KMAJ)
-                fb[buf][q] = read_frag_k8(sb + ((slab >> 1) & (kBBufs - 1)) * (BN * 64),
-                                          wrow_b + q * 16, slab & 1, lane);
-            else
-                fb[buf][q] = read_frag_mn<BN>(sb + (slab % (2 * kBBufs)) * (BN * kBK),
-                                              wrow_b + q * 16, lane);
-        }
-    };
-    auto mfma_group = [&](int g, int buf) {
-#pragma unroll
-        for (int a = g; a < kFragM; a += kGroups)
-#pragma unroll
-            for (int b = 0; b < kFragN; ++b)
-                acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[buf][b], fa[buf][a],
-                                                                    acc[a][b], 0, 0, 0);
-    };
-    // Slab kt: wait for slab kt+1 (own loads, then everybody's via the
-    // barrier, which also retires every wave's reads of slab kt), then refill
-    // while multiplying slab kt (fragments read during the previous slab) and
-    // reading the fragments of slab kt+1.  B's loads for slab kt+1 were
-    // issued at step kt-2 (kt odd) or kt-3 (kt even), A's at step kt-3 (kt
-    // odd) or kt-4 (kt even), so only the loads of step kt-1 (an even step,
-    // kt odd) or of steps kt-2 and kt-1 (one of each, kt even) may stay
-    // outstanding.
-    auto slab_step = [&](auto odd, int kt, int cbuf, int nbuf) {
-        constexpr bool kOdd = decltype(odd)::value;
-        if constexpr (kOdd) wait_vmcnt<kDmaEven>();
-        else wait_vmcnt<kDmaEven + kDmaOdd>();
-        wait_lgkmcnt0();
-        barrier();
-        constexpr int kSteps = kOdd ? kDmaOdd : kDmaEven;
-#pragma unroll
-        for (int g = 0; g < kGroups; ++g) {
-            mfma_group(g, cbuf);
-            if (g < kReadGroups) {
-                __builtin_amdgcn_s_setprio(1);
-                read_group(g, kt + 1, nbuf);
-                __builtin_amdgcn_s_setprio(0);
-            }
-#pragma unroll
-            for (int d = g; d < kSteps; d += kGroups) dma_op(d, kt);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    };
-    using Even = std::integral_constant<bool, false>;
-    using Odd = std::integral_constant<bool, true>;
-
-    const int nk = (int)((p.K + kBK - 1) / kBK);
-    if (nk > 0) {
-        static_assert(kLead == 5, "prologue parity pattern");
-#pragma unroll
-        for (int vs = -kLead; vs < 0; ++vs) {
-            constexpr int kDmaMax = kDmaOdd > kDmaEven ? kDmaOdd : kDmaEven;
-            const int steps = (vs & 1) ? kDmaOdd : kDmaEven;
-#pragma unroll
-            for (int d = 0; d < kDmaMax; ++d)
-                if (d < steps) dma_op(d, vs);
-        }
-        // Slab 0 came with steps -4 (A) and -3 (B): only steps -2 and -1 may
-        // be outstanding.
-        wait_vmcnt<kDmaEven + kDmaOdd>();
-        barrier();
-#pragma unroll
-        for (int g = 0; g < kReadGroups; ++g) read_group(g, 0, 0);
-        int kt = 0;
-        for (; kt + 1 < nk; kt += 2) {
-            slab_step(Even{}, kt, 0, 1);
-            slab_step(Odd{}, kt + 1, 1, 0);
-        }
-        if (kt < nk) slab_step(Even{}, kt, 0, 1);
-    }
-    wait_vmcnt<0>();
-    wait_lgkmcnt0();
-
-    // Epilogue: lane holds row (lane % 16) and columns 4 * (lane / 16) + 0..3
-    // of every 16 x 16 fragment.
     const bf16* bias = static_cast<const bf16*>(p.bias);
     const bf16* aux = static_cast<const bf16*>(p.aux);
     OutT* C = static_cast<OutT*>(p.C);
@@ -674,6 +498,210 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_ring_kernel(GemmArgs p, int t
             }
         }
     }
+}
+
+// The tile (tm, tn) this workgroup computes.  Tiles of all products are in
+// one numbering, product-major; workgroups are remapped so that each XCD
+// (the dispatcher sends workgroup w to XCD w mod 8) owns a contiguous run of
+// tiles, which then lies in one product (one shard per XCD when eight shards
+// are batched).  For a batch, p's operand pointers are moved to the
+// workgroup's product.
+template <typename OutT>
+__device__ __forceinline__ void tile_of_block(GemmArgs& p, int tiles_m, int tiles_n, int group_m,
+                                              int& tm, int& tn)
+{
+    const int per_product = tiles_m * tiles_n;
+    const int ntiles = per_product * (int)p.batch;
+    int tile = blockIdx.x;
+    if (ntiles % kXcds == 0) tile = (tile % kXcds) * (ntiles / kXcds) + tile / kXcds;
+    if (p.batch > 1) {
+        const int64_t b = tile / per_product;
+        tile -= (int)b * per_product;
+        p.A = static_cast<const bf16*>(p.A) + b * p.sA;
+        p.B = static_cast<const bf16*>(p.B) + b * p.sB;
+        p.C = static_cast<OutT*>(p.C) + b * p.sC;
+        if (p.bias) p.bias = static_cast<const bf16*>(p.bias) + b * p.sBias;
+        if (p.save) p.save = static_cast<bf16*>(p.save) + b * p.sSave;
+    }
+    tm = tile % tiles_m;
+    tn = tile / tiles_m;
+    if (group_m > 0 && tiles_m % group_m == 0) {
+        // Tiles in groups of group_m tile rows, column by column inside a
+        // group, so that an XCD's run of tiles covers a group_m-row block.
+        const int per_group = group_m * tiles_n;
+        const int grp = tile / per_group, r = tile % per_group;
+        tm = grp * group_m + r % group_m;
+        tn = r / group_m;
+    }
+}
+
+static_assert(kBM == kGemmRingTileRows, "row blocks of GemmArgs::colsum");
+
+template <int NW, int WM, bool A_KMAJ, bool B_KMAJ, Epi EPI, typename OutT>
+__global__ __launch_bounds__(64 * NW, 1) void gemm_ring_kernel(GemmArgs p, int tiles_m,
+                                                               int tiles_n, int group_m)
+{
+    constexpr int BN = kBN;
+    constexpr int kWavesM = WM, kWavesN = NW / WM;
+    constexpr int kWaveM = kBM / kWavesM, kWaveN = BN / kWavesN;
+    constexpr int kFragM = kWaveM / 16, kFragN = kWaveN / 16;
+    // A: 64-k units (K-contiguous) or pairs of 32-k slabs (M-contiguous) in
+    // a ring of three, all of one unit or pair at each even step; B likewise
+    // (units for NT, slab pairs for NN and TN) in a ring of two at the odd
+    // steps.  The steps alternate between A's loads and B's.
+    using PlanAU = UnitPlan<NW, kBM, kABufs>;
+    using PlanAP = PairPlan<NW, kBM, kABufs>;
+    using PlanBU = UnitPlan<NW, BN, kBBufs>;
+    using PlanBP = PairPlan<NW, BN, kBBufs>;
+    static_assert(PlanAU::kBufBytes == 2 * PlanAP::kSlabBytes &&
+                      PlanBU::kBufBytes == 2 * PlanBP::kSlabBytes,
+                  "a unit and a slab pair take the same bytes");
+    // DMA instructions per wave at even steps (A) and at odd steps (B).
+    constexpr int kDmaEven = A_KMAJ ? PlanAU::kPerUnit : PlanAP::kPer;
+    constexpr int kDmaOdd = B_KMAJ ? PlanBU::kPerUnit : PlanBP::kPer;
+    __shared__ __attribute__((aligned(1024))) bf16 smem[(kABytes + kBBytes) / 2];
+    bf16* const sa = smem;                  // A ring
+    bf16* const sb = smem + kABytes / 2;    // B ring
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave / kWavesN, wn = wave % kWavesN;
+
+    int tm, tn;
+    tile_of_block<OutT>(p, tiles_m, tiles_n, group_m, tm, tn);
+    const int64_t m0 = (int64_t)tm * kBM, n0 = (int64_t)tn * BN;
+
+    const int64_t lda = p.lda ? p.lda : (A_KMAJ ? p.K : p.M);
+    const int64_t ldb = p.ldb ? p.ldb : (B_KMAJ ? p.K : p.N);
+    const i32x4 da = make_desc(p.A, (uint32_t)operand_bytes(A_KMAJ, p.M, p.K, lda));
+    const i32x4 db = make_desc(p.B, (uint32_t)operand_bytes(B_KMAJ, p.N, p.K, ldb));
+    PlanAU pau;
+    PlanAP pap;
+    if constexpr (A_KMAJ) pau.init(wave, lane, m0, lda, p.M, p.K);
+    else pap.init(wave, lane, m0, lda, p.M, p.K);
+    PlanBU pbu;
+    PlanBP pbp;
+    if constexpr (B_KMAJ) pbu.init(wave, lane, n0, ldb, p.N, p.K);
+    else pbp.init(wave, lane, n0, ldb, p.N, p.K);
+    const uint32_t a_base = lds_addr(sa), b_base = lds_addr(sb);
+
+    const int wrow_a = wm * kWaveM, wrow_b = wn * kWaveN;
+    f32x4 acc[kFragM][kFragN];
+#pragma unroll
+    for (int a = 0; a < kFragM; ++a)
+#pragma unroll
+        for (int b = 0; b < kFragN; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    bf16x8 fa[2][kFragM], fb[2][kFragN];
+
+    // DMA instruction d of step vs (negative in the prologue).  Even vs: A's
+    // unit or pair (vs + 4) / 2, into the buffer of (vs - 2) / 2, whose last
+    // slab (vs - 1) was read during step vs - 2.  Odd vs: B's unit or pair
+    // (vs + 3) / 2, into the buffer of (vs - 1) / 2, whose last slab (vs)
+    // was read during step vs - 1.  Each lands two or three slabs before its
+    // first slab is read; B's unit or pair -1, at the first prologue step,
+    // reads nothing and keeps the prologue in the same pattern.
+    auto dma_op = [&](int d, int vs) {
+        if ((vs & 1) == 0) {
+            if constexpr (A_KMAJ) pau.issue_q(d, wave, da, a_base, (vs + 4) >> 1);
+            else pap.issue(d, da, a_base, (vs + 4) >> 1);
+        } else {
+            if constexpr (B_KMAJ) pbu.issue_q(d, wave, db, b_base, (vs + 3) >> 1);
+            else pbp.issue(d, db, b_base, (vs + 3) >> 1);
+        }
+    };
+    // The work of one slab is cut into kGroups groups, each holding (in this
+    // order) the MFMAs of the A fragments a with a % kGroups == g, (for g <
+    // kReadGroups) the fragment reads of the next slab with index %
+    // kReadGroups == g and the DMA instructions d with d % kGroups == g, so
+    // that the waves never stall on a burst of memory instructions while the
+    // matrix pipe idles.
+    static_assert(kFragM % kGroups == 0, "whole A fragments per group");
+    auto read_group = [&](int g, int slab, int buf) {
+#pragma unroll
+        for (int a = g; a < kFragM; a += kReadGroups) {
+            if constexpr (A_KMAJ)
+                fa[buf][a] = read_frag_k8(sa + ((slab >> 1) % kABufs) * (kBM * 64),
+                                          wrow_a + a * 16, slab & 1, lane);
+            else
+                fa[buf][a] = read_frag_mn<kBM>(sa + (slab % (2 * kABufs)) * (kBM * kBK),
+                                               wrow_a + a * 16, lane);
+        }
+#pragma unroll
+        for (int q = g; q < kFragN; q += kReadGroups) {
+            if constexpr (B_KMAJ)
+                fb[buf][q] = read_frag_k8(sb + ((slab >> 1) & (kBBufs - 1)) * (BN * 64),
+                                          wrow_b + q * 16, slab & 1, lane);
+            else
+                fb[buf][q] = read_frag_mn<BN>(sb + (slab % (2 * kBBufs)) * (BN * kBK),
+                                              wrow_b + q * 16, lane);
+        }
+    };
+    auto mfma_group = [&](int g, int buf) {
+#pragma unroll
+        for (int a = g; a < kFragM; a += kGroups)
+#pragma unroll
+            for (int b = 0; b < kFragN; ++b)
+                acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[buf][b], fa[buf][a],
+                                                                    acc[a][b], 0, 0, 0);
+    };
+    // Slab kt: wait for slab kt+1 (own loads, then everybody's via the
+    // barrier, which also retires every wave's reads of slab kt), then refill
+    // while multiplying slab kt (fragments read during the previous slab) and
+    // reading the fragments of slab kt+1.  B's loads for slab kt+1 were
+    // issued at step kt-2 (kt odd) or kt-3 (kt even), A's at step kt-3 (kt
+    // odd) or kt-4 (kt even), so only the loads of step kt-1 (an even step,
+    // kt odd) or of steps kt-2 and kt-1 (one of each, kt even) may stay
+    // outstanding.
+    auto slab_step = [&](auto odd, int kt, int cbuf, int nbuf) {
+        constexpr bool kOdd = decltype(odd)::value;
+        if constexpr (kOdd) wait_vmcnt<kDmaEven>();
+        else wait_vmcnt<kDmaEven + kDmaOdd>();
+        wait_lgkmcnt0();
+        barrier();
+        constexpr int kSteps = kOdd ? kDmaOdd : kDmaEven;
+#pragma unroll
+        for (int g = 0; g < kGroups; ++g) {
+            mfma_group(g, cbuf);
+            if (g < kReadGroups) {
+                __builtin_amdgcn_s_setprio(1);
+                read_group(g, kt + 1, nbuf);
+                __builtin_amdgcn_s_setprio(0);
+            }
+#pragma unroll
+            for (int d = g; d < kSteps; d += kGroups) dma_op(d, kt);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    using Even = std::integral_constant<bool, false>;
+    using Odd = std::integral_constant<bool, true>;
+
+    const int nk = (int)((p.K + kBK - 1) / kBK);
+    if (nk > 0) {
+        static_assert(kLead == 5, "prologue parity pattern");
+#pragma unroll
+        for (int vs = -kLead; vs < 0; ++vs) {
+            constexpr int kDmaMax = kDmaOdd > kDmaEven ? kDmaOdd : kDmaEven;
+            const int steps = (vs & 1) ? kDmaOdd : kDmaEven;
+#pragma unroll
+            for (int d = 0; d < kDmaMax; ++d)
+                if (d < steps) dma_op(d, vs);
+        }
+        // Slab 0 came with steps -4 (A) and -3 (B): only steps -2 and -1 may
+        // be outstanding.
+        wait_vmcnt<kDmaEven + kDmaOdd>();
+        barrier();
+#pragma unroll
+        for (int g = 0; g < kReadGroups; ++g) read_group(g, 0, 0);
+        int kt = 0;
+        for (; kt + 1 < nk; kt += 2) {
+            slab_step(Even{}, kt, 0, 1);
+            slab_step(Odd{}, kt + 1, 1, 0);
+        }
+        if (kt < nk) slab_step(Even{}, kt, 0, 1);
+    }
+    wait_vmcnt<0>();
+    wait_lgkmcnt0();
+    store_tile<NW, WM, EPI, OutT>(p, acc, smem, m0, n0, tm, wm, wrow_a, wrow_b, lane);
 }
 
 // NW waves per workgroup, WM of them along M (and NW / WM along N).  Four
