@@ -717,12 +717,14 @@ hipError_t launch(const GemmArgs& p, hipStream_t stream)
     const int tn = (int)((p.N + kBN - 1) / kBN);
     // Products with several waves of tiles walk an XCD's tiles in 4-row
     // groups: the weight gradients (six waves) about 4% faster, the two-wave
-    // NN row-layer product about 2%.  One-wave products and the two-wave NT
-    // product keep the plain order, which measured as fast or faster for them.
-    // Batched products give each XCD one product's tiles for its 32 CUs, so
-    // they take the 4-row groups as well.
-    const int group_m =
-        tm * tn > 2 * kCUs || (!BK && tm * tn >= 2 * kCUs) || p.batch > 1 ? 4 : 0;
+    // NN row-layer product about 2%.  For the one-wave NN product (the column
+    // layer: 8 x 32 tiles) the groups give each XCD a 4 x 8 block of tiles
+    // instead of 8 x 4, so its L2 fetches half of X and a quarter of W1
+    // (503 MB from HBM in all instead of 553) at the same speed.  NT
+    // products with one or two waves of tiles keep the plain order, which
+    // measured as fast or faster for them.  Batched products give each XCD
+    // one product's tiles for its 32 CUs, so they take the 4-row groups too.
+    const int group_m = tm * tn > 2 * kCUs || !BK || p.batch > 1 ? 4 : 0;
     hipLaunchKernelGGL((gemm_ring_kernel<NW, WM, AK, BK, E, O>),
                        dim3((unsigned)(tm * tn * p.batch)), dim3(64 * NW), 0, stream, p, tm, tn,
                        group_m);

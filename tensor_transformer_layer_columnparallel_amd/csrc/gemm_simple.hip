@@ -214,14 +214,33 @@ __global__ __launch_bounds__(kThreads) void gemm_simple_kernel(GemmArgs p)
     }
 }
 
-template <typename T, bool A_KMAJ, bool B_KMAJ, Epi EPI, typename OutT>
-hipError_t launch(const GemmArgs& p, hipStream_t stream)
+template <typename T, bool A_KMAJ, bool B_KMAJ, Epi EPI, typename OutT, int BM, int BN>
+hipError_t launch_tile(const GemmArgs& p, hipStream_t stream)
 {
-    constexpr int BM = 128, BN = 128;
     dim3 grid((unsigned)((p.N + BN - 1) / BN), (unsigned)((p.M + BM - 1) / BM));
     hipLaunchKernelGGL((gemm_simple_kernel<T, A_KMAJ, B_KMAJ, EPI, OutT, BM, BN>), grid,
                        dim3(kThreads), 0, stream, p);
     return hipGetLastError();
+}
+
+// 128 x 128 tiles, or smaller ones (64 x 64; 32 x 32 for fp32, whose slab
+// of 32 rows fills the 256 threads' loads) when the larger tiles would leave
+// most of the 256 CUs idle: a product of a few rows (the tiny fp32 layer's
+// 32 tokens) otherwise runs its whole K loop on a tile that is mostly
+// padding, on a handful of CUs.  Every output sums k in the same order
+// whatever the tile, so the results are the same bits.
+template <typename T, bool A_KMAJ, bool B_KMAJ, Epi EPI, typename OutT>
+hipError_t launch(const GemmArgs& p, hipStream_t stream)
+{
+    auto tiles = [&](int64_t b) { return ((p.M + b - 1) / b) * ((p.N + b - 1) / b); };
+    constexpr int64_t kFew = 128;   // half the CUs
+    if (tiles(128) >= kFew) return launch_tile<T, A_KMAJ, B_KMAJ, EPI, OutT, 128, 128>(p, stream);
+    if constexpr (sizeof(T) == 2) {
+        return launch_tile<T, A_KMAJ, B_KMAJ, EPI, OutT, 64, 64>(p, stream);
+    } else {
+        if (tiles(64) >= kFew) return launch_tile<T, A_KMAJ, B_KMAJ, EPI, OutT, 64, 64>(p, stream);
+        return launch_tile<T, A_KMAJ, B_KMAJ, EPI, OutT, 32, 32>(p, stream);
+    }
 }
 
 }  // namespace

@@ -10,9 +10,12 @@
 namespace tpmlp {
 namespace {
 
-constexpr int kThreads = 512;
+// 1024 threads (16 waves) per row: more loads issued at once per CU than
+// with 512 (3% faster on a [256, 12288] fp32 shard, where every row is one
+// CU's only work; 256 threads were 29% slower).
+constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
-constexpr int kMaxOcts = 4;   // register-resident row: up to 16384 columns
+constexpr int kMaxOcts = 4;   // register-resident row: up to 32768 columns
 
 struct Oct {
     float v[8];

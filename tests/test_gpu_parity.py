@@ -1080,9 +1080,10 @@ def test_concat_tokens_is_the_stacked_layout_bitexact(B):
 
 @pytest.mark.parametrize("in_dt,out_dt", [("f32", "f32"), ("f32", "bf16"), ("bf16", "bf16"),
                                           ("bf16", "f32")])
-@pytest.mark.parametrize("T,cols", [(77, 520), (9, 6152), (9, 17008)])
+@pytest.mark.parametrize("T,cols", [(77, 520), (9, 12296), (9, 17008), (5, 33008)])
 def test_layernorm_matches_oracle(B, in_dt, out_dt, T, cols):
-    # rows held in registers (520, 6152 columns) and rows read three times (17008)
+    # rows held in registers, one, two and four 8-column octets per thread
+    # of 1024 (520, 12296, 17008 columns), and rows read three times (33008)
     _log(f"case layernorm {in_dt}->{out_dt} {T}x{cols}")
     g = torch.Generator().manual_seed(41)
     idt = torch.float32 if in_dt == "f32" else torch.bfloat16
