@@ -478,8 +478,9 @@ def small_configs(B, stream, reps=50):
     HIP events on the launch stream, both as `reps` eager calls and as the
     same calls captured once in a HIP graph and replayed (the graph removes
     the host's launch gaps, which dominate at these sizes):
-      tiny fp32 MLP, t = 2: both shards' forward (tp_mlp_shard_fwd) and the
-        fp32 shard sum (tp_shard_reduce) of the two partials;
+      tiny fp32 MLP, t = 2: both shards' forward (tp_mlp_shard_fwd per shard,
+        and both at once with tp_mlp_layer_fwd) and the fp32 shard sum
+        (tp_shard_reduce) of the two partials;
       column-parallel linear 768 -> 3072, t = 4, rank 0, bf16: one
         tp_column_linear call, X [4096, 768] x W_0 [768, 768], bf16 output."""
     import torch
@@ -501,6 +502,15 @@ def small_configs(B, stream, reps=50):
         for r in w1.ranks:
             B.tp_mlp_shard_fwd(X, W1[r], b1[r], W2[r], H[r], None, parts[r], w1.T, w1.h, w1.ffn,
                                w1.t, r, f32, stream=st.cuda_stream)
+        B.tp_shard_reduce(parts, Z, w1.T, w1.h, w1.t, B.TP_REDUCE_SUM, f32, f32,
+                          stream=st.cuda_stream)
+
+    W1s, b1s, W2s = torch.stack(W1), torch.stack(b1), torch.stack(W2)
+    Hs = torch.empty(w1.t, w1.T, w1.n, device=dev)
+
+    def c1_batched(st):
+        B.tp_mlp_layer_fwd(X, W1s, b1s, W2s, Hs, None, parts, w1.T, w1.h, w1.ffn, w1.t, f32,
+                           stream=st.cuda_stream)
         B.tp_shard_reduce(parts, Z, w1.T, w1.h, w1.t, B.TP_REDUCE_SUM, f32, f32,
                           stream=st.cuda_stream)
 
@@ -543,6 +553,8 @@ def small_configs(B, stream, reps=50):
             ("tiny_mlp_f32_t2", c1, w1.fwd_flops(),
              f"tiny fp32 MLP, t={w1.t}, both shards: X[{w1.T},{w1.h}], W1_r[{w1.h},{w1.n}], "
              f"W2_r[{w1.n},{w1.h}]; two tp_mlp_shard_fwd + tp_shard_reduce SUM (5 kernels)"),
+            ("tiny_mlp_f32_t2_batched", c1_batched, w1.fwd_flops(),
+             f"the same, both shards in one tp_mlp_layer_fwd + tp_shard_reduce SUM (3 kernels)"),
             ("column_linear_768", c2, w2.fwd_flops(),
              f"column-parallel linear 768->3072, t={w2.t}, rank 0: X[{w2.T},{w2.h}] x "
              f"W_0[{w2.h},{w2.n}], bf16 out, no activation; one tp_column_linear")):

@@ -85,8 +85,28 @@ constexpr int kReadGroups = 3;
 // MFMAs' or the DMA's priority instead measured no gain or slower.
 constexpr int kXcds = 8;
 constexpr int kCUs = 256;
-constexpr int kABytes = kABufs * kBM * 64 * 2;   // A's ring: 96 KiB
-constexpr int kBBytes = kBBufs * kBN * 64 * 2;   // B's ring: 48 KiB
+
+// A tile configuration: BM x BN outputs per workgroup of NW waves, WM of them
+// along M, at most OCC workgroups per CU.  The rings hold kABufs 64-k units
+// of A and kBBufs of B.
+template <int BM_, int BN_, int NW_, int WM_, int OCC_>
+struct TileCfg {
+    static constexpr int BM = BM_, BN = BN_, NW = NW_, WM = WM_, OCC = OCC_;
+    static constexpr int ABytes = kABufs * BM * 64 * 2;
+    static constexpr int BBytes = kBBufs * BN * 64 * 2;
+};
+// 256 x 192: every product of the GPT-3 shard splits into whole waves of 256
+// CUs (256, 512 or 1536 tiles); 8 waves, 2 x 4 (NN, NT) or 4 x 2 (TN); rings
+// of 96 + 48 KiB, one workgroup per CU.
+using TileNN = TileCfg<256, 192, 8, 2, 1>;
+using TileTN = TileCfg<256, 192, 8, 4, 1>;
+// 128 x 96 for products with fewer 256 x 192 tiles than half the CUs (the
+// 768 -> 3072 column layer: 64 tiles become 256, 20.6 -> 11.4 us): 4 waves of
+// 64 x 48, rings of 48 + 24 KiB, up to two workgroups per CU (padding the
+// LDS to one per CU measured 13% slower).  Each wave issues the same number
+// of DMA instructions per step as in the large tile (4 for A's unit, 3 for
+// B's), so the schedule and its waits are the same.
+using TileSmall = TileCfg<128, 96, 4, 2, 2>;
 
 // Raw buffer descriptor (gfx9 family): base, stride 0, byte extent, word 3.
 __device__ __forceinline__ i32x4 make_desc(const void* base, uint32_t bytes)
@@ -146,15 +166,21 @@ __device__ __forceinline__ int xor_mn(int krow)
 {
     return ((krow >> 1) & 1) + 2 * ((krow & 1) ^ ((krow >> 3) & 1));
 }
+// R = 96 (the small tile's B): the 6 pairs rotated by one for k-rows with
+// bit 3 set, conflict-free for the transposing reads in the same bank model.
 template <int R>
 __device__ __forceinline__ int mn_phys(int krow, int chunk)
 {
+    static_assert(R == 256 || R == 192 || R == 96, "slab widths with a chunk permutation");
     int pair = chunk >> 1;
     if constexpr (R == 256) {
         pair += rot_mn(krow);
         if (pair >= 16) pair -= 16;
-    } else {
+    } else if constexpr (R == 192) {
         pair ^= xor_mn(krow);
+    } else {
+        pair += (krow >> 3) & 1;
+        if (pair >= 6) pair -= 6;
     }
     return 2 * pair + (chunk & 1);
 }
@@ -165,8 +191,11 @@ __device__ __forceinline__ int mn_logical(int krow, int phys)
     if constexpr (R == 256) {
         pair -= rot_mn(krow);
         if (pair < 0) pair += 16;
-    } else {
+    } else if constexpr (R == 192) {
         pair ^= xor_mn(krow);
+    } else {
+        pair -= (krow >> 3) & 1;
+        if (pair < 0) pair += 6;
     }
     return 2 * pair + (phys & 1);
 }
@@ -303,13 +332,14 @@ __device__ __forceinline__ bf16x8 read_frag_mn(const bf16* buf, int row0, int la
 // (wave row wm, first rows/columns wrow_a/wrow_b of the tile).  Plain fp32
 // results are staged through the LDS ring, which must no longer be read or
 // written by any wave's loads.
-template <int NW, int WM, Epi EPI, typename OutT>
-__device__ __forceinline__ void store_tile(const GemmArgs& p,
-                                           f32x4 (&acc)[kBM / WM / 16][kBN / (NW / WM) / 16],
-                                           bf16* smem, int64_t m0, int64_t n0, int tm, int wm,
-                                           int wrow_a, int wrow_b, int lane)
+template <class Cfg, Epi EPI, typename OutT>
+__device__ __forceinline__ void store_tile(
+    const GemmArgs& p, f32x4 (&acc)[Cfg::BM / Cfg::WM / 16][Cfg::BN / (Cfg::NW / Cfg::WM) / 16],
+    bf16* smem, int64_t m0, int64_t n0, int tm, int wm, int wrow_a, int wrow_b, int lane)
 {
-    constexpr int BN = kBN;
+    constexpr int NW = Cfg::NW, WM = Cfg::WM, BN = Cfg::BN, kBM = Cfg::BM;
+    constexpr int kABytes = Cfg::ABytes, kBBytes = Cfg::BBytes;
+    static_assert(EPI != Epi::DGelu || kBM == kGemmRingTileRows, "row blocks of GemmArgs::colsum");
     constexpr int kWavesM = WM, kWavesN = NW / WM;
     constexpr int kWaveN = BN / kWavesN;
     constexpr int kFragM = kBM / kWavesM / 16, kFragN = kWaveN / 16;
@@ -535,13 +565,14 @@ __device__ __forceinline__ void tile_of_block(GemmArgs& p, int tiles_m, int tile
     }
 }
 
-static_assert(kBM == kGemmRingTileRows, "row blocks of GemmArgs::colsum");
-
-template <int NW, int WM, bool A_KMAJ, bool B_KMAJ, Epi EPI, typename OutT>
-__global__ __launch_bounds__(64 * NW, 1) void gemm_ring_kernel(GemmArgs p, int tiles_m,
-                                                               int tiles_n, int group_m)
+template <class Cfg, bool A_KMAJ, bool B_KMAJ, Epi EPI, typename OutT>
+__global__ __launch_bounds__(64 * Cfg::NW, Cfg::OCC) void gemm_ring_kernel(GemmArgs p,
+                                                                           int tiles_m,
+                                                                           int tiles_n,
+                                                                           int group_m)
 {
-    constexpr int BN = kBN;
+    constexpr int NW = Cfg::NW, WM = Cfg::WM, BN = Cfg::BN, kBM = Cfg::BM;
+    constexpr int kABytes = Cfg::ABytes, kBBytes = Cfg::BBytes;
     constexpr int kWavesM = WM, kWavesN = NW / WM;
     constexpr int kWaveM = kBM / kWavesM, kWaveN = BN / kWavesN;
     constexpr int kFragM = kWaveM / 16, kFragN = kWaveN / 16;
@@ -701,20 +732,14 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_ring_kernel(GemmArgs p, int t
     }
     wait_vmcnt<0>();
     wait_lgkmcnt0();
-    store_tile<NW, WM, EPI, OutT>(p, acc, smem, m0, n0, tm, wm, wrow_a, wrow_b, lane);
+    store_tile<Cfg, EPI, OutT>(p, acc, smem, m0, n0, tm, wm, wrow_a, wrow_b, lane);
 }
 
-// NW waves per workgroup, WM of them along M (and NW / WM along N).  Four
-// waves (one per SIMD, 256 x 48 or 128 x 96 outputs each) read less LDS per
-// flop but measured about 35% slower than eight: with one wave per SIMD
-// nothing covers a wave's own waits.
-template <bool AK, bool BK, Epi E, typename O>
-hipError_t launch(const GemmArgs& p, hipStream_t stream)
+template <class Cfg, bool AK, bool BK, Epi E, typename O>
+hipError_t launch_cfg(const GemmArgs& p, hipStream_t stream)
 {
-    constexpr int NW = 8;
-    constexpr int WM = AK ? 2 : 4;   // TN: 4 x 2 waves (its A fragments in four groups)
-    const int tm = (int)((p.M + kBM - 1) / kBM);
-    const int tn = (int)((p.N + kBN - 1) / kBN);
+    const int tm = (int)((p.M + Cfg::BM - 1) / Cfg::BM);
+    const int tn = (int)((p.N + Cfg::BN - 1) / Cfg::BN);
     // Products with several waves of tiles walk an XCD's tiles in 4-row
     // groups: the weight gradients (six waves) about 4% faster, the two-wave
     // NN row-layer product about 2%.  For the one-wave NN product (the column
@@ -725,10 +750,26 @@ hipError_t launch(const GemmArgs& p, hipStream_t stream)
     // measured as fast or faster for them.  Batched products give each XCD
     // one product's tiles for its 32 CUs, so they take the 4-row groups too.
     const int group_m = tm * tn > 2 * kCUs || !BK || p.batch > 1 ? 4 : 0;
-    hipLaunchKernelGGL((gemm_ring_kernel<NW, WM, AK, BK, E, O>),
-                       dim3((unsigned)(tm * tn * p.batch)), dim3(64 * NW), 0, stream, p, tm, tn,
-                       group_m);
+    hipLaunchKernelGGL((gemm_ring_kernel<Cfg, AK, BK, E, O>),
+                       dim3((unsigned)(tm * tn * p.batch)), dim3(64 * Cfg::NW), 0, stream, p, tm,
+                       tn, group_m);
     return hipGetLastError();
+}
+
+// Eight waves per workgroup on 256 x 192 tiles.  Four waves on the same tile
+// (one per SIMD, 256 x 48 or 128 x 96 outputs each) read less LDS per flop
+// but measured about 35% slower: with one wave per SIMD nothing covers a
+// wave's own waits.  Products with a K-contiguous A and a forward epilogue
+// that would have fewer 256 x 192 tiles than half the CUs run on 128 x 96
+// tiles instead (two workgroups of four waves per CU).
+template <bool AK, bool BK, Epi E, typename O>
+hipError_t launch(const GemmArgs& p, hipStream_t stream)
+{
+    if constexpr (AK && (E == Epi::Store || E == Epi::Bias || E == Epi::BiasGelu)) {
+        const int64_t tiles = ((p.M + kBM - 1) / kBM) * ((p.N + kBN - 1) / kBN) * p.batch;
+        if (tiles < kCUs / 2) return launch_cfg<TileSmall, AK, BK, E, O>(p, stream);
+    }
+    return launch_cfg<std::conditional_t<AK, TileNN, TileTN>, AK, BK, E, O>(p, stream);
 }
 
 }  // namespace

@@ -111,6 +111,15 @@ __global__ __launch_bounds__(kThreads) void gemm_simple_kernel(GemmArgs p)
     const int wm = wave >> 1, wn = wave & 1;
     const int64_t m0 = (int64_t)blockIdx.y * BM;
     const int64_t n0 = (int64_t)blockIdx.x * BN;
+    if (p.batch > 1) {
+        // product blockIdx.z of a batch: its operands at the batch strides
+        const int64_t b = blockIdx.z;
+        p.A = static_cast<const T*>(p.A) + b * p.sA;
+        p.B = static_cast<const T*>(p.B) + b * p.sB;
+        p.C = static_cast<OutT*>(p.C) + b * p.sC;
+        if (p.bias) p.bias = static_cast<const T*>(p.bias) + b * p.sBias;
+        if (p.save) p.save = static_cast<T*>(p.save) + b * p.sSave;
+    }
     const T* __restrict__ A = static_cast<const T*>(p.A);
     const T* __restrict__ B = static_cast<const T*>(p.B);
 
@@ -217,7 +226,9 @@ __global__ __launch_bounds__(kThreads) void gemm_simple_kernel(GemmArgs p)
 template <typename T, bool A_KMAJ, bool B_KMAJ, Epi EPI, typename OutT, int BM, int BN>
 hipError_t launch_tile(const GemmArgs& p, hipStream_t stream)
 {
-    dim3 grid((unsigned)((p.N + BN - 1) / BN), (unsigned)((p.M + BM - 1) / BM));
+    if ((p.M + BM - 1) / BM > 65535) return hipErrorInvalidValue;   // grid y
+    dim3 grid((unsigned)((p.N + BN - 1) / BN), (unsigned)((p.M + BM - 1) / BM),
+              (unsigned)p.batch);
     hipLaunchKernelGGL((gemm_simple_kernel<T, A_KMAJ, B_KMAJ, EPI, OutT, BM, BN>), grid,
                        dim3(kThreads), 0, stream, p);
     return hipGetLastError();
@@ -232,7 +243,7 @@ hipError_t launch_tile(const GemmArgs& p, hipStream_t stream)
 template <typename T, bool A_KMAJ, bool B_KMAJ, Epi EPI, typename OutT>
 hipError_t launch(const GemmArgs& p, hipStream_t stream)
 {
-    auto tiles = [&](int64_t b) { return ((p.M + b - 1) / b) * ((p.N + b - 1) / b); };
+    auto tiles = [&](int64_t b) { return ((p.M + b - 1) / b) * ((p.N + b - 1) / b) * p.batch; };
     constexpr int64_t kFew = 128;   // half the CUs
     if (tiles(128) >= kFew) return launch_tile<T, A_KMAJ, B_KMAJ, EPI, OutT, 128, 128>(p, stream);
     if constexpr (sizeof(T) == 2) {
@@ -249,24 +260,10 @@ hipError_t gemm_simple(const GemmArgs& p, Elt elt, Layout layout, Epi epi, Elt o
                        hipStream_t stream)
 {
     if (p.lda || p.ldb) return hipErrorInvalidValue;   // packed operands only
-    if (p.batch > 1) {
-        // Batched products: one launch per product.
-        if (epi != Epi::Store && epi != Epi::Bias && epi != Epi::BiasGelu)
-            return hipErrorInvalidValue;
-        const int64_t es = elt == Elt::F32 ? 4 : 2, os = out == Elt::F32 ? 4 : 2;
-        for (int64_t b = 0; b < p.batch; ++b) {
-            GemmArgs q = p;
-            q.batch = 1;
-            q.A = static_cast<const char*>(p.A) + b * p.sA * es;
-            q.B = static_cast<const char*>(p.B) + b * p.sB * es;
-            q.C = static_cast<char*>(p.C) + b * p.sC * os;
-            if (p.bias) q.bias = static_cast<const char*>(p.bias) + b * p.sBias * es;
-            if (p.save) q.save = static_cast<char*>(p.save) + b * p.sSave * es;
-            const hipError_t e = gemm_simple(q, elt, layout, epi, out, stream);
-            if (e != hipSuccess) return e;
-        }
-        return hipSuccess;
-    }
+    // A batch of products runs as one launch, grid z = product.
+    if (p.batch < 1 || p.batch > 65535) return hipErrorInvalidValue;
+    if (p.batch > 1 && epi != Epi::Store && epi != Epi::Bias && epi != Epi::BiasGelu)
+        return hipErrorInvalidValue;
 #define TP_CASE(T, AK, BK_, E, O)                                                    \
     return launch<T, AK, BK_, E, O>(p, stream)
     if (elt == Elt::F32) {

@@ -135,10 +135,14 @@ def test_replay_constants_match_the_kernel_source():
         return int(m.group(1))
 
     a_bufs, b_bufs, lead = const("kABufs"), const("kBBufs"), const("kLead")
-    bm, bn, bk, nw = const("kBM"), const("kBN"), const("kBK"), const("NW")
+    bk = const("kBK")
     assert (a_bufs, 2 * a_bufs, 2 * b_bufs, lead) == (A_UNITS, A_SLABS, B_SLABS, LEAD)
-    # loads per wave: a 64-deep unit of R rows is R / 8 loads of 8 rows, a
-    # slab pair 2 R / 16 loads of 64 16-byte chunks; both R * 64 * 2 bytes
     assert bk == 32
-    assert bm // 8 // nw == 2 * bm // 16 // nw == 4     # even steps (A)
-    assert bn // 8 // nw == 2 * bn // 16 // nw == 3     # odd steps (B)
+    # every tile configuration: loads per wave of a 64-deep unit of R rows
+    # (R / 8 loads of 8 rows) or of a slab pair (2 R / 16 loads of 64 16-byte
+    # chunks), both R * 64 * 2 bytes, must be the counts the waits assume
+    cfgs = re.findall(r"using Tile\w+ = TileCfg<(\d+), (\d+), (\d+), (\d+), (\w+)>;", src)
+    assert len(cfgs) >= 3, cfgs
+    for bm, bn, nw in (tuple(map(int, c[:3])) for c in cfgs):
+        assert bm // 8 // nw == 2 * bm // 16 // nw == 4, (bm, nw)   # even steps (A)
+        assert bn // 8 // nw == 2 * bn // 16 // nw == 3, (bn, nw)   # odd steps (B)
