@@ -407,11 +407,17 @@ def sequence_parallel(B, stream, sptr, reps=10):
                                                                B.TP_REDUCE_CONCAT_TOKENS, bf,
                                                                bf, stream=sptr))(nxt(n_cat)),
                           2 * T * h * 2),
+        # the first two in one pass: the rank's rows summed as they are loaded
+        # and normalised without writing the fp32 sum
+        "reduce_scatter_layernorm": (lambda: B.tp_shard_reduce_scatter_layernorm(
+            parts, gam, bet, ln_out[nxt(n_ln)], T, h, t, nxt(t), 1e-5, f32, bf, stream=sptr),
+            (t * Tr * h) * 4 + Tr * h * 2 + 2 * h * 2),
     }
     out = {"workload": f"t={t}, {T} tokens, h={h}: ReduceScatter of {t} fp32 partials to "
                        f"{Tr} tokens; layer norm of the shard (fp32 -> bf16); token "
-                       f"AllGather of {t} bf16 shards; every repetition on data not in the "
-                       f"last-level cache", "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+                       f"AllGather of {t} bf16 shards; ReduceScatter and layer norm fused "
+                       f"(bf16 out); every repetition on data not in the last-level cache",
+           "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     for name, (f, nbytes) in ops.items():
         warm(f)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -783,7 +789,8 @@ def main():
         sp = out["sequence_parallel"]
         log("sequence parallel: " + ", ".join(f"{k} {sp[k]['ms']:.4f} ms {sp[k]['achieved']:.0f} GB/s"
                                               for k in ("reduce_scatter", "layernorm",
-                                                        "concat_tokens")))
+                                                        "concat_tokens",
+                                                        "reduce_scatter_layernorm")))
 
     if not args.no_full_layer:
         out["full_layer"] = full_layer(B, stream, sptr)

@@ -261,6 +261,29 @@ TP_API int tp_layernorm(const void* x, const void* gamma, const void* beta, void
                         int64_t tokens, int64_t cols, float eps, int in_dtype, int out_dtype,
                         void* stream);
 
+/*
+ * ReduceScatter over tokens and the layer normalisation of the rank's rows,
+ * in one pass: the sequence-parallel rank's path from the row-parallel
+ * partials to its normalised token shard (ReduceScatter in place of the
+ * AllReduce [P1 introduction; P2 "延伸阅读"], then the normalisation of whole
+ * token rows, which needs no exchange of statistics [P1 introduction; P4
+ * §4.2]):
+ *   s[m][c] = parts[0][rank*tokens/t + m][c] + ... + parts[t-1][...][c]
+ *             (fp32, rank order 0..t-1)
+ *   y[m][c] = (s[m][c] - mu_m) / sqrt(var_m + eps) * gamma[c] + beta[c]
+ * The result is bit for bit that of tp_shard_reduce_scatter with an fp32
+ * output followed by tp_layernorm of that output, without writing or
+ * re-reading s.  parts [t][tokens][cols] (in_dtype); y [tokens/t][cols] and
+ * gamma, beta [cols] (out_dtype; gamma NULL means 1, beta NULL means 0).
+ * Errors as for those two calls: tokens % t != 0 -> TP_ERR_INDIVISIBLE, rank
+ * outside [0, t) -> TP_ERR_RANK, cols a positive multiple of 8, eps finite
+ * and >= 0 (TP_ERR_ARG otherwise); y must not overlap parts, gamma or beta.
+ */
+TP_API int tp_shard_reduce_scatter_layernorm(const void* parts, const void* gamma,
+                                             const void* beta, void* y, int64_t tokens,
+                                             int64_t cols, int t, int rank, float eps,
+                                             int in_dtype, int out_dtype, void* stream);
+
 /* Static description of a status code (never NULL). */
 TP_API const char* tp_status_string(int status);
 

@@ -34,7 +34,8 @@ TP_REDUCE_SUM, TP_REDUCE_CONCAT, TP_REDUCE_CONCAT_TOKENS = 0, 1, 2
 
 ABI_FUNCTIONS = ("tp_column_linear", "tp_row_linear", "tp_mlp_shard_fwd",
                  "tp_mlp_layer_fwd", "tp_mlp_shard_bwd", "tp_linear_bwd", "tp_shard_reduce",
-                 "tp_shard_reduce_scatter", "tp_layernorm", "tp_status_string")
+                 "tp_shard_reduce_scatter", "tp_layernorm", "tp_shard_reduce_scatter_layernorm",
+                 "tp_status_string")
 
 
 class TPError(RuntimeError):
@@ -57,6 +58,8 @@ def load_library() -> ctypes.CDLL:
     lib.tp_shard_reduce.argtypes = [vp, vp, i64, i64, ci, ci, ci, ci, vp]
     lib.tp_shard_reduce_scatter.argtypes = [vp, vp, i64, i64, ci, ci, ci, ci, vp]
     lib.tp_layernorm.argtypes = [vp, vp, vp, vp, i64, i64, ctypes.c_float, ci, ci, vp]
+    lib.tp_shard_reduce_scatter_layernorm.argtypes = [vp, vp, vp, vp, i64, i64, ci, ci,
+                                                      ctypes.c_float, ci, ci, vp]
     for name in ABI_FUNCTIONS[:-1]:
         getattr(lib, name).restype = ci
     lib.tp_status_string.argtypes = [ci]
@@ -233,6 +236,16 @@ def tp_layernorm(x, gamma, beta, y, tokens, cols, eps, in_dtype, out_dtype, stre
                            _ptr(y, "y", odt, _prod(tokens, cols)), tokens, cols, float(eps),
                            idt, odt, _stream(stream))
     return _ret("tp_layernorm", st, check)
+
+
+def tp_shard_reduce_scatter_layernorm(parts, gamma, beta, y, tokens, cols, t, rank, eps,
+                                      in_dtype, out_dtype, stream=None, check=True) -> int:
+    idt, odt = _dt(in_dtype), _dt(out_dtype)
+    st = _lib.tp_shard_reduce_scatter_layernorm(
+        _ptr(parts, "parts", idt, _prod(t, tokens, cols)), _ptr(gamma, "gamma", odt, cols),
+        _ptr(beta, "beta", odt, cols), _ptr(y, "y", odt, _prod(_split(tokens, t), cols)), tokens,
+        cols, t, rank, float(eps), idt, odt, _stream(stream))
+    return _ret("tp_shard_reduce_scatter_layernorm", st, check)
 
 
 def tp_status_string(status: int) -> str:

@@ -38,6 +38,14 @@ hipError_t shard_sum(const void* parts, void* out, int64_t count, int64_t stride
 hipError_t layernorm(const void* x, const void* gamma, const void* beta, void* y, int64_t rows,
                      int64_t cols, float eps, Elt in, Elt out, hipStream_t stream);
 
+// The layer norm above of rows that are sums of t partials: row m is
+// sum_{r=0}^{t-1} parts[r * stride + m * cols + c] (fp32, rank order), the
+// values shard_sum writes with an fp32 output, normalised without being
+// stored.  rows = the rank's token rows; parts points at its first row.
+hipError_t sum_layernorm(const void* parts, int64_t stride, int t, const void* gamma,
+                         const void* beta, void* y, int64_t rows, int64_t cols, float eps, Elt in,
+                         Elt out, hipStream_t stream);
+
 // out[m][r*cols + c] = parts[r][m][c]; cols % 8 == 0.
 hipError_t shard_concat(const void* parts, void* out, int64_t rows, int64_t cols, int t,
                         Elt elt, hipStream_t stream);

@@ -505,6 +505,29 @@ int tp_shard_reduce_scatter(const void* parts, void* out, int64_t tokens, int64_
                                to_elt(out_dtype), static_cast<hipStream_t>(stream)));
 }
 
+int tp_shard_reduce_scatter_layernorm(const void* parts, const void* gamma, const void* beta,
+                                      void* y, int64_t tokens, int64_t cols, int t, int rank,
+                                      float eps, int in_dtype, int out_dtype, void* stream)
+{
+    if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return TP_ERR_DTYPE;
+    int st = check_ptrs({parts, y}, {gamma, beta});
+    if (st) return st;
+    if (t < 1 || rank < 0 || rank >= t) return TP_ERR_RANK;
+    if (tokens < 0 || !feature_dim_ok(cols)) return TP_ERR_SHAPE;
+    if (tokens % t != 0) return TP_ERR_INDIVISIBLE;
+    if (!(eps >= 0.0f) || eps == INFINITY) return TP_ERR_ARG;
+    const int64_t rows = tokens / t;
+    if ((st = check_overlap({{y, nbytes(rows, cols, 1, elt_size(out_dtype))}},
+                            {{parts, nbytes(t, tokens, cols, elt_size(in_dtype))},
+                             {gamma, nbytes(cols, 1, 1, elt_size(out_dtype))},
+                             {beta, nbytes(cols, 1, 1, elt_size(out_dtype))}})))
+        return st;
+    const char* base = static_cast<const char*>(parts) + rank * rows * cols * elt_size(in_dtype);
+    return status_of(sum_layernorm(base, tokens * cols, t, gamma, beta, y, rows, cols, eps,
+                                   to_elt(in_dtype), to_elt(out_dtype),
+                                   static_cast<hipStream_t>(stream)));
+}
+
 int tp_layernorm(const void* x, const void* gamma, const void* beta, void* y, int64_t tokens,
                  int64_t cols, float eps, int in_dtype, int out_dtype, void* stream)
 {

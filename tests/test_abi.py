@@ -38,7 +38,7 @@ def test_header_declares_the_entry_points_and_status_string():
         "tp_column_linear", "tp_row_linear", "tp_mlp_shard_fwd", "tp_mlp_layer_fwd",
         "tp_mlp_shard_bwd",
         "tp_linear_bwd", "tp_shard_reduce", "tp_shard_reduce_scatter", "tp_layernorm",
-        "tp_status_string"}
+        "tp_shard_reduce_scatter_layernorm", "tp_status_string"}
 
 
 def test_library_exports_every_declared_symbol(B):
@@ -214,6 +214,24 @@ def test_layernorm_rejects(Bfake):
     assert f(out_dtype=5) == B.TP_ERR_DTYPE
 
 
+def test_reduce_scatter_layernorm_rejects(Bfake):
+    B = Bfake
+    f = lambda **kw: B.tp_shard_reduce_scatter_layernorm(**{**dict(
+        parts=P, gamma=None, beta=None, y=P2, tokens=16, cols=16, t=8, rank=3, eps=1e-5,
+        in_dtype=B.TP_F32, out_dtype=B.TP_BF16, stream=0, check=False), **kw})
+    assert f(parts=None) == B.TP_ERR_NULL
+    assert f(y=None) == B.TP_ERR_NULL
+    assert f(beta=MIS) == B.TP_ERR_ALIGN
+    assert f(rank=8) == B.TP_ERR_RANK
+    assert f(t=0) == B.TP_ERR_RANK
+    assert f(tokens=12) == B.TP_ERR_INDIVISIBLE
+    assert f(cols=12) == B.TP_ERR_SHAPE
+    assert f(tokens=-8) == B.TP_ERR_SHAPE
+    assert f(eps=float("nan")) == B.TP_ERR_ARG
+    assert f(eps=-1.0) == B.TP_ERR_ARG
+    assert f(out_dtype=5) == B.TP_ERR_DTYPE
+
+
 def test_binding_checks_tensor_arguments(Bfake):
     B = Bfake
     # The binding refuses tensors the library would misread, before the call:
@@ -319,3 +337,9 @@ def test_outputs_may_not_overlap_inputs_or_each_other(Bfake):
         out_dtype=B.TP_F32, stream=0, check=False), **kw})
     assert ln(y=r[0] + 16) == OV
     assert ln(y=r[1]) == OV
+    # fused reduce-scatter + layer norm: the output over the partials or gamma
+    rl = lambda **kw: B.tp_shard_reduce_scatter_layernorm(**{**dict(
+        parts=r[0], gamma=r[1], beta=r[2], y=r[3], tokens=T, cols=h, t=t, rank=1, eps=1e-5,
+        in_dtype=B.TP_F32, out_dtype=B.TP_F32, stream=0, check=False), **kw})
+    assert rl(y=r[0] + t * T * h * 4 - 16) == OV
+    assert rl(y=r[1]) == OV

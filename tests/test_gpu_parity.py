@@ -1107,6 +1107,43 @@ def test_layernorm_matches_oracle(B, in_dt, out_dt, T, cols):
     assert torch.equal(y.cpu(), y2.cpu())          # fixed reduction order
 
 
+@pytest.mark.parametrize("in_dt,out_dt", [("f32", "bf16"), ("f32", "f32"), ("bf16", "bf16")])
+@pytest.mark.parametrize("T,cols,t", [(24, 136, 8), (18, 12296, 3), (4, 33008, 2), (64, 520, 1)])
+def test_reduce_scatter_layernorm_fused(B, in_dt, out_dt, T, cols, t):
+    # The fused call gives the bits of the two calls it replaces (the
+    # ReduceScatter with an fp32 output, then the layer norm of that output)
+    # for every rank, and matches the oracle's sum-then-normalise.  Widths
+    # cover one, two and four octets per thread of the register-resident
+    # rows and the three-pass rows; t = 3 takes the kernel's runtime rank loop.
+    _log(f"case reduce-scatter + layer norm {in_dt}->{out_dt} T={T} cols={cols} t={t}")
+    g = torch.Generator().manual_seed(61)
+    idt = torch.float32 if in_dt == "f32" else torch.bfloat16
+    odt = torch.float32 if out_dt == "f32" else torch.bfloat16
+    parts_h = (2.0 * torch.randn(t, T, cols, generator=g) + 0.5).to(idt)
+    gam_h = (1.0 + 0.1 * torch.randn(cols, generator=g)).to(odt)
+    bet_h = (0.1 * torch.randn(cols, generator=g)).to(odt)
+    parts, gam, bet = dev(parts_h), dev(gam_h), dev(bet_h)
+    for r in range(t):
+        y = torch.empty(T // t, cols, dtype=odt, device="cuda")
+        B.tp_shard_reduce_scatter_layernorm(parts, gam, bet, y, T, cols, t, r, 1e-5, idt, odt)
+        s32 = torch.empty(T // t, cols, dtype=torch.float32, device="cuda")
+        B.tp_shard_reduce_scatter(parts, s32, T, cols, t, r, idt, torch.float32)
+        y2 = torch.empty_like(y)
+        B.tp_layernorm(s32, gam, bet, y2, T // t, cols, 1e-5, torch.float32, odt)
+        torch.cuda.synchronize()
+        assert torch.equal(y, y2), f"rank {r}: fused result differs from the two calls"
+        ref = oracle.layernorm(oracle.reduce_scatter(parts_h, r), gam_h, bet_h, 1e-5)
+        if out_dt == "f32":
+            assert rel_fro_ok(y, ref)
+        else:
+            assert_close(y, ref, "bf16", f"rs+ln rank {r}")
+
+
+def rel_fro_ok(got, ref):
+    rf = np.linalg.norm(to_np64(got) - ref) / np.linalg.norm(ref)
+    return rf <= 1e-5
+
+
 def test_sequence_parallel_chain_gpt3_whole(B):
     """Row-layer partials of t = 8 ranks at the GPT-3 shape -> ReduceScatter
     to rank 3's 256 tokens (fp32) -> layer norm -> bf16 -> token AllGather
@@ -1133,3 +1170,9 @@ def test_sequence_parallel_chain_gpt3_whole(B):
     assert np.all(np.abs(to_np64(rs) - ref_rs) <= bound)
     _whole(y, oracle.layernorm(ref_rs, gam_h, bet_h, 1e-5), "bf16", "sp chain layer norm")
     assert torch.equal(full[r * (T // t):(r + 1) * (T // t)].cpu(), y.cpu())
+    # the same shard from the fused reduce-scatter + layer norm, bit for bit
+    yf = torch.empty_like(y)
+    B.tp_shard_reduce_scatter_layernorm(parts, dev(gam_h), dev(bet_h), yf, T, h, t, r, 1e-5,
+                                        B.TP_F32, B.TP_BF16)
+    torch.cuda.synchronize()
+    assert torch.equal(yf, y)
