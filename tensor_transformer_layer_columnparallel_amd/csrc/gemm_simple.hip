@@ -260,10 +260,27 @@ hipError_t gemm_simple(const GemmArgs& p, Elt elt, Layout layout, Epi epi, Elt o
                        hipStream_t stream)
 {
     if (p.lda || p.ldb) return hipErrorInvalidValue;   // packed operands only
-    // A batch of products runs as one launch, grid z = product.
-    if (p.batch < 1 || p.batch > 65535) return hipErrorInvalidValue;
+    // A batch of products runs as one launch, grid z = product (in launches of
+    // at most 65535 products, the grid's z limit).
+    if (p.batch < 1) return hipErrorInvalidValue;
     if (p.batch > 1 && epi != Epi::Store && epi != Epi::Bias && epi != Epi::BiasGelu)
         return hipErrorInvalidValue;
+    constexpr int64_t kMaxZ = 65535;
+    if (p.batch > kMaxZ) {
+        const int64_t es = elt == Elt::F32 ? 4 : 2, os = out == Elt::F32 ? 4 : 2;
+        for (int64_t b0 = 0; b0 < p.batch; b0 += kMaxZ) {
+            GemmArgs q = p;
+            q.batch = p.batch - b0 < kMaxZ ? p.batch - b0 : kMaxZ;
+            q.A = static_cast<const char*>(p.A) + b0 * p.sA * es;
+            q.B = static_cast<const char*>(p.B) + b0 * p.sB * es;
+            q.C = static_cast<char*>(p.C) + b0 * p.sC * os;
+            if (p.bias) q.bias = static_cast<const char*>(p.bias) + b0 * p.sBias * es;
+            if (p.save) q.save = static_cast<char*>(p.save) + b0 * p.sSave * es;
+            const hipError_t e = gemm_simple(q, elt, layout, epi, out, stream);
+            if (e != hipSuccess) return e;
+        }
+        return hipSuccess;
+    }
 #define TP_CASE(T, AK, BK_, E, O)                                                    \
     return launch<T, AK, BK_, E, O>(p, stream)
     if (elt == Elt::F32) {

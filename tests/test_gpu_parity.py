@@ -142,6 +142,49 @@ def test_column_linear_tile_kernel_epilogues(B, act, out_dt):
     assert_close(Y, ref, "bf16", f"column tile act={act} out={out_dt}")
 
 
+def test_small_tile_instance_every_epilogue(B):
+    # Products with fewer than 128 tiles of 256 x 192 run on 128 x 96 tiles
+    # (four waves, two workgroups per CU).  770 x 544 -> 392 (12 large tiles,
+    # 7 x 5 small ones, ragged in M and N) through every epilogue that
+    # instance serves: bias + GeLU with the pre-activation saved, bias with
+    # bf16 and fp32 (LDS-staged) outputs, plain fp32 and bf16 row products,
+    # and the NT product of a linear backward's dX; element-wise vs the oracle.
+    T, k, n = 770, 544, 392
+    bf, f32 = torch.bfloat16, torch.float32
+    g = torch.Generator().manual_seed(71)
+    X = (torch.randn(T, k, generator=g)).to(bf)
+    W = (0.02 * torch.randn(k, n, generator=g)).to(bf)
+    b = (0.02 * torch.randn(n, generator=g)).to(bf)
+    Xd, Wd, bd = dev(X), dev(W), dev(b)
+    H = torch.empty(T, n, dtype=bf, device="cuda")
+    Y = torch.empty(T, n, dtype=bf, device="cuda")
+    B.tp_column_linear(Xd, Wd, bd, H, Y, T, k, n, 1, 0, bf, bf, B.TP_ACT_GELU_TANH)
+    Yb = torch.empty(T, n, dtype=bf, device="cuda")
+    B.tp_column_linear(Xd, Wd, bd, Yb, None, T, k, n, 1, 0, bf, bf, B.TP_ACT_NONE)
+    Yf = torch.empty(T, n, dtype=f32, device="cuda")
+    B.tp_column_linear(Xd, Wd, bd, Yf, None, T, k, n, 1, 0, bf, f32, B.TP_ACT_NONE)
+    Zf = torch.empty(T, n, dtype=f32, device="cuda")
+    B.tp_row_linear(Xd, Wd, Zf, T, k, n, 1, 0, bf, f32)
+    Zb = torch.empty(T, n, dtype=bf, device="cuda")
+    B.tp_row_linear(Xd, Wd, Zb, T, k, n, 1, 0, bf, bf)
+    dY = (torch.randn(T, n, generator=g)).to(bf)
+    dX = torch.empty(T, k, dtype=f32, device="cuda")
+    dW = torch.empty(k, n, dtype=f32, device="cuda")
+    B.tp_linear_bwd(Xd, Wd, dev(dY), dX, dW, None, T, k, n, bf)
+    torch.cuda.synchronize()
+    rY = oracle.column_linear(X, W, b)
+    _whole(Y, rY, "bf16", "small tiles: saved pre-activation")
+    _whole(H, oracle.column_linear(X, W, b, gelu=True), "bf16", "small tiles: GeLU")
+    _whole(Yb, rY, "bf16", "small tiles: bias, bf16 out")
+    _whole(Yf, rY, "bf16", "small tiles: bias, fp32 out")
+    rZ = oracle.row_linear(X, W)
+    _whole(Zf, rZ, "bf16", "small tiles: plain fp32")
+    _whole(Zb, rZ, "bf16", "small tiles: plain bf16")
+    ref = oracle.linear_bwd(X, W, dY, with_db=False)
+    _whole(dX, ref["dX"], "bf16", "small tiles: NT dX")
+    _whole(dW, ref["dW"], "bf16", "linear bwd dW (TN)")
+
+
 def test_row_linear_ragged_partials_sum(B):
     # row-parallel partials of t = 4 ranks, summed on the device
     T, n_full, hout, t = 77, 512, 136, 4
