@@ -144,12 +144,13 @@ def test_column_linear_tile_kernel_epilogues(B, act, out_dt):
 
 def test_small_tile_instance_every_epilogue(B):
     # Products with fewer than 128 tiles of 256 x 192 run on 128 x 96 tiles
-    # (four waves, two workgroups per CU).  770 x 544 -> 392 (12 large tiles,
+    # (four waves, two workgroups per CU).  770 x 544 -> 416 (12 large tiles,
     # 7 x 5 small ones, ragged in M and N) through every epilogue that
     # instance serves: bias + GeLU with the pre-activation saved, bias with
     # bf16 and fp32 (LDS-staged) outputs, plain fp32 and bf16 row products,
-    # and the NT product of a linear backward's dX; element-wise vs the oracle.
-    T, k, n = 770, 544, 392
+    # and the NT product of a linear backward's dX (770 x 416 -> 544, K a
+    # multiple of 32 and not of 64); element-wise vs the oracle.
+    T, k, n = 770, 544, 416
     bf, f32 = torch.bfloat16, torch.float32
     g = torch.Generator().manual_seed(71)
     X = (torch.randn(T, k, generator=g)).to(bf)
