@@ -111,6 +111,43 @@ def ingest_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, comman
     print(json.dumps(out, indent=1))
 
 
+TILE_NAMES = {"TileCfg<256, 192, 8, 2, 1>": "256x192", "TileCfg<256, 192, 8, 4, 1>": "256x192tn",
+              "TileCfg<128, 96, 4, 2, 2>": "128x96"}
+
+
+def kernel_label(name: str) -> str:
+    """A short readable label for a kernel name from a rocprofv3 table:
+    demangled (c++filt) when it is mangled, without namespaces, `void` and
+    the parameter list, tile configurations by their tile size."""
+    import subprocess
+    if name.startswith("_Z"):
+        try:
+            # c++filt does not know the bf16 builtin's code; spell it as a
+            # vendor type of the same name
+            name = subprocess.run(["c++filt", name.replace("DF16b", "u6__bf16")],
+                                  capture_output=True, text=True,
+                                  timeout=10).stdout.strip() or name
+        except (OSError, subprocess.SubprocessError):
+            pass
+    name = name.replace("tpmlp::(anonymous namespace)::", "").replace("tpmlp::", "")
+    name = name.replace("(anonymous namespace)::", "")
+    if name.startswith("void "):
+        name = name[5:]
+    if name.endswith(")") and "(" in name:          # drop the parameter list
+        depth = 0
+        for i in range(len(name) - 1, -1, -1):
+            depth += {")": 1, "(": -1}.get(name[i], 0)
+            if depth == 0:
+                name = name[:i]
+                break
+    for cfg, short in TILE_NAMES.items():
+        name = name.replace(cfg, short)
+    # the profiler's own demangler reads two bf16 template arguments as this
+    name = name.replace("bool _Accum", "bf16, bf16")
+    name = name.replace("__bf16", "bf16").replace("unsigned short", "u16")
+    return name if len(name) <= 110 else name[:107] + "..."
+
+
 COPY_ROWS, COPY_COLS = 8192, 8192
 
 MFMA_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES",
@@ -150,7 +187,7 @@ def ingest_mfma(pmc_dir: str, simds: int = 1024, xcds: int = 8):
         mean = lambda k: sum(d.get(k, 0.0) for d in ds) / len(ds)
         act, ns = mean("GRBM_GUI_ACTIVE") / xcds, mean("ns")
         busy = mean("SQ_VALU_MFMA_BUSY_CYCLES") / (act * simds) if act else float("nan")
-        short = name if len(name) <= 90 else name[:87] + "..."
+        short = kernel_label(name)
         print(f"| `{short}` | {len(ds)} | {mean('SQ_INSTS_VALU_MFMA_MOPS_BF16') * 512 / 1e9:.1f} | "
               f"{100 * busy:.1f}% | {act:.0f} | {act / ns:.2f} | {ns / 1e3:.1f} |")
 
@@ -193,7 +230,7 @@ def ingest_pmc(pmc_dir: str, xcds: int = 8, cus: int = 256):
             v = mean(c)
             frac = f" ({v / (act * cus):.3f})" if act and c != "GRBM_GUI_ACTIVE" else ""
             cells.append(f"{v:.4g}{frac}")
-        short = name if len(name) <= 90 else name[:87] + "..."
+        short = kernel_label(name)
         print(f"| `{short}` | {len(ds)} | {mean('ns') / 1e3:.1f} | " + " | ".join(cells) + " |")
 
 
@@ -263,7 +300,7 @@ def trace_summary(trace_dir: str, warmup: int, steps: int):
     print(f"| kernel | calls | mean us | min us | max us | calls in the timed steps | mean us in the timed steps |")
     print("|---|---|---|---|---|---|---|")
     for _, name, c, mean, mn, mx, nt, tmean in rows:
-        short = name if len(name) <= 90 else name[:87] + "..."
+        short = kernel_label(name)
         print(f"| `{short}` | {c} | {mean:.1f} | {mn:.1f} | {mx:.1f} | {nt} | {tmean:.1f} |")
 
 
