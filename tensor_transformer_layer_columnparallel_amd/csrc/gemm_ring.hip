@@ -86,14 +86,17 @@ constexpr int kReadGroups = 3;
 constexpr int kXcds = 8;
 constexpr int kCUs = 256;
 
-// A tile configuration: BM x BN outputs per workgroup of NW waves, WM of them
-// along M, at most OCC workgroups per CU.  The rings hold kABufs 64-k units
-// of A and kBBufs of B.
-template <int BM_, int BN_, int NW_, int WM_, int OCC_>
+// A tile configuration: BM x BN outputs per pipeline of NW waves, WM of them
+// along M, KS pipelines per workgroup, at most OCC workgroups per CU.  Each
+// pipeline has its own rings of kABufs 64-k units of A and kBBufs of B.
+// With KS = 2 the workgroup's two pipelines compute the same tile over the
+// two halves of K, and the second hands its sums to the first at the end.
+template <int BM_, int BN_, int NW_, int WM_, int OCC_, int KS_ = 1>
 struct TileCfg {
-    static constexpr int BM = BM_, BN = BN_, NW = NW_, WM = WM_, OCC = OCC_;
+    static constexpr int BM = BM_, BN = BN_, NW = NW_, WM = WM_, OCC = OCC_, KS = KS_;
     static constexpr int ABytes = kABufs * BM * 64 * 2;
     static constexpr int BBytes = kBBufs * BN * 64 * 2;
+    static_assert(KS == 1 || KS == 2, "one pipeline, or two over the halves of K");
 };
 // 256 x 192: every product of the GPT-3 shard splits into whole waves of 256
 // CUs (256, 512 or 1536 tiles); 8 waves, 2 x 4 (NN, NT) or 4 x 2 (TN); rings
@@ -107,6 +110,14 @@ using TileTN = TileCfg<256, 192, 8, 4, 1>;
 // of DMA instructions per step as in the large tile (4 for A's unit, 3 for
 // B's), so the schedule and its waits are the same.
 using TileSmall = TileCfg<128, 96, 4, 2, 2>;
+// The same tile with K split between two pipelines of four waves in one
+// workgroup (rings of 2 x 72 KiB, one workgroup per CU), for products with
+// at most one 128 x 96 tile per CU: a lone four-wave workgroup spends about
+// 500 cycles per 32-k slab on 192 cycles of MFMAs, its waits and barriers
+// exposed with one wave per SIMD, and the second pipeline fills them while
+// halving the slabs each one walks.  The halves' sums are added in a fixed
+// order (first half + second half).
+using TileSplit = TileCfg<128, 96, 4, 2, 1, 2>;
 
 // Raw buffer descriptor (gfx9 family): base, stride 0, byte extent, word 3.
 __device__ __forceinline__ i32x4 make_desc(const void* base, uint32_t bytes)
@@ -566,7 +577,7 @@ __device__ __forceinline__ void tile_of_block(GemmArgs& p, int tiles_m, int tile
 }
 
 template <class Cfg, bool A_KMAJ, bool B_KMAJ, Epi EPI, typename OutT>
-__global__ __launch_bounds__(64 * Cfg::NW, Cfg::OCC) void gemm_ring_kernel(GemmArgs p,
+__global__ __launch_bounds__(64 * Cfg::NW * Cfg::KS, Cfg::OCC) void gemm_ring_kernel(GemmArgs p,
                                                                            int tiles_m,
                                                                            int tiles_n,
                                                                            int group_m)
@@ -590,13 +601,22 @@ __global__ __launch_bounds__(64 * Cfg::NW, Cfg::OCC) void gemm_ring_kernel(GemmA
     // DMA instructions per wave at even steps (A) and at odd steps (B).
     constexpr int kDmaEven = A_KMAJ ? PlanAU::kPerUnit : PlanAP::kPer;
     constexpr int kDmaOdd = B_KMAJ ? PlanBU::kPerUnit : PlanBP::kPer;
-    __shared__ __attribute__((aligned(1024))) bf16 smem[(kABytes + kBBytes) / 2];
-    bf16* const sa = smem;                  // A ring
-    bf16* const sb = smem + kABytes / 2;    // B ring
+    constexpr int KS = Cfg::KS;
+    // A workgroup of two pipelines ends with the second handing its sums to
+    // the first and leaving; only the register-path epilogues (no barrier,
+    // no workgroup-wide loops) follow that.
+    static_assert(KS == 1 || (EPI != Epi::DGelu && EPI != Epi::StoreT &&
+                              !(sizeof(OutT) == 4 && (EPI == Epi::Store || EPI == Epi::Bias))),
+                  "split-K workgroups take the register-path epilogues");
+    __shared__ __attribute__((aligned(1024))) bf16 smem[KS * (kABytes + kBBytes) / 2];
 
     const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wave_wg = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int half = wave_wg / NW;          // the pipeline (0 unless KS = 2)
+    const int wave = wave_wg % NW;          // the wave inside its pipeline
     const int wm = wave / kWavesN, wn = wave % kWavesN;
+    bf16* const sa = smem + half * ((kABytes + kBBytes) / 2);   // A ring
+    bf16* const sb = sa + kABytes / 2;                          // B ring
 
     int tm, tn;
     tile_of_block<OutT>(p, tiles_m, tiles_n, group_m, tm, tn);
@@ -604,16 +624,28 @@ __global__ __launch_bounds__(64 * Cfg::NW, Cfg::OCC) void gemm_ring_kernel(GemmA
 
     const int64_t lda = p.lda ? p.lda : (A_KMAJ ? p.K : p.M);
     const int64_t ldb = p.ldb ? p.ldb : (B_KMAJ ? p.K : p.N);
-    const i32x4 da = make_desc(p.A, (uint32_t)operand_bytes(A_KMAJ, p.M, p.K, lda));
-    const i32x4 db = make_desc(p.B, (uint32_t)operand_bytes(B_KMAJ, p.N, p.K, ldb));
+    // The k range of this pipeline: all of K, or with two pipelines the
+    // first kspan = ceil(K / 2) rounded up to a 64-k unit and the rest.
+    // Both walk kspan (the same slabs, so the same barriers); the loads of
+    // k past the range read zeros.
+    int64_t kspan = p.K, k0 = 0, klen = p.K;
+    if constexpr (KS == 2) {
+        kspan = (p.K + 127) / 128 * 64;
+        k0 = half * kspan;
+        klen = p.K - k0 < kspan ? (p.K - k0 > 0 ? p.K - k0 : 0) : kspan;
+    }
+    const bf16* const A = static_cast<const bf16*>(p.A) + (A_KMAJ ? k0 : k0 * lda);
+    const bf16* const Bp = static_cast<const bf16*>(p.B) + (B_KMAJ ? k0 : k0 * ldb);
+    const i32x4 da = make_desc(A, (uint32_t)operand_bytes(A_KMAJ, p.M, klen, lda));
+    const i32x4 db = make_desc(Bp, (uint32_t)operand_bytes(B_KMAJ, p.N, klen, ldb));
     PlanAU pau;
     PlanAP pap;
-    if constexpr (A_KMAJ) pau.init(wave, lane, m0, lda, p.M, p.K);
-    else pap.init(wave, lane, m0, lda, p.M, p.K);
+    if constexpr (A_KMAJ) pau.init(wave, lane, m0, lda, p.M, klen);
+    else pap.init(wave, lane, m0, lda, p.M, klen);
     PlanBU pbu;
     PlanBP pbp;
-    if constexpr (B_KMAJ) pbu.init(wave, lane, n0, ldb, p.N, p.K);
-    else pbp.init(wave, lane, n0, ldb, p.N, p.K);
+    if constexpr (B_KMAJ) pbu.init(wave, lane, n0, ldb, p.N, klen);
+    else pbp.init(wave, lane, n0, ldb, p.N, klen);
     const uint32_t a_base = lds_addr(sa), b_base = lds_addr(sb);
 
     const int wrow_a = wm * kWaveM, wrow_b = wn * kWaveN;
@@ -706,7 +738,7 @@ __global__ __launch_bounds__(64 * Cfg::NW, Cfg::OCC) void gemm_ring_kernel(GemmA
     using Even = std::integral_constant<bool, false>;
     using Odd = std::integral_constant<bool, true>;
 
-    const int nk = (int)((p.K + kBK - 1) / kBK);
+    const int nk = (int)((kspan + kBK - 1) / kBK);
     if (nk > 0) {
         static_assert(kLead == 5, "prologue parity pattern");
 #pragma unroll
@@ -732,6 +764,32 @@ __global__ __launch_bounds__(64 * Cfg::NW, Cfg::OCC) void gemm_ring_kernel(GemmA
     }
     wait_vmcnt<0>();
     wait_lgkmcnt0();
+    if constexpr (KS == 2) {
+        // The second pipeline's sums go through LDS (48 KiB, in the rings
+        // that nobody reads any more) to the wave of the first pipeline that
+        // holds the same outputs, which adds them to its own.
+        static_assert(NW * kFragM * kFragN * 64 * 16 <= kABytes + kBBytes, "hand-over space");
+        f32x4* const red = reinterpret_cast<f32x4*>(smem);
+        barrier();   // both pipelines are done with their rings
+        if (half == 1) {
+#pragma unroll
+            for (int a = 0; a < kFragM; ++a)
+#pragma unroll
+                for (int b = 0; b < kFragN; ++b)
+                    red[((wave * kFragM + a) * kFragN + b) * 64 + lane] = acc[a][b];
+        }
+        wait_lgkmcnt0();   // s_barrier itself does not wait for LDS stores
+        barrier();
+        if (half == 1) return;   // no barrier follows in the register-path epilogues
+#pragma unroll
+        for (int a = 0; a < kFragM; ++a)
+#pragma unroll
+            for (int b = 0; b < kFragN; ++b) {
+                const f32x4 r = red[((wave * kFragM + a) * kFragN + b) * 64 + lane];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[a][b][e] = acc[a][b][e] + r[e];
+            }
+    }
     store_tile<Cfg, EPI, OutT>(p, acc, smem, m0, n0, tm, wm, wrow_a, wrow_b, lane);
 }
 
@@ -751,8 +809,8 @@ hipError_t launch_cfg(const GemmArgs& p, hipStream_t stream)
     // one product's tiles for its 32 CUs, so they take the 4-row groups too.
     const int group_m = tm * tn > 2 * kCUs || !BK || p.batch > 1 ? 4 : 0;
     hipLaunchKernelGGL((gemm_ring_kernel<Cfg, AK, BK, E, O>),
-                       dim3((unsigned)(tm * tn * p.batch)), dim3(64 * Cfg::NW), 0, stream, p, tm,
-                       tn, group_m);
+                       dim3((unsigned)(tm * tn * p.batch)), dim3(64 * Cfg::NW * Cfg::KS), 0,
+                       stream, p, tm, tn, group_m);
     return hipGetLastError();
 }
 
@@ -761,13 +819,23 @@ hipError_t launch_cfg(const GemmArgs& p, hipStream_t stream)
 // but measured about 35% slower: with one wave per SIMD nothing covers a
 // wave's own waits.  Products with a K-contiguous A and a forward epilogue
 // that would have fewer 256 x 192 tiles than half the CUs run on 128 x 96
-// tiles instead (two workgroups of four waves per CU).
+// tiles instead: two workgroups of four waves per CU, or, when there are no
+// more 128 x 96 tiles than CUs and K has at least four 64-k units, one
+// workgroup of two K-split pipelines per tile (results from registers only).
 template <bool AK, bool BK, Epi E, typename O>
 hipError_t launch(const GemmArgs& p, hipStream_t stream)
 {
     if constexpr (AK && (E == Epi::Store || E == Epi::Bias || E == Epi::BiasGelu)) {
         const int64_t tiles = ((p.M + kBM - 1) / kBM) * ((p.N + kBN - 1) / kBN) * p.batch;
-        if (tiles < kCUs / 2) return launch_cfg<TileSmall, AK, BK, E, O>(p, stream);
+        if (tiles < kCUs / 2) {
+            if constexpr (sizeof(O) == 2 || E == Epi::BiasGelu) {
+                const int64_t small = ((p.M + TileSmall::BM - 1) / TileSmall::BM) *
+                                      ((p.N + TileSmall::BN - 1) / TileSmall::BN) * p.batch;
+                if (small <= kCUs && p.K >= 256)
+                    return launch_cfg<TileSplit, AK, BK, E, O>(p, stream);
+            }
+            return launch_cfg<TileSmall, AK, BK, E, O>(p, stream);
+        }
     }
     return launch_cfg<std::conditional_t<AK, TileNN, TileTN>, AK, BK, E, O>(p, stream);
 }

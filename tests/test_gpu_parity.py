@@ -143,13 +143,15 @@ def test_column_linear_tile_kernel_epilogues(B, act, out_dt):
 
 
 def test_small_tile_instance_every_epilogue(B):
-    # Products with fewer than 128 tiles of 256 x 192 run on 128 x 96 tiles
-    # (four waves, two workgroups per CU).  770 x 544 -> 416 (12 large tiles,
-    # 7 x 5 small ones, ragged in M and N) through every epilogue that
-    # instance serves: bias + GeLU with the pre-activation saved, bias with
-    # bf16 and fp32 (LDS-staged) outputs, plain fp32 and bf16 row products,
-    # and the NT product of a linear backward's dX (770 x 416 -> 544, K a
-    # multiple of 32 and not of 64); element-wise vs the oracle.
+    # Products with fewer than 128 tiles of 256 x 192 run on 128 x 96 tiles.
+    # 770 x 544 -> 416 (12 large tiles, 7 x 5 small ones, ragged in M and N)
+    # through every epilogue those instances serve: bias + GeLU with the
+    # pre-activation saved, bias with bf16 output and plain bf16 row products
+    # (at most one small tile per CU and K >= 256: the K-split workgroups,
+    # K = 320 + 224), bias with fp32 (LDS-staged) output and plain fp32 row
+    # products (four-wave workgroups), and the NT product of a linear
+    # backward's dX (770 x 416 -> 544, K a multiple of 32 and not of 64);
+    # element-wise vs the oracle.
     T, k, n = 770, 544, 416
     bf, f32 = torch.bfloat16, torch.float32
     g = torch.Generator().manual_seed(71)
@@ -184,6 +186,38 @@ def test_small_tile_instance_every_epilogue(B):
     ref = oracle.linear_bwd(X, W, dY, with_db=False)
     _whole(dX, ref["dX"], "bf16", "small tiles: NT dX")
     _whole(dW, ref["dW"], "bf16", "linear bwd dW (TN)")
+
+
+@pytest.mark.parametrize("T,k,n", [(4000, 288, 1000), (1000, 288, 488), (520, 2080, 200)],
+                         ids=["four-wave", "split-288", "split-2080"])
+def test_small_tile_register_epilogues(B, T, k, n):
+    # The register-path epilogues (bias + GeLU with the pre-activation saved,
+    # bias, plain; bf16 out) on both 128 x 96 instances: 4000 x 288 -> 1000
+    # has 32 x 11 small tiles, more than the CUs, so it takes the four-wave
+    # workgroups; the other two have at most one small tile per CU and take
+    # the two K-split pipelines, with halves of 192 + 96 and 1088 + 992 k
+    # (the second pipeline's last loads past K read zeros).  Ragged in M and
+    # N; element-wise vs the oracle.
+    _log(f"case small tiles register epilogues {T}x{k}x{n}")
+    bf = torch.bfloat16
+    g = torch.Generator().manual_seed(73)
+    X = torch.randn(T, k, generator=g).to(bf)
+    W = (0.02 * torch.randn(k, n, generator=g)).to(bf)
+    b = (0.02 * torch.randn(n, generator=g)).to(bf)
+    Xd, Wd, bd = dev(X), dev(W), dev(b)
+    H = torch.empty(T, n, dtype=bf, device="cuda")
+    Y = torch.empty(T, n, dtype=bf, device="cuda")
+    B.tp_column_linear(Xd, Wd, bd, H, Y, T, k, n, 1, 0, bf, bf, B.TP_ACT_GELU_TANH)
+    Yb = torch.empty(T, n, dtype=bf, device="cuda")
+    B.tp_column_linear(Xd, Wd, bd, Yb, None, T, k, n, 1, 0, bf, bf, B.TP_ACT_NONE)
+    Zb = torch.empty(T, n, dtype=bf, device="cuda")
+    B.tp_row_linear(Xd, Wd, Zb, T, k, n, 1, 0, bf, bf)
+    torch.cuda.synchronize()
+    rY = oracle.column_linear(X, W, b)
+    _whole(Y, rY, "bf16", "small tiles: saved pre-activation")
+    _whole(H, oracle.column_linear(X, W, b, gelu=True), "bf16", "small tiles: GeLU")
+    _whole(Yb, rY, "bf16", "small tiles: bias, bf16 out")
+    _whole(Zb, oracle.row_linear(X, W), "bf16", "small tiles: plain bf16")
 
 
 def test_row_linear_ragged_partials_sum(B):

@@ -141,8 +141,10 @@ def test_replay_constants_match_the_kernel_source():
     # every tile configuration: loads per wave of a 64-deep unit of R rows
     # (R / 8 loads of 8 rows) or of a slab pair (2 R / 16 loads of 64 16-byte
     # chunks), both R * 64 * 2 bytes, must be the counts the waits assume
-    cfgs = re.findall(r"using Tile\w+ = TileCfg<(\d+), (\d+), (\d+), (\d+), (\w+)>;", src)
-    assert len(cfgs) >= 3, cfgs
+    # (BM, BN, NW waves per pipeline, WM, occupancy[, pipelines per workgroup])
+    cfgs = re.findall(r"using Tile\w+ = TileCfg<(\d+), (\d+), (\d+), (\d+), (\w+)(?:, (\d+))?>;",
+                      src)
+    assert len(cfgs) >= 4, cfgs
     for bm, bn, nw in (tuple(map(int, c[:3])) for c in cfgs):
         assert bm // 8 // nw == 2 * bm // 16 // nw == 4, (bm, nw)   # even steps (A)
         assert bn // 8 // nw == 2 * bn // 16 // nw == 3, (bn, nw)   # odd steps (B)
