@@ -818,24 +818,26 @@ hipError_t launch_cfg(const GemmArgs& p, hipStream_t stream)
 // (one per SIMD, 256 x 48 or 128 x 96 outputs each) read less LDS per flop
 // but measured about 35% slower: with one wave per SIMD nothing covers a
 // wave's own waits.  Products with a K-contiguous A and a forward epilogue
-// that would have fewer 256 x 192 tiles than half the CUs run on 128 x 96
-// tiles instead: two workgroups of four waves per CU, or, when there are no
-// more 128 x 96 tiles than CUs and K has at least four 64-k units, one
-// workgroup of two K-split pipelines per tile (results from registers only).
+// run on 128 x 96 tiles instead:
+//  - on two K-split pipelines per workgroup when one product has no more
+//    128 x 96 tiles than CUs, K has at least four 64-k units and the results
+//    leave from registers.  This depends on the product alone, not on the
+//    batch: the split adds each output's k range in another order, and a
+//    batch must give the same bits as its products launched one by one;
+//  - otherwise on two workgroups of four waves per CU when the launch would
+//    have fewer 256 x 192 tiles than half the CUs (the same k order as the
+//    large tiles).
 template <bool AK, bool BK, Epi E, typename O>
 hipError_t launch(const GemmArgs& p, hipStream_t stream)
 {
     if constexpr (AK && (E == Epi::Store || E == Epi::Bias || E == Epi::BiasGelu)) {
-        const int64_t tiles = ((p.M + kBM - 1) / kBM) * ((p.N + kBN - 1) / kBN) * p.batch;
-        if (tiles < kCUs / 2) {
-            if constexpr (sizeof(O) == 2 || E == Epi::BiasGelu) {
-                const int64_t small = ((p.M + TileSmall::BM - 1) / TileSmall::BM) *
-                                      ((p.N + TileSmall::BN - 1) / TileSmall::BN) * p.batch;
-                if (small <= kCUs && p.K >= 256)
-                    return launch_cfg<TileSplit, AK, BK, E, O>(p, stream);
-            }
-            return launch_cfg<TileSmall, AK, BK, E, O>(p, stream);
+        if constexpr (sizeof(O) == 2 || E == Epi::BiasGelu) {
+            const int64_t small = ((p.M + TileSmall::BM - 1) / TileSmall::BM) *
+                                  ((p.N + TileSmall::BN - 1) / TileSmall::BN);
+            if (small <= kCUs && p.K >= 256) return launch_cfg<TileSplit, AK, BK, E, O>(p, stream);
         }
+        const int64_t tiles = ((p.M + kBM - 1) / kBM) * ((p.N + kBN - 1) / kBN) * p.batch;
+        if (tiles < kCUs / 2) return launch_cfg<TileSmall, AK, BK, E, O>(p, stream);
     }
     return launch_cfg<std::conditional_t<AK, TileNN, TileTN>, AK, BK, E, O>(p, stream);
 }

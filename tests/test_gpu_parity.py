@@ -984,6 +984,8 @@ LAYER_FWD = [  # (tokens, h, ffn, t, dtype, bias, save)
     (96, 256, 2 * 128, 2, "bf16", True, False),    # shard narrower than a tile: general kernel
     (64, 128, 512, 4, "f32", True, True),          # fp32: general kernel, one launch per shard
     (272, 256, 1 * 448, 1, "bf16", True, True),    # t = 1: the unsharded layer
+    # 40 small tiles per shard (K-split pipelines), 320 for the batch
+    (1000, 256, 8 * 480, 8, "bf16", True, True),
     (0, 256, 8 * 192, 8, "bf16", True, True),      # no tokens: nothing to do
 ]
 
