@@ -638,6 +638,85 @@ def cpu_baseline(w, d_h, seconds: float):
                       f"({done // chunk} chunks of {chunk}), {el:.1f} s wall"}
 
 
+BUSY_CU_SHAPES = ((2048, 12288, 6144), (1536, 12288, 6144), (1024, 12288, 6144), (2048, 12288, 4608))
+
+
+def busy_cus_sweep(rounds: int = 2, reps: int = 40):
+    """The column product (bias + GeLU, pre-activation saved, K = 12288) with
+    256, 192 and 128 tiles of 256 x 192 (T = 2048, 1536, 1024 at n = 6144)
+    and the QKV shard's shape (192 tiles): median time per launch over `reps`
+    event-timed launches after 150 ms of warm-up calls.  Under rocprofv3
+    --pmc the dispatches are told apart by their workgroup counts."""
+    import torch
+    from tensor_transformer_layer_columnparallel_amd import binding as B
+    dev, bf = "cuda", torch.bfloat16
+    out = []
+    for rnd in range(rounds):
+        for T, h, n in BUSY_CU_SHAPES:
+            g = torch.Generator(device=dev).manual_seed(3)
+            X = torch.randn(T, h, device=dev, generator=g).to(bf)
+            W = (0.02 * torch.randn(h, n, device=dev, generator=g)).to(bf)
+            b = (0.02 * torch.randn(n, device=dev, generator=g)).to(bf)
+            H = torch.empty(T, n, device=dev, dtype=bf)
+            Y = torch.empty(T, n, device=dev, dtype=bf)
+            f = lambda: B.tp_column_linear(X, W, b, H, Y, T, h, n, 1, 0, bf, bf,
+                                           B.TP_ACT_GELU_TANH)
+            warm(f, 150.0)
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(reps)]
+            for e0, e1 in ev:
+                e0.record()
+                f()
+                e1.record()
+            torch.cuda.synchronize()
+            ts = sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in ev)
+            us = ts[len(ts) // 2]
+            tiles = ((T + 255) // 256) * ((n + 191) // 192)
+            r = {"round": rnd, "T": T, "h": h, "n": n, "tiles": tiles, "median_us": round(us, 1),
+                 "tflops": round(2 * T * h * n / us / 1e6, 1)}
+            out.append(r)
+            print(json.dumps(r), flush=True)
+    return out
+
+
+def ingest_clock(pmc_dir: str, xcds: int = 8, simds: int = 1024, cus: int = 256):
+    """Markdown table from a rocprofv3 --pmc run of SQ_VALU_MFMA_BUSY_CYCLES and
+    GRBM_GUI_ACTIVE over --busy-cus-sweep: per workgroup count (one
+    workgroup per CU), the median over the dispatches after the first
+    quarter of the kernel's duration, its engine clock (GPU-active cycles of
+    one XCD over the duration) and the MFMA busy fraction of all SIMDs and
+    of the SIMDs in use."""
+    import csv
+    import glob
+    import statistics
+    disp = {}
+    for path in glob.glob(os.path.join(pmc_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                if "gemm_ring" not in row["Kernel_Name"]:
+                    continue
+                d = disp.setdefault(row["Dispatch_Id"], {
+                    "wgs": int(row["Grid_Size"]) // int(row["Workgroup_Size"]),
+                    "ns": int(row["End_Timestamp"]) - int(row["Start_Timestamp"])})
+                d[row["Counter_Name"]] = d.get(row["Counter_Name"], 0.0) + float(row["Counter_Value"])
+    if not disp:
+        raise SystemExit(f"no GEMM dispatches under {pmc_dir}")
+    per = {}
+    for k in sorted(disp, key=int):
+        per.setdefault(disp[k]["wgs"], []).append(disp[k])
+    print("| workgroups (CUs busy) | dispatches | duration us | clock GHz | MFMA busy, all SIMDs | "
+          "MFMA busy, SIMDs in use |")
+    print("|---|---|---|---|---|---|")
+    for wgs, ds in sorted(per.items()):
+        ds = ds[len(ds) // 4:]
+        med = lambda f: statistics.median(f(d) for d in ds)
+        act = lambda d: d["GRBM_GUI_ACTIVE"] / xcds
+        busy = med(lambda d: d["SQ_VALU_MFMA_BUSY_CYCLES"] / (act(d) * simds))
+        print(f"| {wgs} | {len(ds)} | {med(lambda d: d['ns']) / 1e3:.1f} | "
+              f"{med(lambda d: act(d) / d['ns']):.2f} | {100 * busy:.1f}% | "
+              f"{100 * busy * cus / min(wgs, cus):.1f}% |")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -679,7 +758,19 @@ def main():
     ap.add_argument("--ingest-mfma", metavar="PMC_DIR",
                     help="MFMA work, busy fraction and clock per GEMM from a rocprofv3 --pmc run "
                          "of " + " ".join(MFMA_COUNTERS))
+    ap.add_argument("--busy-cus-sweep", action="store_true",
+                    help="only time the column product on 256, 192 and 128 tiles (and the QKV "
+                         "shard's shape), for the clock and MFMA counters per busy CU count")
+    ap.add_argument("--ingest-clock", metavar="PMC_DIR",
+                    help="clock and MFMA busy fraction per workgroup count from a rocprofv3 --pmc "
+                         "run of SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE over --busy-cus-sweep")
     args = ap.parse_args()
+    if args.ingest_clock:
+        ingest_clock(args.ingest_clock)
+        return
+    if args.busy_cus_sweep:
+        busy_cus_sweep()
+        return
     if args.ingest_mfma:
         ingest_mfma(args.ingest_mfma)
         return
