@@ -111,8 +111,8 @@ def ingest_counters(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, comman
     print(json.dumps(out, indent=1))
 
 
-TILE_NAMES = {"TileCfg<256, 192, 8, 2, 1>": "256x192", "TileCfg<256, 192, 8, 4, 1>": "256x192tn",
-              "TileCfg<128, 96, 4, 2, 2>": "128x96"}
+TILE_NAMES = {"TileCfg<256, 192, 8, 2, 1, 1>": "256x192", "TileCfg<256, 192, 8, 4, 1, 1>": "256x192tn",
+              "TileCfg<128, 96, 4, 2, 2, 1>": "128x96", "TileCfg<128, 96, 4, 2, 1, 2>": "128x96 K-split"}
 
 
 def kernel_label(name: str) -> str:
