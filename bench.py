@@ -679,6 +679,34 @@ def busy_cus_sweep(rounds: int = 2, reps: int = 40):
     return out
 
 
+def column_load(T: int, seconds: float):
+    """The column product (bias + GeLU, saved pre-activation, K = 12288,
+    n = 6144) on T tokens back to back for `seconds`, its launch rate
+    printed twice a second: a steady load beside which power and clock are
+    read (amd-smi)."""
+    import torch
+    from tensor_transformer_layer_columnparallel_amd import binding as B
+    h, n, dev, bf = 12288, 6144, "cuda", torch.bfloat16
+    g = torch.Generator(device=dev).manual_seed(3)
+    X = torch.randn(T, h, device=dev, generator=g).to(bf)
+    W = (0.02 * torch.randn(h, n, device=dev, generator=g)).to(bf)
+    b = (0.02 * torch.randn(n, device=dev, generator=g)).to(bf)
+    H = torch.empty(T, n, device=dev, dtype=bf)
+    Y = torch.empty(T, n, device=dev, dtype=bf)
+    t0 = last = time.perf_counter()
+    calls = 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(20):
+            B.tp_column_linear(X, W, b, H, Y, T, h, n, 1, 0, bf, bf, B.TP_ACT_GELU_TANH)
+        torch.cuda.synchronize()
+        calls += 20
+        now = time.perf_counter()
+        if now - last > 0.5:
+            print(f"column load T={T}: {now - t0:.1f} s, {calls} launches, "
+                  f"{1e6 * (now - t0) / calls:.1f} us per launch", flush=True)
+            last = now
+
+
 def ingest_clock(pmc_dir: str, xcds: int = 8, simds: int = 1024, cus: int = 256):
     """Markdown table from a rocprofv3 --pmc run of SQ_VALU_MFMA_BUSY_CYCLES and
     GRBM_GUI_ACTIVE over --busy-cus-sweep: per workgroup count (one
@@ -764,7 +792,13 @@ def main():
     ap.add_argument("--ingest-clock", metavar="PMC_DIR",
                     help="clock and MFMA busy fraction per workgroup count from a rocprofv3 --pmc "
                          "run of SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE over --busy-cus-sweep")
+    ap.add_argument("--column-load", nargs=2, type=float, metavar=("TOKENS", "SECONDS"),
+                    help="only run the column product on TOKENS tokens back to back for SECONDS "
+                         "(a steady load for power and clock readings)")
     args = ap.parse_args()
+    if args.column_load:
+        column_load(int(args.column_load[0]), args.column_load[1])
+        return
     if args.ingest_clock:
         ingest_clock(args.ingest_clock)
         return
