@@ -25,7 +25,12 @@ hipError_t gemm_ring(const GemmArgs& p, Layout layout, Epi epi, Elt out, hipStre
 constexpr int64_t kGemmRingTileRows = 256;
 
 // out[c][r] = in[r][c] for 16-bit elements, in [rows][cols] (cols % 8 == 0).
-hipError_t transpose16(const void* in, void* out, int64_t rows, int64_t cols, hipStream_t stream);
+// With col_part non-null the same launch also does column_finish(col_part,
+// col_out, col_parts, col_count) (below): the backward runs the bias
+// gradient's last pass beside the transpose that follows the dY product.
+hipError_t transpose16(const void* in, void* out, int64_t rows, int64_t cols, hipStream_t stream,
+                       const float* col_part = nullptr, float* col_out = nullptr,
+                       int64_t col_parts = 0, int64_t col_count = 0);
 
 // out[e] = sum_{r=0}^{t-1} parts[r][e] (fp32, rank order), parts[r] at
 // element offset r * stride; count % 8 == 0 and stride % 8 == 0.
@@ -60,5 +65,23 @@ hipError_t column_sum(const void* in, float* out, int64_t rows, int64_t cols, El
 // a column sum whose row-block partials another kernel wrote.
 hipError_t column_finish(const float* part, float* out, int64_t nparts, int64_t cols,
                          hipStream_t stream);
+
+// One column of column_finish (every kernel that runs it adds in this order).
+__device__ __forceinline__ void column_finish_one(const float* __restrict__ part,
+                                                  float* __restrict__ out, int64_t nparts,
+                                                  int64_t cols, int64_t c)
+{
+    float acc = 0.f;
+    int64_t rb = 0;
+    for (; rb + 8 <= nparts; rb += 8) {   // eight loads in flight, adds in order
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = part[(rb + u) * cols + c];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc += v[u];
+    }
+    for (; rb < nparts; ++rb) acc += part[rb * cols + c];
+    out[c] = acc;
+}
 
 }  // namespace tpmlp

@@ -220,18 +220,7 @@ __global__ __launch_bounds__(kThreads) void column_final_kernel(const float* __r
                                                                 int64_t nrb, int64_t cols)
 {
     const int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    if (c >= cols) return;
-    float acc = 0.f;
-    int64_t rb = 0;
-    for (; rb + 8 <= nrb; rb += 8) {   // eight loads in flight, adds in order
-        float v[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = part[(rb + u) * cols + c];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) acc += v[u];
-    }
-    for (; rb < nrb; ++rb) acc += part[rb * cols + c];
-    out[c] = acc;
+    if (c < cols) column_finish_one(part, out, nrb, cols, c);
 }
 
 unsigned stream_grid(int64_t work_items)

@@ -340,19 +340,26 @@ int tp_mlp_shard_bwd(const void* X, const void* W1_i, const void* W2_i, const vo
     if ((err = run_gemm(dZ, W2_i, dY_i, nullptr, Y_i, nullptr, tokens, n, h, e, Layout::NT,
                         Epi::DGelu, e, s, colsum)) != hipSuccess)
         return TP_ERR_HIP;
-    if (colsum) {
+    // With the transposed operands the blocks' partials are added up in the
+    // launch of the first transpose (both read and write disjoint memory,
+    // and the partials are in dW2_i until its product); otherwise by their
+    // own pass here.
+    const bool transposed = use_transposed_operands(tokens, h, n, e);
+    if (colsum && !transposed) {
         if ((err = column_finish(colsum, static_cast<float*>(db1_i), row_blocks, n, s)) !=
             hipSuccess)
             return TP_ERR_HIP;
-    } else if (db1_i && (err = column_sum(dY_i, static_cast<float*>(db1_i), tokens, n, e,
-                                          dW2_i, n * h * 4, s)) != hipSuccess) {
+    } else if (!colsum && db1_i &&
+               (err = column_sum(dY_i, static_cast<float*>(db1_i), tokens, n, e, dW2_i,
+                                 n * h * 4, s)) != hipSuccess) {
         return TP_ERR_HIP;
     }
-    if (use_transposed_operands(tokens, h, n, e)) {
+    if (transposed) {
         // The weight gradients as products with a K-contiguous first operand.
         // dW2_i = (H_i^T) dZ, with H_i^T [n][T] staged in dW1_i's memory
         // (written only afterwards).
-        if ((err = transpose16(H_i, dW1_i, tokens, n, s)) != hipSuccess ||
+        if ((err = transpose16(H_i, dW1_i, tokens, n, s, colsum, static_cast<float*>(db1_i),
+                               colsum ? row_blocks : 0, colsum ? n : 0)) != hipSuccess ||
             (err = run_gemm(dW1_i, dZ, dW2_i, nullptr, nullptr, nullptr, n, h, tokens, e,
                             Layout::NN, Epi::Store, Elt::F32, s)) != hipSuccess)
             return TP_ERR_HIP;

@@ -23,11 +23,21 @@ __device__ __forceinline__ uint32_t hi_pair(uint32_t a, uint32_t b)
     return (a >> 16) | (b & 0xffff0000u);   // high halves of a and b
 }
 
+// Blocks from tblocks on do the column-finish job (one column per thread).
 __global__ __launch_bounds__(kThreads) void transpose16_kernel(const uint16_t* __restrict__ in,
                                                                uint16_t* __restrict__ out,
                                                                int64_t rows, int64_t cols,
-                                                               int64_t tiles_c, int64_t ntiles)
+                                                               int64_t tiles_c, int64_t ntiles,
+                                                               int64_t tblocks,
+                                                               const float* __restrict__ col_part,
+                                                               float* __restrict__ col_out,
+                                                               int64_t col_parts, int64_t col_count)
 {
+    if ((int64_t)blockIdx.x >= tblocks) {
+        const int64_t c = ((int64_t)blockIdx.x - tblocks) * kThreads + threadIdx.x;
+        if (c < col_count) column_finish_one(col_part, col_out, col_parts, col_count, c);
+        return;
+    }
     const int lane = threadIdx.x & 63;
     const int64_t tile = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
     if (tile >= ntiles) return;
@@ -72,16 +82,20 @@ __global__ __launch_bounds__(kThreads) void transpose16_kernel(const uint16_t* _
 
 }  // namespace
 
-hipError_t transpose16(const void* in, void* out, int64_t rows, int64_t cols, hipStream_t stream)
+hipError_t transpose16(const void* in, void* out, int64_t rows, int64_t cols, hipStream_t stream,
+                       const float* col_part, float* col_out, int64_t col_parts,
+                       int64_t col_count)
 {
-    if (rows == 0 || cols == 0) return hipSuccess;
+    if (!col_part) col_count = 0;
     const int64_t tiles_r = (rows + kTile - 1) / kTile, tiles_c = (cols + kTile - 1) / kTile;
-    const int64_t ntiles = tiles_r * tiles_c;
-    const int64_t blocks = (ntiles + kWavesPerBlock - 1) / kWavesPerBlock;
+    const int64_t ntiles = rows > 0 && cols > 0 ? tiles_r * tiles_c : 0;
+    const int64_t tblocks = (ntiles + kWavesPerBlock - 1) / kWavesPerBlock;
+    const int64_t blocks = tblocks + (col_count + kThreads - 1) / kThreads;
+    if (blocks == 0) return hipSuccess;
     if (blocks > INT32_MAX) return hipErrorInvalidValue;
     hipLaunchKernelGGL(transpose16_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream,
                        static_cast<const uint16_t*>(in), static_cast<uint16_t*>(out), rows, cols,
-                       tiles_c, ntiles);
+                       tiles_c, ntiles, tblocks, col_part, col_out, col_parts, col_count);
     return hipGetLastError();
 }
 
