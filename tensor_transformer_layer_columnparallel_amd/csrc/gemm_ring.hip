@@ -461,50 +461,140 @@ __device__ __forceinline__ void store_tile(
     for (int b = 0; b < kFragN; ++b)
 #pragma unroll
         for (int e = 0; e < 4; ++e) cs[b][e] = 0.f;
+    if constexpr (sizeof(OutT) == 2) {
+        // bf16 results leave in 16-byte pieces: for each pair of neighbouring
+        // 16-column fragments b, b + 1, v_permlane16_swap exchanges fragment
+        // b's values of lane rows 1 and 3 with fragment b + 1's of rows 0 and
+        // 2, so that lane row g then holds eight consecutive columns
+        // (fragment b + (g & 1), columns 8 (g >> 1) ..) and each store covers
+        // 64 contiguous bytes of 16 rows instead of 32.  Every lane takes part
+        // in the exchange; loads and stores outside the matrix are skipped.
+        const int g = lane >> 4;
+        float bv[kFragN][4];
 #pragma unroll
-    for (int b = 0; b < kFragN; ++b) {
-        const int64_t col = n0 + wrow_b + b * 16 + 4 * (lane >> 4);
-        if (col >= p.N) continue;
-        float bv[4] = {0.f, 0.f, 0.f, 0.f};
-        if constexpr (EPI == Epi::Bias || EPI == Epi::BiasGelu) {
-            if (bias) {
-                const bf16x4 t4 = *reinterpret_cast<const bf16x4*>(bias + col);
+        for (int b = 0; b < kFragN; ++b) {
+            const int64_t col = n0 + wrow_b + b * 16 + 4 * g;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) bv[e] = (float)t4[e];
+            for (int e = 0; e < 4; ++e) bv[b][e] = 0.f;
+            if constexpr (EPI == Epi::Bias || EPI == Epi::BiasGelu) {
+                if (bias && col < p.N) {
+                    const bf16x4 t4 = *reinterpret_cast<const bf16x4*>(bias + col);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) bv[b][e] = (float)t4[e];
+                }
             }
         }
+        auto pack = [](float x0, float x1) {
+            return (uint32_t)__builtin_bit_cast(uint16_t, (bf16)x0) |
+                   ((uint32_t)__builtin_bit_cast(uint16_t, (bf16)x1) << 16);
+        };
+        // Stores one row of 16 x 16 fragments (w: packed pairs per fragment).
+        auto store_row = [&](bf16* dst, uint32_t (&w)[kFragN][2], int64_t row) {
+            const bool rowok = row < p.M;
+#pragma unroll
+            for (int b = 0; b + 1 < kFragN; b += 2) {
+#pragma unroll
+                for (int h2 = 0; h2 < 2; ++h2) {
+                    const auto r = __builtin_amdgcn_permlane16_swap(w[b][h2], w[b + 1][h2], false,
+                                                                    false);
+                    w[b][h2] = r[0];
+                    w[b + 1][h2] = r[1];
+                }
+                const int64_t col = n0 + wrow_b + (b + (g & 1)) * 16 + 8 * (g >> 1);
+                if (rowok && col < p.N)   // N % 8 == 0: eight columns all in or all out
+                    *reinterpret_cast<uint4*>(dst + row * p.N + col) =
+                        uint4{w[b][0], w[b][1], w[b + 1][0], w[b + 1][1]};
+            }
+            if constexpr (kFragN % 2 == 1) {
+                constexpr int b = kFragN - 1;
+                const int64_t col = n0 + wrow_b + b * 16 + 4 * g;
+                if (rowok && col < p.N)
+                    *reinterpret_cast<uint2*>(dst + row * p.N + col) = uint2{w[b][0], w[b][1]};
+            }
+        };
 #pragma unroll
         for (int a = 0; a < kFragM; ++a) {
             const int64_t row = m0 + wrow_a + a * 16 + (lane & 15);
-            if (row >= p.M) continue;
-            const int64_t off = row * p.N + col;
-            float v[4];
+            uint32_t hw[kFragN][2], yw[kFragN][2];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = acc[a][b][e];
-            if constexpr (EPI == Epi::Bias) {
+            for (int b = 0; b < kFragN; ++b) {
+                const int64_t col = n0 + wrow_b + b * 16 + 4 * g;
+                const bool ok = row < p.M && col < p.N;
+                float v[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] += bv[e];
-            } else if constexpr (EPI == Epi::BiasGelu) {
+                for (int e = 0; e < 4; ++e) v[e] = acc[a][b][e];
+                if constexpr (EPI == Epi::Bias) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] += bv[e];
-                if (save)
-                    *reinterpret_cast<bf16x4*>(save + off) =
-                        bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+                    for (int e = 0; e < 4; ++e) v[e] += bv[b][e];
+                } else if constexpr (EPI == Epi::BiasGelu) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = gelu_tanh(v[e]);
-            } else if constexpr (EPI == Epi::DGelu) {
-                const bf16x4 y4 = *reinterpret_cast<const bf16x4*>(aux + off);
+                    for (int e = 0; e < 4; ++e) v[e] += bv[b][e];
+                    yw[b][0] = pack(v[0], v[1]);
+                    yw[b][1] = pack(v[2], v[3]);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    v[e] *= gelu_tanh_grad((float)y4[e]);
-                    cs[b][e] += v[e];
+                    for (int e = 0; e < 4; ++e) v[e] = gelu_tanh(v[e]);
+                } else if constexpr (EPI == Epi::DGelu) {
+                    bf16x4 y4{};
+                    if (ok) y4 = *reinterpret_cast<const bf16x4*>(aux + row * p.N + col);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        // the column sums add the products as computed, never
+                        // fused with them into one multiply-add
+#pragma clang fp contract(off)
+                        v[e] *= gelu_tanh_grad((float)y4[e]);
+                        if (ok) cs[b][e] += v[e];
+                    }
+                }
+                hw[b][0] = pack(v[0], v[1]);
+                hw[b][1] = pack(v[2], v[3]);
+            }
+            if constexpr (EPI == Epi::BiasGelu) {
+                if (save) store_row(save, yw, row);
+            }
+            store_row(C, hw, row);
+        }
+    } else {   // fp32 results from registers (bias + GeLU, GeLU')
+#pragma unroll
+        for (int b = 0; b < kFragN; ++b) {
+            const int64_t col = n0 + wrow_b + b * 16 + 4 * (lane >> 4);
+            if (col >= p.N) continue;
+            float bv[4] = {0.f, 0.f, 0.f, 0.f};
+            if constexpr (EPI == Epi::Bias || EPI == Epi::BiasGelu) {
+                if (bias) {
+                    const bf16x4 t4 = *reinterpret_cast<const bf16x4*>(bias + col);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) bv[e] = (float)t4[e];
                 }
             }
-            if constexpr (sizeof(OutT) == 4) {
+#pragma unroll
+            for (int a = 0; a < kFragM; ++a) {
+                const int64_t row = m0 + wrow_a + a * 16 + (lane & 15);
+                if (row >= p.M) continue;
+                const int64_t off = row * p.N + col;
+                float v[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = acc[a][b][e];
+                if constexpr (EPI == Epi::Bias) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] += bv[e];
+                } else if constexpr (EPI == Epi::BiasGelu) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] += bv[e];
+                    if (save)
+                        *reinterpret_cast<bf16x4*>(save + off) =
+                            bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] = gelu_tanh(v[e]);
+                } else if constexpr (EPI == Epi::DGelu) {
+                    const bf16x4 y4 = *reinterpret_cast<const bf16x4*>(aux + off);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+#pragma clang fp contract(off)
+                        v[e] *= gelu_tanh_grad((float)y4[e]);
+                        cs[b][e] += v[e];
+                    }
+                }
                 *reinterpret_cast<f32x4*>(C + off) = f32x4{v[0], v[1], v[2], v[3]};
-            } else {
-                *reinterpret_cast<bf16x4*>(C + off) =
-                    bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
             }
         }
     }
