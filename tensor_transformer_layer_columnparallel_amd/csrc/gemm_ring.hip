@@ -115,8 +115,8 @@ using TileSmall = TileCfg<128, 96, 4, 2, 2>;
 // at most one 128 x 96 tile per CU: a lone four-wave workgroup spends about
 // 500 cycles per 32-k slab on 192 cycles of MFMAs, its waits and barriers
 // exposed with one wave per SIMD, and the second pipeline fills them while
-// halving the slabs each one walks.  The halves' sums are added in a fixed
-// order (first half + second half).
+// halving the slabs each one walks.  Each output is the first half's sum plus
+// the second's; each pipeline finishes half of the tile's rows.
 using TileSplit = TileCfg<128, 96, 4, 2, 1, 2>;
 
 // Raw buffer descriptor (gfx9 family): base, stride 0, byte extent, word 3.
@@ -346,7 +346,8 @@ __device__ __forceinline__ bf16x8 read_frag_mn(const bf16* buf, int row0, int la
 template <class Cfg, Epi EPI, typename OutT>
 __device__ __forceinline__ void store_tile(
     const GemmArgs& p, f32x4 (&acc)[Cfg::BM / Cfg::WM / 16][Cfg::BN / (Cfg::NW / Cfg::WM) / 16],
-    bf16* smem, int64_t m0, int64_t n0, int tm, int wm, int wrow_a, int wrow_b, int lane)
+    bf16* smem, int64_t m0, int64_t n0, int tm, int wm, int wrow_a, int wrow_b, int lane,
+    int a_lo = 0, int a_hi = Cfg::BM / Cfg::WM / 16)
 {
     constexpr int NW = Cfg::NW, WM = Cfg::WM, BN = Cfg::BN, kBM = Cfg::BM;
     constexpr int kABytes = Cfg::ABytes, kBBytes = Cfg::BBytes;
@@ -514,6 +515,7 @@ __device__ __forceinline__ void store_tile(
         };
 #pragma unroll
         for (int a = 0; a < kFragM; ++a) {
+            if (a < a_lo || a >= a_hi) continue;   // uniform per wave
             const int64_t row = m0 + wrow_a + a * 16 + (lane & 15);
             uint32_t hw[kFragN][2], yw[kFragN][2];
 #pragma unroll
@@ -692,12 +694,12 @@ __global__ __launch_bounds__(64 * Cfg::NW * Cfg::KS, Cfg::OCC) void gemm_ring_ke
     constexpr int kDmaEven = A_KMAJ ? PlanAU::kPerUnit : PlanAP::kPer;
     constexpr int kDmaOdd = B_KMAJ ? PlanBU::kPerUnit : PlanBP::kPer;
     constexpr int KS = Cfg::KS;
-    // A workgroup of two pipelines ends with the second handing its sums to
-    // the first and leaving; only the register-path epilogues (no barrier,
-    // no workgroup-wide loops) follow that.
-    static_assert(KS == 1 || (EPI != Epi::DGelu && EPI != Epi::StoreT &&
-                              !(sizeof(OutT) == 4 && (EPI == Epi::Store || EPI == Epi::Bias))),
-                  "split-K workgroups take the register-path epilogues");
+    // A workgroup of two pipelines ends with them exchanging halves of their
+    // sums; only the bf16 register-path epilogue (no barrier, no
+    // workgroup-wide loops) follows, each pipeline writing its half.
+    static_assert(KS == 1 || ((EPI == Epi::Store || EPI == Epi::Bias || EPI == Epi::BiasGelu) &&
+                              sizeof(OutT) == 2),
+                  "split-K workgroups take the bf16 register-path epilogues");
     __shared__ __attribute__((aligned(1024))) bf16 smem[KS * (kABytes + kBBytes) / 2];
 
     const int lane = threadIdx.x & 63;
@@ -855,30 +857,50 @@ __global__ __launch_bounds__(64 * Cfg::NW * Cfg::KS, Cfg::OCC) void gemm_ring_ke
     wait_vmcnt<0>();
     wait_lgkmcnt0();
     if constexpr (KS == 2) {
-        // The second pipeline's sums go through LDS (48 KiB, in the rings
-        // that nobody reads any more) to the wave of the first pipeline that
-        // holds the same outputs, which adds them to its own.
+        // The two pipelines' sums of the same outputs meet through LDS
+        // (48 KiB, in the rings that nobody reads any more): pipeline h keeps
+        // the fragment rows a in [h kFragM / 2, (h + 1) kFragM / 2), sends the
+        // others to the wave of the other pipeline that holds the same
+        // outputs, adds what it receives (fp32 addition is commutative, so
+        // both halves get first half + second half) and writes its rows.
+        static_assert(kFragM % 2 == 0, "fragment rows split between the pipelines");
         static_assert(NW * kFragM * kFragN * 64 * 16 <= kABytes + kBBytes, "hand-over space");
+        constexpr int kHalf = kFragM / 2;
         f32x4* const red = reinterpret_cast<f32x4*>(smem);
-        barrier();   // both pipelines are done with their rings
-        if (half == 1) {
+        // fragment rows [kKeep, kKeep + kHalf) stay, the others go (constant
+        // offsets: the accumulators stay in registers)
+        auto send = [&](auto keep) {
+            constexpr int kSend = kHalf - decltype(keep)::value;
 #pragma unroll
-            for (int a = 0; a < kFragM; ++a)
+            for (int a = 0; a < kHalf; ++a)
 #pragma unroll
                 for (int b = 0; b < kFragN; ++b)
-                    red[((wave * kFragM + a) * kFragN + b) * 64 + lane] = acc[a][b];
-        }
+                    red[((wave * kFragM + kSend + a) * kFragN + b) * 64 + lane] = acc[kSend + a][b];
+        };
+        auto receive = [&](auto keep) {
+            constexpr int kKeep = decltype(keep)::value;
+#pragma unroll
+            for (int a = 0; a < kHalf; ++a)
+#pragma unroll
+                for (int b = 0; b < kFragN; ++b) {
+                    const f32x4 r = red[((wave * kFragM + kKeep + a) * kFragN + b) * 64 + lane];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[kKeep + a][b][e] = acc[kKeep + a][b][e] + r[e];
+                }
+        };
+        using Lo = std::integral_constant<int, 0>;
+        using Hi = std::integral_constant<int, kHalf>;
+        const int a_lo = half * kHalf;
+        barrier();   // both pipelines are done with their rings
+        if (half == 0) send(Lo{});
+        else send(Hi{});
         wait_lgkmcnt0();   // s_barrier itself does not wait for LDS stores
         barrier();
-        if (half == 1) return;   // no barrier follows in the register-path epilogues
-#pragma unroll
-        for (int a = 0; a < kFragM; ++a)
-#pragma unroll
-            for (int b = 0; b < kFragN; ++b) {
-                const f32x4 r = red[((wave * kFragM + a) * kFragN + b) * 64 + lane];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) acc[a][b][e] = acc[a][b][e] + r[e];
-            }
+        if (half == 0) receive(Lo{});
+        else receive(Hi{});
+        store_tile<Cfg, EPI, OutT>(p, acc, smem, m0, n0, tm, wm, wrow_a, wrow_b, lane, a_lo,
+                                   a_lo + kHalf);
+        return;
     }
     store_tile<Cfg, EPI, OutT>(p, acc, smem, m0, n0, tm, wm, wrow_a, wrow_b, lane);
 }
@@ -911,7 +933,7 @@ hipError_t launch_cfg(const GemmArgs& p, hipStream_t stream)
 // run on 128 x 96 tiles instead:
 //  - on two K-split pipelines per workgroup when one product has no more
 //    128 x 96 tiles than CUs, K has at least four 64-k units and the results
-//    leave from registers.  This depends on the product alone, not on the
+//    are bf16 (stored from registers).  This depends on the product alone, not on the
 //    batch: the split adds each output's k range in another order, and a
 //    batch must give the same bits as its products launched one by one;
 //  - otherwise on two workgroups of four waves per CU when the launch would
@@ -921,7 +943,7 @@ template <bool AK, bool BK, Epi E, typename O>
 hipError_t launch(const GemmArgs& p, hipStream_t stream)
 {
     if constexpr (AK && (E == Epi::Store || E == Epi::Bias || E == Epi::BiasGelu)) {
-        if constexpr (sizeof(O) == 2 || E == Epi::BiasGelu) {
+        if constexpr (sizeof(O) == 2) {
             const int64_t small = ((p.M + TileSmall::BM - 1) / TileSmall::BM) *
                                   ((p.N + TileSmall::BN - 1) / TileSmall::BN);
             if (small <= kCUs && p.K >= 256) return launch_cfg<TileSplit, AK, BK, E, O>(p, stream);
