@@ -518,6 +518,35 @@ __device__ __forceinline__ void store_tile(
             if (a < a_lo || a >= a_hi) continue;   // uniform per wave
             const int64_t row = m0 + wrow_a + a * 16 + (lane & 15);
             uint32_t hw[kFragN][2], yw[kFragN][2];
+            // GeLU': the saved pre-activation comes in the same 16-byte
+            // pieces and goes back to the fragments' layout through the same
+            // exchange (it is its own inverse)
+            uint32_t aw[kFragN][2];
+            if constexpr (EPI == Epi::DGelu) {
+                const bool rowok = row < p.M;
+#pragma unroll
+                for (int b = 0; b + 1 < kFragN; b += 2) {
+                    const int64_t col = n0 + wrow_b + (b + (g & 1)) * 16 + 8 * (g >> 1);
+                    uint4 q{0u, 0u, 0u, 0u};
+                    if (rowok && col < p.N)
+                        q = *reinterpret_cast<const uint4*>(aux + row * p.N + col);
+                    const auto r0 = __builtin_amdgcn_permlane16_swap(q.x, q.z, false, false);
+                    const auto r1 = __builtin_amdgcn_permlane16_swap(q.y, q.w, false, false);
+                    aw[b][0] = r0[0];
+                    aw[b + 1][0] = r0[1];
+                    aw[b][1] = r1[0];
+                    aw[b + 1][1] = r1[1];
+                }
+                if constexpr (kFragN % 2 == 1) {
+                    constexpr int b = kFragN - 1;
+                    const int64_t col = n0 + wrow_b + b * 16 + 4 * g;
+                    uint2 q{0u, 0u};
+                    if (rowok && col < p.N)
+                        q = *reinterpret_cast<const uint2*>(aux + row * p.N + col);
+                    aw[b][0] = q.x;
+                    aw[b][1] = q.y;
+                }
+            }
 #pragma unroll
             for (int b = 0; b < kFragN; ++b) {
                 const int64_t col = n0 + wrow_b + b * 16 + 4 * g;
@@ -536,8 +565,7 @@ __device__ __forceinline__ void store_tile(
 #pragma unroll
                     for (int e = 0; e < 4; ++e) v[e] = gelu_tanh(v[e]);
                 } else if constexpr (EPI == Epi::DGelu) {
-                    bf16x4 y4{};
-                    if (ok) y4 = *reinterpret_cast<const bf16x4*>(aux + row * p.N + col);
+                    const bf16x4 y4 = __builtin_bit_cast(bf16x4, uint2{aw[b][0], aw[b][1]});
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         // the column sums add the products as computed, never
