@@ -220,6 +220,37 @@ def test_small_tile_register_epilogues(B, T, k, n):
     _whole(Zb, oracle.row_linear(X, W), "bf16", "small tiles: plain bf16")
 
 
+@pytest.mark.parametrize("n", [200, 208, 216, 224, 232, 240],
+                         ids=lambda n: f"n{n}-tail{n % 48}")
+def test_bf16_epilogue_every_column_tail(B, n):
+    # The bf16 epilogues pair neighbouring 16-column fragments through a lane
+    # exchange and store (load, for the saved pre-activation) eight columns
+    # per lane.  A wave covers 48 columns, so N can end 8, 16, 24, 32, 40 or
+    # 48 columns into a wave's range: n % 48 runs through all six.  Each n on
+    # the K-split workgroups (300 rows), the four-wave 128 x 96 instance
+    # (12000 rows) and the 256 x 192 tiles (16400 rows): bias + GeLU with the
+    # pre-activation saved; and the shard forward + backward at 300 tokens,
+    # whose GeLU' product (dY with the bias gradient) reads the saved
+    # pre-activation that way; element-wise vs the oracle.
+    bf = torch.bfloat16
+    k = 256
+    g = torch.Generator().manual_seed(79)
+    W = (0.02 * torch.randn(k, n, generator=g)).to(bf)
+    b = (0.02 * torch.randn(n, generator=g)).to(bf)
+    Wd, bd = dev(W), dev(b)
+    for T in (300, 12000, 16400):
+        _log(f"case bf16 epilogue tail n={n} T={T}")
+        X = torch.randn(T, k, generator=g).to(bf)
+        H = torch.empty(T, n, dtype=bf, device="cuda")
+        Y = torch.empty(T, n, dtype=bf, device="cuda")
+        B.tp_column_linear(dev(X), Wd, bd, H, Y, T, k, n, 1, 0, bf, bf, B.TP_ACT_GELU_TANH)
+        torch.cuda.synchronize()
+        assert_close(Y, oracle.column_linear(X, W, b), "bf16", f"tail n={n} T={T} Y")
+        assert_close(H, oracle.column_linear(X, W, b, gelu=True), "bf16", f"tail n={n} T={T} H")
+    w = configs.Workload(f"tail{n}", T=300, h=k, ffn=n, t=1, dtype="bf16", ranks=(0,), bias=True)
+    _full_check(B, w, seed=83)
+
+
 def test_row_linear_ragged_partials_sum(B):
     # row-parallel partials of t = 4 ranks, summed on the device
     T, n_full, hout, t = 77, 512, 136, 4
