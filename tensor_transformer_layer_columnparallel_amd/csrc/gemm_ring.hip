@@ -408,8 +408,8 @@ __device__ __forceinline__ void store_tile(
         // gradients) go through LDS (the ring is free now) so that the stores
         // to HBM are whole 16-byte chunks of consecutive columns, one row
         // segment per group of lanes, instead of 16 rows x 64 bytes per store
-        // instruction: 3-4% faster on those products.  (For the bf16 outputs
-        // the extra LDS passes cost more than they saved.)
+        // instruction: 3-4% faster on those products.  (The bf16 outputs,
+        // stored in 64-byte pieces of 16 rows, gain nothing from staging.)
         constexpr int kRowBytes = BN * 4;
         constexpr int kPitch = kRowBytes + 16;   // rows 16 bytes apart in bank space
         constexpr int kRows = kBM * kPitch <= kABytes + kBBytes ? kBM : kBM / 2;
