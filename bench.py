@@ -61,8 +61,12 @@ def stored_traffic():
 
 # The column GEMM is the only bf16-output GEMM with the bias + GeLU epilogue
 # (mangled and demangled spellings; every part of a key must match).
-COLUMN_KERNEL_KEYS = (("gemm_ring_kernel", "ELNS_3EpiE2EDF16b"),
-                      ("gemm_ring_kernel<", "(tpmlp::Epi)2, __bf16>"))
+# the 256 x 192-tile instance with the bias + GeLU epilogue and bf16 results,
+# as rocprofv3 names it (mangled, or demangled)
+COLUMN_KERNEL_KEYS = (("gemm_ring_kernel",
+                       "TileCfgILi256ELi192ELi8ELi2ELi1ELi1EEELb1ELb0ELNS_3EpiE2EDF16b"),
+                      ("gemm_ring_kernel<", "TileCfg<256, 192, 8, 2, 1, 1>, true, false, "
+                                            "(tpmlp::Epi)2, __bf16>"))
 COPY_KERNEL_KEYS = (("shard_concat_kernel",),)
 
 
