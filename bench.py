@@ -19,6 +19,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -35,15 +36,24 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+def code_text(src: str) -> str:
+    """C++ source without its comments and with runs of blank space folded to
+    one space: what a compiler sees of it (the sources hold no string
+    literal with a comment marker in it)."""
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    return " ".join(src.split())
+
+
 def kernel_source_digest() -> str:
-    """Digest of the GEMM kernel sources; stored HBM counters are used only
-    while it matches."""
+    """Digest of the GEMM kernel sources' code (comments and layout left
+    out); stored HBM counters are used only while it matches."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "tensor_transformer_layer_columnparallel_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
         if name.startswith("gemm") or name in ("common.h", "epilogue.h"):
-            with open(os.path.join(csrc, name), "rb") as f:
-                h.update(name.encode() + f.read())
+            with open(os.path.join(csrc, name)) as f:
+                h.update((name + "\n" + code_text(f.read())).encode())
     return h.hexdigest()[:16]
 
 
@@ -59,10 +69,9 @@ def stored_traffic():
     return None if b is None else int(round(b))
 
 
-# The column GEMM is the only bf16-output GEMM with the bias + GeLU epilogue
-# (mangled and demangled spellings; every part of a key must match).
-# the 256 x 192-tile instance with the bias + GeLU epilogue and bf16 results,
-# as rocprofv3 names it (mangled, or demangled)
+# The column GEMM: the 256 x 192-tile instance with the bias + GeLU epilogue
+# and bf16 results, as rocprofv3 names it (mangled, or demangled; every part
+# of a key must match).
 COLUMN_KERNEL_KEYS = (("gemm_ring_kernel",
                        "TileCfgILi256ELi192ELi8ELi2ELi1ELi1EEELb1ELb0ELNS_3EpiE2EDF16b"),
                       ("gemm_ring_kernel<", "TileCfg<256, 192, 8, 2, 1, 1>, true, false, "

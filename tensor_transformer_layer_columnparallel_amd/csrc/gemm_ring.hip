@@ -39,10 +39,12 @@
 // Plain fp32 results are staged through the (then free) LDS ring so that the
 // stores to HBM cover whole row segments (transposed on the way, for a
 // result stored as C^T), written with non-temporal stores (the backward 2%
-// faster; they measured slower for the stores below); other results are
-// stored from the registers, four consecutive columns per lane.  The GeLU'
-// epilogue can also sum its fp32 results per column in a fixed order (one
-// row of partials per 256-row block), the bias gradient's first step.
+// faster; they measured slower for the stores below).  bf16 results are
+// stored from the registers, eight consecutive columns per lane after a
+// lane exchange between neighbouring fragments; the fp32 results of the
+// GeLU epilogues four per lane.  The GeLU' epilogue can also sum its fp32
+// results per column in a fixed order (one row of partials per 256-row
+// block), the bias gradient's first step.
 //
 // LDS layouts (16-byte chunks permuted per row for conflict-free reads):
 //   K-major 64-k unit [rows][64 k]: chunk c of row r at c ^ swz8(r), read
@@ -90,7 +92,8 @@ constexpr int kCUs = 256;
 // along M, KS pipelines per workgroup, at most OCC workgroups per CU.  Each
 // pipeline has its own rings of kABufs 64-k units of A and kBBufs of B.
 // With KS = 2 the workgroup's two pipelines compute the same tile over the
-// two halves of K, and the second hands its sums to the first at the end.
+// two halves of K and at the end exchange halves of their sums, each
+// finishing half of the tile's rows.
 template <int BM_, int BN_, int NW_, int WM_, int OCC_, int KS_ = 1>
 struct TileCfg {
     static constexpr int BM = BM_, BN = BN_, NW = NW_, WM = WM_, OCC = OCC_, KS = KS_;

@@ -2,6 +2,7 @@
 of rocprofv3 names, the clock table of a counter run, and the timed-step
 window of the kernel-trace summary, on small synthetic CSV files."""
 import csv
+import json
 import os
 import sys
 
@@ -91,3 +92,18 @@ def test_trace_summary_needs_exactly_one_column_kernel(tmp_path):
         w.writerow({"Kernel_Name": "other", "Start_Timestamp": 0, "End_Timestamp": 1})
     with pytest.raises(SystemExit):
         bench.trace_summary(str(tmp_path), 0, 1)
+
+
+def test_code_text_drops_comments_and_layout():
+    src = "int a; // one\n/* two\n three */  int   b;\n"
+    assert bench.code_text(src) == "int a; int b;"
+    # the same code with other comments and line breaks reads the same
+    assert bench.code_text("int a;\n\n// x\nint b; /* y */") == bench.code_text(src)
+    assert bench.code_text("int a; int c;") != bench.code_text(src)
+
+
+def test_stored_counters_match_the_kernel_code():
+    with open(bench.COUNTERS_FILE) as f:
+        stored = json.load(f)
+    assert stored["kernel_source_digest"] == bench.kernel_source_digest()
+    assert bench.stored_traffic() == int(round(stored["hbm_bytes_per_launch"]))
