@@ -315,6 +315,45 @@ def trace_summary(trace_dir: str, warmup: int, steps: int):
     for _, name, c, mean, mn, mx, nt, tmean in rows:
         short = kernel_label(name)
         print(f"| `{short}` | {c} | {mean:.1f} | {mn:.1f} | {mx:.1f} | {nt} | {tmean:.1f} |")
+    print()
+    for line in step_launch_table(runs, col[warmup:warmup + steps]):
+        print(line)
+
+
+# The launches of one bench step in issue order: tp_column_linear, then
+# tp_row_linear, then tp_mlp_shard_bwd (transposed-operand weight gradients).
+STEP_LAUNCHES = ("column GEMM + bias + GeLU, Y saved (a1+a2)", "row GEMM, fp32 partial (a3)",
+                 "dY with GeLU' and db1's row-block partials (a5)",
+                 "H_i transpose, with db1's last pass in extra blocks",
+                 "dW2_i = (H_i^T) dZ (a6)", "dY_i transpose",
+                 "dW1_i^T = (dY_i^T) X, stored transposed (a7)", "dX_i = dY_i W1_i^T (a8)")
+
+
+def step_launch_table(runs, col_starts):
+    """Markdown lines: the mean duration of each launch of the timed steps by
+    its place in the step.  A step runs from the start of one column-GEMM
+    dispatch (`col_starts`, (start, duration) pairs) to the next or, for the
+    last, 3 ms on.  Launches are named after STEP_LAUNCHES when every step
+    has that many."""
+    launches = sorted((t, d, name) for name, v in runs.items() for t, d in v)
+    starts = [t for t, _ in col_starts]
+    ends = starts[1:] + [starts[-1] + 3_000_000]
+    steps = [[(d, name) for t, d, name in launches if a <= t < b] for a, b in zip(starts, ends)]
+    counts = {len(s) for s in steps}
+    if len(counts) != 1:
+        return [f"(steps hold different launch counts: {sorted(counts)})"]
+    n = counts.pop()
+    named = n == len(STEP_LAUNCHES)
+    lines = ["| place in the step | kernel | product | mean us in the timed steps | share of the step |",
+             "|---|---|---|---|---|"]
+    means = [sum(s[i][0] for s in steps) / len(steps) for i in range(n)]
+    total = sum(means)
+    for i in range(n):
+        lines.append(f"| {i + 1} | `{kernel_label(steps[0][i][1])}` | "
+                     f"{STEP_LAUNCHES[i] if named else '-'} | {means[i]:.1f} | "
+                     f"{100 * means[i] / total:.1f}% |")
+    lines.append(f"| | | sum of the kernel durations | {total:.1f} | |")
+    return lines
 
 
 def max_engine_clock_mhz():

@@ -77,12 +77,17 @@ def test_trace_summary_counts_the_timed_steps(tmp_path, capsys):
                         "Start_Timestamp": t0 + 200_000, "End_Timestamp": t0 + 250_000})
     bench.trace_summary(str(tmp_path), 1, 2)
     out = capsys.readouterr().out.splitlines()
+    blank = out.index("")
     rows = {l.split("`")[1]: [c.strip() for c in l.split("`")[2].strip().strip("|").split("|")]
-            for l in out[2:]}
+            for l in out[2:blank]}
     col = rows["gemm_ring_kernel<256x192, true, false, (Epi)2, bf16>"]
     assert col[:2] == ["4", "100.0"] and col[4:] == ["2", "100.0"]
     tr = rows["transpose16_kernel"]
     assert tr[0] == "4" and tr[4] == "2"
+    # then the launches by place in the step: two per step, not the bench step's eight
+    places = out[blank + 3:]
+    assert [p.split("|")[1].strip() for p in places[:2]] == ["1", "2"]
+    assert places[0].split("|")[3].strip() == "-" and places[1].split("|")[4].strip() == "50.0"
 
 
 def test_trace_summary_needs_exactly_one_column_kernel(tmp_path):
@@ -107,3 +112,26 @@ def test_stored_counters_match_the_kernel_code():
         stored = json.load(f)
     assert stored["kernel_source_digest"] == bench.kernel_source_digest()
     assert bench.stored_traffic() == int(round(stored["hbm_bytes_per_launch"]))
+
+
+def test_step_launch_table_names_launches_by_place():
+    col = "gemm_ring_kernel_column"
+    names = [col, "row", "dy", "tr", "dw2", "tr", "dw1", "dx"]
+    runs = {}
+    t = 0
+    for step in range(3):
+        for i, name in enumerate(names):
+            runs.setdefault(name, []).append((t, 10.0 * (i + 1) + step))
+            t += 1000
+    starts = sorted(runs[col])
+    lines = bench.step_launch_table(runs, starts)
+    assert len(lines) == 2 + len(names) + 1
+    # place 5 is dW2 (the second "tr" launch is place 6), means over the 3 steps
+    assert "| 5 | `dw2` | " + bench.STEP_LAUNCHES[4] + " | 51.0 |" in lines[2 + 4]
+    assert lines[-1].endswith("| " + f"{sum(10.0 * (i + 1) + 1 for i in range(8)):.1f}" + " | |")
+
+
+def test_step_launch_table_flags_uneven_steps():
+    runs = {"col": [(0, 5.0), (100, 5.0)], "x": [(50, 1.0)]}
+    lines = bench.step_launch_table(runs, sorted(runs["col"]))
+    assert lines == ["(steps hold different launch counts: [1, 2])"]
