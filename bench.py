@@ -501,11 +501,17 @@ def sequence_parallel(B, stream, sptr, reps=10):
         "reduce_scatter_layernorm": (lambda: B.tp_shard_reduce_scatter_layernorm(
             parts, gam, bet, ln_out[nxt(n_ln)], T, h, t, nxt(t), 1e-5, f32, bf, stream=sptr),
             (t * Tr * h) * 4 + Tr * h * 2 + 2 * h * 2),
+        # context, not the product path: torch's fp32 -> bf16 copy of the same
+        # rows (no reduction), the floor of any one pass over the layer norm's
+        # bytes timed this way
+        "context_cast": (lambda: (lambda i: ln_out[i].copy_(ln_in[i]))(nxt(n_ln)),
+                         Tr * h * 4 + Tr * h * 2),
     }
     out = {"workload": f"t={t}, {T} tokens, h={h}: ReduceScatter of {t} fp32 partials to "
                        f"{Tr} tokens; layer norm of the shard (fp32 -> bf16); token "
                        f"AllGather of {t} bf16 shards; ReduceScatter and layer norm fused "
-                       f"(bf16 out); every repetition on data not in the last-level cache",
+                       f"(bf16 out); every repetition on data not in the last-level cache; "
+                       f"context_cast: torch's fp32 -> bf16 copy of the shard, for scale",
            "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     for name, (f, nbytes) in ops.items():
         warm(f)
@@ -1004,7 +1010,8 @@ def main():
         log("sequence parallel: " + ", ".join(f"{k} {sp[k]['ms']:.4f} ms {sp[k]['achieved']:.0f} GB/s"
                                               for k in ("reduce_scatter", "layernorm",
                                                         "concat_tokens",
-                                                        "reduce_scatter_layernorm")))
+                                                        "reduce_scatter_layernorm",
+                                                        "context_cast")))
 
     if not args.no_full_layer:
         out["full_layer"] = full_layer(B, stream, sptr)
