@@ -661,8 +661,11 @@ def small_configs(B, stream, reps=50):
              f"W_0[{w2.h},{w2.n}], bf16 out, no activation; one tp_column_linear")):
         eager_us, graph_us = timed(f)
         tf = flops / (graph_us * 1e-6) / 1e12
+        tf_eager = flops / (eager_us * 1e-6) / 1e12
         out[name] = {"workload": what, "flops": flops, "eager_us": round(eager_us, 2),
-                     "graph_us": round(graph_us, 2), "tflops_graph": round(tf, 3),
+                     "graph_us": round(graph_us, 2), "tflops_eager": round(tf_eager, 3),
+                     "pct_peak_eager": round(100 * tf_eager / PEAK_BF16_TFLOPS, 2),
+                     "tflops_graph": round(tf, 3),
                      "pct_peak_graph": round(100 * tf / PEAK_BF16_TFLOPS, 2)}
     out["reps"] = reps
     return out
