@@ -1218,6 +1218,35 @@ def test_layernorm_matches_oracle(B, in_dt, out_dt, T, cols):
     assert torch.equal(y.cpu(), y2.cpu())          # fixed reduction order
 
 
+@pytest.mark.parametrize("affine", [True, False])
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("T,cols", [(77, 520), (9, 17008), (5, 33008)])
+def test_layernorm_in_place(B, dt, T, cols, affine):
+    # y == x is allowed for equal types: the registers-held rows and the
+    # three-pass rows (33008 columns) give the out-of-place bits in place;
+    # without gamma and beta (NULL) the scale is 1 and the shift 0
+    _log(f"case layernorm in place {dt} {T}x{cols} affine={affine}")
+    g = torch.Generator().manual_seed(43)
+    t_dt = torch.float32 if dt == "f32" else torch.bfloat16
+    x_h = (2.0 * torch.randn(T, cols, generator=g) - 0.5).to(t_dt)
+    gam_h = (1.0 + 0.1 * torch.randn(cols, generator=g)).to(t_dt) if affine else None
+    bet_h = (0.1 * torch.randn(cols, generator=g)).to(t_dt) if affine else None
+    gam = dev(gam_h) if affine else None
+    bet = dev(bet_h) if affine else None
+    y = torch.empty(T, cols, dtype=t_dt, device="cuda")
+    B.tp_layernorm(dev(x_h), gam, bet, y, T, cols, 1e-5, t_dt, t_dt)
+    x = dev(x_h)
+    B.tp_layernorm(x, gam, bet, x, T, cols, 1e-5, t_dt, t_dt)
+    torch.cuda.synchronize()
+    assert torch.equal(x.cpu(), y.cpu())
+    ref = oracle.layernorm(x_h, gam_h, bet_h, 1e-5)
+    if dt == "f32":
+        rf = np.linalg.norm(to_np64(x) - ref) / np.linalg.norm(ref)
+        assert rf <= 1e-5, rf
+    else:
+        assert_close(x, ref, "bf16", "layernorm in place")
+
+
 @pytest.mark.parametrize("in_dt,out_dt", [("f32", "bf16"), ("f32", "f32"), ("bf16", "bf16")])
 @pytest.mark.parametrize("T,cols,t", [(24, 136, 8), (18, 12296, 3), (4, 33008, 2), (64, 520, 1)])
 def test_reduce_scatter_layernorm_fused(B, in_dt, out_dt, T, cols, t):
