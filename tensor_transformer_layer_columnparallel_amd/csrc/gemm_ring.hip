@@ -855,7 +855,11 @@ __global__ __launch_bounds__(64 * Cfg::NW * Cfg::KS, Cfg::OCC) void gemm_ring_ke
             }
 #pragma unroll
             for (int d = g; d < kSteps; d += kGroups) dma_op(d, kt);
-            __builtin_amdgcn_sched_barrier(0);
+            // A scheduling barrier closes each group, except in the NN
+            // products: there the compiler's own placement of the transposing
+            // B reads across groups is 2-3% faster (column and row products;
+            // for the NT products it measured 0.6% slower).
+            if constexpr (!(A_KMAJ && !B_KMAJ)) __builtin_amdgcn_sched_barrier(0);
         }
     };
     using Even = std::integral_constant<bool, false>;
