@@ -30,6 +30,19 @@ PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published
 METRIC = "TFLOP/s per TP-shard MLP fwd+bwd (bf16) and % of MI355X MFMA peak"
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_counters_column_gemm_gpt3.json")
+# How the stored HBM counters are taken (recorded with them unless given
+# otherwise): two passes over a short bench run, two over a plain copy.
+COUNTER_COMMANDS = (
+    "B='python3 bench.py --steps 2 --warmup 1 --warmup-ms 0 --cpu-seconds 0 --no-reduce "
+    "--no-vendor --no-attention --no-sp --no-full-layer --no-small'; "
+    "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o c -- $B; "
+    "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o c -- $B; "
+    "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_cfetch -o c -- "
+    "python3 bench.py --copy-calibration 3; "
+    "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_cwrite -o c -- "
+    "python3 bench.py --copy-calibration 3; "
+    "python3 bench.py --ingest-counters gpurun_out/pmc_fetch gpurun_out/pmc_write "
+    "gpurun_out/pmc_cfetch gpurun_out/pmc_cwrite")
 
 
 def log(msg):
@@ -848,7 +861,8 @@ def main():
     ap.add_argument("--ingest-counters", nargs=4,
                     metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                     help="turn rocprofv3 --pmc CSV output into the stored traffic figure")
-    ap.add_argument("--counter-commands", default="", help="commands recorded with the counters")
+    ap.add_argument("--counter-commands", default=COUNTER_COMMANDS,
+                    help="commands recorded with the counters (default: the standard recipe)")
     ap.add_argument("--trace-summary", nargs=3, metavar=("TRACE_DIR", "WARMUP", "STEPS"),
                     help="per-kernel durations from a rocprofv3 --kernel-trace CSV of a bench "
                          "run with these warm-up and timed step counts: over all dispatches "

@@ -135,3 +135,10 @@ def test_step_launch_table_flags_uneven_steps():
     runs = {"col": [(0, 5.0), (100, 5.0)], "x": [(50, 1.0)]}
     lines = bench.step_launch_table(runs, sorted(runs["col"]))
     assert lines == ["(steps hold different launch counts: [1, 2])"]
+
+
+def test_stored_counters_record_their_commands():
+    with open(bench.COUNTERS_FILE) as f:
+        stored = json.load(f)
+    assert "FETCH_SIZE" in stored["commands"] and "WRITE_SIZE" in stored["commands"]
+    assert "--ingest-counters" in stored["commands"]
