@@ -1018,6 +1018,9 @@ LAYER_FWD = [  # (tokens, h, ffn, t, dtype, bias, save)
     # 40 small tiles per shard (K-split pipelines), 320 for the batch
     (1000, 256, 8 * 480, 8, "bf16", True, True),
     (0, 256, 8 * 192, 8, "bf16", True, True),      # no tokens: nothing to do
+    # three shards of 66 large tiles each (198 in the batch, not a multiple of the
+    # 8 XCDs: no remap), ragged M and N; each shard alone runs on 128 x 96 tiles
+    (1500, 256, 3 * 2104, 3, "bf16", True, True),
 ]
 
 
