@@ -178,8 +178,9 @@ TP_API int tp_mlp_layer_fwd(const void* X, const void* W1, const void* b1, const
  * tokens == 0 is valid: the weight gradients are then written as zeros.
  * db1_i is summed in fp32 in a fixed order (run-to-run deterministic); its
  * summands are the dY product's fp32 results before rounding to `dtype` when
- * that product runs on the tile kernel (bf16, tokens >= 256, n >= 192,
- * h % 32 == 0), else the stored dY_i.
+ * that product runs on the tile kernel and its per-256-row partials fit in
+ * dW2_i (bf16, 256 <= tokens <= 256 h, n >= 192, h % 32 == 0), else the
+ * stored dY_i.
  * dW2_i, dW1_i and dX_i also serve as scratch space during the call (partial
  * sums of db1_i; transposed copies of H_i and of dY_i or X) before they
  * receive their results, so no output may overlap an input.

@@ -485,6 +485,9 @@ REDUCED = [
     (288, 544, 2304, 8),     # K = 544 and K = T = 288: an odd number of 32-deep slabs
                              # in the tile kernel (half of the last 64-deep unit past K),
                              # in the forward and in the transposed weight gradients
+    (8448, 32, 192, 1),      # more than 256 h tokens: the dY product's 33 row-block
+                             # partials would not fit in dW2's 32 rows, so db1 sums the
+                             # stored dY instead
 ]
 
 
