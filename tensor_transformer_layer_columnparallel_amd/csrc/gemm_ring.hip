@@ -68,7 +68,7 @@ constexpr int kBK = 32;
 constexpr int kBN = 192;
 constexpr int kABufs = 3;                   // A's ring: 64-k units or 32-k slab pairs
 constexpr int kBBufs = 2;                   // B's ring (a power of two)
-constexpr int kLead = 5;                    // DMA steps issued before the first slab
+constexpr int kLead = 4;                    // DMA steps issued before the first slab
 // Interleave groups per slab, and how many of them carry fragment reads.
 // Only the first three of four groups carry reads, so the last group's
 // MFMAs cover the latency of the last reads before the next barrier (2-3%
@@ -784,8 +784,9 @@ __global__ __launch_bounds__(64 * Cfg::NW * Cfg::KS, Cfg::OCC) void gemm_ring_ke
     // slab (vs - 1) was read during step vs - 2.  Odd vs: B's unit or pair
     // (vs + 3) / 2, into the buffer of (vs - 1) / 2, whose last slab (vs)
     // was read during step vs - 1.  Each lands two or three slabs before its
-    // first slab is read; B's unit or pair -1, at the first prologue step,
-    // reads nothing and keeps the prologue in the same pattern.
+    // first slab is read.  The prologue issues steps -4 .. -1 (A's units or
+    // pairs 0 and 1, B's 0 and 1); the waits only ever count the most recent
+    // steps, so they are those of the main loop.
     auto dma_op = [&](int d, int vs) {
         if ((vs & 1) == 0) {
             if constexpr (A_KMAJ) pau.issue_q(d, wave, da, a_base, (vs + 4) >> 1);
@@ -867,7 +868,7 @@ __global__ __launch_bounds__(64 * Cfg::NW * Cfg::KS, Cfg::OCC) void gemm_ring_ke
 
     const int nk = (int)((kspan + kBK - 1) / kBK);
     if (nk > 0) {
-        static_assert(kLead == 5, "prologue parity pattern");
+        static_assert(kLead == 4, "the prologue starts at an even (A) step");
 #pragma unroll
         for (int vs = -kLead; vs < 0; ++vs) {
             constexpr int kDmaMax = kDmaOdd > kDmaEven ? kDmaOdd : kDmaEven;

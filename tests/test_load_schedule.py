@@ -25,7 +25,7 @@ slab s are read during step s - 1 (slab 0 after the prologue).
 """
 import pytest
 
-LEAD = 5          # prologue steps
+LEAD = 4          # prologue steps (-4 .. -1)
 A_UNITS = 3       # ring of 64-deep A units (NN, NT)
 A_SLABS = 6       # ring of 32-deep A slabs (TN)
 B_SLABS = 4       # ring of 32-deep B slabs (NN, TN)
