@@ -831,20 +831,25 @@ __global__ __launch_bounds__(64 * Cfg::NW * Cfg::KS, Cfg::OCC) void gemm_ring_ke
                 acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[buf][b], fa[buf][a],
                                                                     acc[a][b], 0, 0, 0);
     };
-    // Slab kt: wait for slab kt+1 (own loads, then everybody's via the
-    // barrier, which also retires every wave's reads of slab kt), then refill
-    // while multiplying slab kt (fragments read during the previous slab) and
-    // reading the fragments of slab kt+1.  B's loads for slab kt+1 were
-    // issued at step kt-2 (kt odd) or kt-3 (kt even), A's at step kt-3 (kt
-    // odd) or kt-4 (kt even), so only the loads of step kt-1 (an even step,
-    // kt odd) or of steps kt-2 and kt-1 (one of each, kt even) may stay
-    // outstanding.
+    // Slab kt: multiply slab kt (fragments read during the previous slab)
+    // while reading the fragments of slab kt+1 and refilling the rings.  An
+    // odd step first waits for its own loads of A's unit or pair and B's
+    // unit or pair (kt+1)/2, issued at steps kt-3 and kt-2 (only the even
+    // step kt-1 may stay outstanding), then passes a barrier that makes
+    // every wave's loads of both slabs kt+1 and kt+2 visible and retires
+    // every wave's reads up to step kt-1.  An even step needs neither: its
+    // reads (slab kt+1, the second slab of the unit the odd step before made
+    // visible) and its refill (A's buffer last read during step kt-2) are
+    // covered by the barrier of step kt-1, and the odd step's refill (B's
+    // buffer last read during step kt-1) by its own barrier.  One barrier per
+    // 64 k instead of two.
     auto slab_step = [&](auto odd, int kt, int cbuf, int nbuf) {
         constexpr bool kOdd = decltype(odd)::value;
-        if constexpr (kOdd) wait_vmcnt<kDmaEven>();
-        else wait_vmcnt<kDmaEven + kDmaOdd>();
-        wait_lgkmcnt0();
-        barrier();
+        if constexpr (kOdd) {
+            wait_vmcnt<kDmaEven>();
+            wait_lgkmcnt0();
+            barrier();
+        }
         constexpr int kSteps = kOdd ? kDmaOdd : kDmaEven;
 #pragma unroll
         for (int g = 0; g < kGroups; ++g) {

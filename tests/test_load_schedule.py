@@ -3,22 +3,25 @@
 For each layout the kernel uses (NN: B's 32-deep slabs in pairs; NT: both
 operands in 64-deep units; TN: both operands' slabs in pairs), the replay
 issues every step's loads into their ring buffers in program order, applies
-the step's static wait (at most W loads of the wave still outstanding, every earlier
+the static wait and the barrier of the steps that have them (odd steps and
+the prologue: at most W loads of the wave still outstanding, every earlier
 one retired; all waves issue the same number of loads, so the barrier after
-the wait makes every wave's retired loads visible) and the barrier, and
-records which slab each fragment read sees.  It checks that
+the wait makes every wave's retired loads visible and retires every wave's
+earlier fragment reads), and records which slab each fragment read sees.
+It checks that
 
   * every fragment read of slab s finds slab s in the buffer it reads, from
-    a load retired before the barrier that precedes the read;
-  * no load refills a buffer before the barrier that follows the last read
-    of what the buffer held;
+    a load retired before the last barrier that precedes the read;
+  * no load refills a buffer unless a barrier lies between the step of the
+    last read of what the buffer held and the refill;
   * every step issues the per-parity load count the wait immediates assume.
 
 The schedule restates the kernel's indexing: at even steps vs A's 64-deep
 unit (vs + 4) / 2, four loads per wave, into ring buffer unit mod 3; at odd
 steps B's unit (NT, ring of 2) or slab pair (NN, slabs 2v and 2v + 1 in a
-ring of 4) v = (vs + 3) / 2, three loads per wave; waits of 4 (odd steps)
-and 7 (even steps, and the prologue).  TN: at even steps A's slab pair
+ring of 4) v = (vs + 3) / 2, three loads per wave; a wait of 4 and a
+barrier at odd steps, a wait of 7 and a barrier after the prologue, neither
+at even steps.  TN: at even steps A's slab pair
 (slabs 2u and 2u + 1, u = (vs + 4) / 2, in a ring of 6 slabs), four loads
 per wave, at odd steps B's pair as for NN, the same waits.  Fragments of
 slab s are read during step s - 1 (slab 0 after the prologue).
@@ -60,11 +63,17 @@ def default_wait(layout, kt):
     return 4 if kt % 2 else 7
 
 
-def replay(layout, nk, wait_of=None, prologue_wait=None):
+def kernel_barrier(kt):
+    return kt % 2 == 1
+
+
+def replay(layout, nk, wait_of=None, prologue_wait=None, barrier_at=kernel_barrier):
     wait_of = wait_of or (lambda kt: default_wait(layout, kt))
     prologue_wait = 7 if prologue_wait is None else prologue_wait
     issued = 0
     retired = 0
+    visible = 0         # loads retired by every wave before the last barrier
+    barriers = []       # steps with a barrier (the prologue's: -0.5)
     content = {}        # buffer -> (slabs, index of the load that wrote it last)
     last_read = {}      # buffer -> step during which it was last read
     counts = {}
@@ -74,11 +83,14 @@ def replay(layout, nk, wait_of=None, prologue_wait=None):
         n, fills = step_loads(layout, vs)
         counts.setdefault(vs % 2, set()).add(n)
         for buf, slabs in fills:
-            assert last_read.get(buf, -10**9) < vs, f"{layout}: step {vs} refills {buf} early"
+            lr = last_read.get(buf)
+            if lr is not None:
+                assert any(lr < b <= vs for b in barriers), \
+                    f"{layout}: step {vs} refills {buf} early (last read in step {lr})"
             content[buf] = (slabs, issued + n - 1)
         issued += n
 
-    def read(s, step, visible):
+    def read(s, step):
         for buf, slab in slab_reads(layout, s):
             slabs, idx = content[buf]
             assert slab in slabs, f"{layout}: slab {s} not in {buf} (holds {slabs})"
@@ -88,12 +100,16 @@ def replay(layout, nk, wait_of=None, prologue_wait=None):
     for vs in range(-LEAD, 0):
         issue(vs)
     retired = max(retired, issued - prologue_wait)
-    read(0, -1, retired)
+    visible = retired
+    barriers.append(-0.5)
+    read(0, -1)
     for kt in range(nk):
-        retired = max(retired, issued - wait_of(kt))
-        visible = retired                      # the barrier
+        if barrier_at(kt):
+            retired = max(retired, issued - wait_of(kt))
+            visible = retired
+            barriers.append(kt)
         issue(kt)
-        read(kt + 1, kt, visible)
+        read(kt + 1, kt)
     return counts
 
 
@@ -109,15 +125,37 @@ def test_replay_rejects_one_more_outstanding_load(layout):
     # Not vacuous, and the waits are tight: one more outstanding load at the
     # odd steps (the last load of B's unit or pair for the next slab, issued
     # two steps back, is then not retired) or after the prologue reads
-    # unretired data.  The
-    # even steps' wait never binds: the odd step before it has already
-    # retired everything the even step reads.
+    # unretired data.
     with pytest.raises(AssertionError, match="before its load retired"):
         replay(layout, 16, wait_of=lambda kt: 5 if kt % 2 else 7)
     with pytest.raises(AssertionError, match="before its load retired"):
         replay(layout, 16, prologue_wait=8)
-    replay(layout, 16, wait_of=lambda kt: 4 if kt % 2 else 10)
 
+
+@pytest.mark.parametrize("layout", ["NN", "NT", "TN"])
+def test_barriers_at_odd_steps_are_needed_and_enough(layout):
+    # A barrier at every step (the earlier kernel) passes as well; barriers
+    # only at even steps, or every third step, let a refill overtake reads.
+    replay(layout, 64, barrier_at=lambda kt: True)
+    for pattern in (lambda kt: kt % 2 == 0, lambda kt: kt % 3 == 2):
+        with pytest.raises(AssertionError, match="refills"):
+            replay(layout, 64, barrier_at=pattern)
+
+
+def test_kernel_barriers_only_at_odd_steps():
+    # The replay's barrier placement is the kernel's: slab_step waits and
+    # passes the barrier under `if constexpr (kOdd)` and nowhere else.
+    import os
+    import re
+    src = open(os.path.join(os.path.dirname(__file__), "..",
+                            "tensor_transformer_layer_columnparallel_amd", "csrc",
+                            "gemm_ring.hip")).read()
+    i = src.index("auto slab_step = ")
+    j = src.index("using Even = ")
+    body = src[i:j]
+    assert re.search(r"if constexpr \(kOdd\) \{\s*wait_vmcnt<kDmaEven>\(\);\s*"
+                     r"wait_lgkmcnt0\(\);\s*barrier\(\);\s*\}", body), body[:600]
+    assert body.count("barrier();") == 1 and body.count("wait_vmcnt") == 1
 
 
 def test_replay_constants_match_the_kernel_source():
