@@ -19,18 +19,21 @@
 // The DMA is issued from inline assembly: the compiler's wait analysis cannot
 // tell the buffers apart and would wait for the DMA just issued before any
 // LDS read.  The waits are explicit instead.  Compute walks K in 32-k slabs;
-// at slab k every wave
-//   1. waits until its loads of slab k+1 have landed (the vector memory
-//      counter retires loads in issue order; every wave issues the same
-//      number of DMA instructions per odd and per even slab, so the counts
-//      are static) and until its own LDS reads of slab k have returned;
-//   2. passes a barrier: slab k+1 is in LDS for everybody and nobody reads
-//      slab k's buffers any more;
-//   3. in four groups, each with the MFMAs of a share of the A fragments,
-//      (in all groups but the last) a share of the fragment reads, at raised
-//      wave priority, and a share of the DMA instructions: multiplies slab k
-//      (fragments read during slab k-1), reads the fragments of slab k+1 and
-//      refills a freed buffer.
+// at an odd slab k every wave first
+//   1. waits until its loads of A's and B's units or pairs for slabs k+1 and
+//      k+2 have landed (the vector memory counter retires loads in issue
+//      order; every wave issues the same number of DMA instructions per odd
+//      and per even slab, so the counts are static) and until its own LDS
+//      reads have returned;
+//   2. passes a barrier: slabs k+1 and k+2 are in LDS for everybody and
+//      nobody reads the buffers of slab k or earlier any more.
+// An even slab needs neither (its reads and refills are covered by the
+// barrier of the odd slab before): one barrier per 64 k.  At every slab the
+// wave then, in four groups, each with the MFMAs of a share of the A
+// fragments, (in all groups but the last) a share of the fragment reads, at
+// raised wave priority, and a share of the DMA instructions, multiplies slab
+// k (fragments read during slab k-1), reads the fragments of slab k+1 and
+// refills a freed buffer.
 // Spreading the memory instructions over the MFMAs keeps the waves of a SIMD
 // from stalling together on a burst of loads while the matrix pipe idles.
 // Loads of elements outside the operands (ragged M/N tails, k past K) use a
@@ -71,8 +74,9 @@ constexpr int kBBufs = 2;                   // B's ring (a power of two)
 constexpr int kLead = 4;                    // DMA steps issued before the first slab
 // Interleave groups per slab, and how many of them carry fragment reads.
 // Only the first three of four groups carry reads, so the last group's
-// MFMAs cover the latency of the last reads before the next barrier (2-3%
-// faster on the NN products than reads in all four groups; reads in two
+// MFMAs cover the latency of the last reads before the next wait (2-3%
+// faster on the NN products than reads in all four groups, also at the odd
+// slabs alone, which an even slab without a wait follows; reads in two
 // groups or all up front were slower).  Within a group the reads follow the
 // MFMAs (about 1% faster on the row-layer product and the backward than
 // before them, the same on the column product) and the DMA instructions
