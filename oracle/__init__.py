@@ -36,17 +36,18 @@ _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 
-def build(force: bool = True) -> str:
-    """Compile oracle.c into liboracle.so with gcc (portable x86-64 code, no
+def build(force: bool = True, src: str = _SRC, out: str = _LIB_PATH) -> str:
+    """Compile oracle.c (or another source, e.g. a test's deliberately broken
+    copy) into a shared library with gcc (portable x86-64 code, no
     -march=native, no fast-math, no FMA contraction)."""
-    if force or not os.path.exists(_LIB_PATH):
-        tmp = _LIB_PATH + ".tmp"
+    if force or not os.path.exists(out):
+        tmp = out + ".tmp"
         cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
                "-fno-fast-math", "-ffp-contract=off", "-Wall", "-Wextra",
-               "-D_DEFAULT_SOURCE", _SRC, "-o", tmp, "-lm"]
+               "-D_DEFAULT_SOURCE", src, "-o", tmp, "-lm"]
         subprocess.run(cmd, check=True)
-        os.replace(tmp, _LIB_PATH)
-    return _LIB_PATH
+        os.replace(tmp, out)
+    return out
 
 
 def _load():
@@ -54,29 +55,34 @@ def _load():
     if _lib is None:
         if not os.path.exists(_LIB_PATH):
             build(force=False)
-        lib = ctypes.CDLL(_LIB_PATH)
-        dp = ctypes.POINTER(ctypes.c_double)
-        i64 = ctypes.c_int64
-        sig = {
-            "oracle_gelu_tanh": [dp, dp, i64],
-            "oracle_gelu_tanh_grad": [dp, dp, i64],
-            "oracle_matmul": [dp, dp, dp, i64, i64, i64],
-            "oracle_column_linear": [dp, dp, dp, dp, i64, i64, i64, ctypes.c_int],
-            "oracle_row_linear": [dp, dp, dp, i64, i64, i64],
-            "oracle_mlp_shard_fwd": [dp, dp, dp, dp, dp, dp, dp, i64, i64, i64],
-            "oracle_mlp_shard_bwd": [dp] * 11 + [i64, i64, i64],
-            "oracle_linear_bwd": [dp] * 6 + [i64, i64, i64],
-            "oracle_shard_sum": [dp, dp, ctypes.c_int, i64],
-            "oracle_shard_concat": [dp, dp, ctypes.c_int, i64, i64],
-            "oracle_reduce_scatter": [dp, dp, ctypes.c_int, i64, i64, ctypes.c_int],
-            "oracle_layernorm": [dp, dp, dp, dp, i64, i64, ctypes.c_double],
-        }
-        for name, args in sig.items():
-            fn = getattr(lib, name)
-            fn.argtypes = args
-            fn.restype = None
-        _lib = lib
+        _lib = load_library(_LIB_PATH)
     return _lib
+
+
+def load_library(path: str):
+    """Loads a build of oracle.c and declares its functions' signatures."""
+    lib = ctypes.CDLL(path)
+    dp = ctypes.POINTER(ctypes.c_double)
+    i64 = ctypes.c_int64
+    sig = {
+        "oracle_gelu_tanh": [dp, dp, i64],
+        "oracle_gelu_tanh_grad": [dp, dp, i64],
+        "oracle_matmul": [dp, dp, dp, i64, i64, i64],
+        "oracle_column_linear": [dp, dp, dp, dp, i64, i64, i64, ctypes.c_int],
+        "oracle_row_linear": [dp, dp, dp, i64, i64, i64],
+        "oracle_mlp_shard_fwd": [dp, dp, dp, dp, dp, dp, dp, i64, i64, i64],
+        "oracle_mlp_shard_bwd": [dp] * 11 + [i64, i64, i64],
+        "oracle_linear_bwd": [dp] * 6 + [i64, i64, i64],
+        "oracle_shard_sum": [dp, dp, ctypes.c_int, i64],
+        "oracle_shard_concat": [dp, dp, ctypes.c_int, i64, i64],
+        "oracle_reduce_scatter": [dp, dp, ctypes.c_int, i64, i64, ctypes.c_int],
+        "oracle_layernorm": [dp, dp, dp, dp, i64, i64, ctypes.c_double],
+    }
+    for name, args in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = None
+    return lib
 
 
 def _f64(a) -> np.ndarray:
